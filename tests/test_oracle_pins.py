@@ -1,0 +1,413 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: exact rational
+arithmetic, brute-force enumeration, a library routine (torch's scaled dot
+product attention and logsumexp in float64, numpy sorting), closed forms,
+special cases named on the pages, or figures the pages print
+(tests/golden/pages_figures.json).  Each is chosen so that a plausible slip in
+the oracle (a dropped term, a wrong index or head mapping, a wrong tie rule,
+truncation instead of rounding, votes over the wrong candidate range) fails.
+"""
+import itertools
+import json
+import math
+import os
+import struct
+from collections import Counter
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_ksa_amd.inputs import (as_numpy_bits, integer_inputs, make_inputs,
+                                                    small_workload, kv_bytes_per_token_per_layer)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+# ----------------------------------------------------------------------------- helpers
+def bits_to_f64(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or float32 -> float64 values."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def frac_round_bits(x: Fraction, sig_bits: int, min_exp: int) -> Fraction:
+    """Round an exact rational to `sig_bits` significant bits, ties to even,
+    with a uniform grid below 2**min_exp (IEEE gradual underflow)."""
+    if x == 0:
+        return Fraction(0)
+    ax = abs(x)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    if Fraction(2) ** e > ax:
+        e -= 1
+    # now 2**e <= ax < 2**(e+1)
+    e = max(e, min_exp)
+    quantum = Fraction(2) ** (e - (sig_bits - 1))
+    n = round(x / quantum)  # Fraction.__round__ rounds half to even
+    return n * quantum
+
+
+def bf16_bits_of(x: Fraction) -> int:
+    r = frac_round_bits(x, 8, -126)
+    return struct.unpack("<I", struct.pack("<f", float(r)))[0] >> 16
+
+
+def f32_of(x: Fraction) -> np.float32:
+    r = frac_round_bits(x, 24, -126)
+    return np.float32(float(r))
+
+
+def sdpa64(q, k, v, T, mask=None, scale=None):
+    """torch scaled_dot_product_attention in float64 on the CPU, GQA by
+    repeat-interleaving KV heads.  q [B,Hq,D]; k, v [B,Hkv,Tcap,D] (bits or f32);
+    mask [B,Hq,T] bool.  Returns (out [B,Hq,D], lse [B,Hq])."""
+    qf = torch.from_numpy(bits_to_f64(q))
+    kf = torch.from_numpy(bits_to_f64(k))[:, :, :T]
+    vf = torch.from_numpy(bits_to_f64(v))[:, :, :T]
+    G = qf.shape[1] // kf.shape[1]
+    kf = kf.repeat_interleave(G, dim=1)
+    vf = vf.repeat_interleave(G, dim=1)
+    am = None if mask is None else torch.from_numpy(mask)[:, :, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(qf[:, :, None, :], kf, vf, attn_mask=am,
+                                                           scale=scale)[:, :, 0, :]
+    s = scale if scale is not None else 1.0 / math.sqrt(qf.shape[-1])
+    logits = torch.einsum("bhd,bhtd->bht", qf, kf) * s
+    if mask is not None:
+        logits = logits.masked_fill(~torch.from_numpy(mask), float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1)
+    return out.numpy(), lse.numpy()
+
+
+def rand_problem(B=2, Hq=4, Hkv=2, D=32, T=61, Tcap=None, dtype="bf16", seed=0):
+    w = small_workload(B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, Tcap=Tcap or T, dtype=dtype, seed=seed)
+    x = make_inputs(w)
+    return w, as_numpy_bits(x["q"]), as_numpy_bits(x["k"]), as_numpy_bits(x["v"])
+
+
+# ----------------------------------------------------------------------------- summaries
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,Bs", [(37, 8), (64, 16), (45, 6), (33, 32)])
+def test_summaries_are_rounded_exact_means(dtype, T, Bs):
+    """Kinetics explainer §五: a block's summary is its mean key.  Pinned by exact
+    rational means rounded to nearest-even (covers a partial last block and
+    non-power-of-two block sizes)."""
+    w, q, k, v = rand_problem(B=2, Hq=2, Hkv=2, D=16, T=T, Tcap=T + 3, dtype=dtype, seed=T + Bs)
+    summ = oracle.block_summaries(k, T, Bs)
+    kv = bits_to_f64(k)
+    nb = oracle.nblocks(T, Bs)
+    for b in range(2):
+        for g in range(2):
+            for j in range(nb):
+                toks = range(j * Bs, min((j + 1) * Bs, T))
+                for d in range(16):
+                    exact = sum(Fraction(float(kv[b, g, t, d])) for t in toks) / len(toks)
+                    if dtype == "bf16":
+                        assert int(summ[b, g, j, d]) == bf16_bits_of(exact), (b, g, j, d)
+                    else:
+                        assert summ[b, g, j, d] == f32_of(exact), (b, g, j, d)
+
+
+def test_summaries_range_and_zero_sum_invariant():
+    """Only blocks [first, first+num) are written; the fp64 mean makes the block's
+    deviations sum to zero."""
+    w, q, k, v = rand_problem(B=1, Hq=1, Hkv=1, D=8, T=50, dtype="f32", seed=3)
+    nbcap = oracle.nblocks(50, 8)
+    sentinel = np.full((1, 1, nbcap, 8), 123.0, np.float32)
+    out, m64 = oracle.block_summaries(k, 50, 8, first_block=2, num_blocks=3, out=sentinel.copy(),
+                                      want_f64=True)
+    assert np.all(out[:, :, :2] == 123.0) and np.all(out[:, :, 5:] == 123.0)
+    assert not np.any(out[:, :, 2:5] == 123.0)
+    kv = bits_to_f64(k)
+    for j in range(2, 5):
+        dev = kv[0, 0, j * 8:(j + 1) * 8] - m64[0, 0, j]
+        assert np.abs(dev.sum(axis=0)).max() < 1e-12
+
+
+def test_summaries_round_half_to_even():
+    """Two bf16 keys whose mean sits exactly halfway between bf16 neighbours:
+    the stored summary must take the even neighbour (truncation would not)."""
+    # mean of 1.0 and 1.0 + 3*2^-7 is 1 + 1.5*2^-7: halfway between 1+2^-7 and 1+2^-6
+    a = np.float32(1.0)
+    b = np.float32(1.0 + 3 * 2.0 ** -7)
+    k = np.zeros((1, 1, 2, 1), np.float32)
+    k[0, 0, 0, 0], k[0, 0, 1, 0] = a, b
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    s = oracle.block_summaries(kb, 2, 2)
+    # 1 + 2^-6 has an even last mantissa bit (mantissa 0b0000010), 1 + 2^-7 odd
+    assert int(s[0, 0, 0, 0]) == bf16_bits_of(Fraction(1) + Fraction(1, 64))
+    assert int(s[0, 0, 0, 0]) == 0x3F82
+
+
+# ----------------------------------------------------------------------------- group scores
+def test_group_scores_token_level_equal_library_logits():
+    """Bs = 1 and G = 1: summaries are the keys themselves, so the scaled block
+    scores are the attention logits q.k / sqrt(D) (torch float64)."""
+    w, q, k, v = rand_problem(B=2, Hq=2, Hkv=2, D=32, T=40, dtype="f32", seed=5)
+    summ = oracle.block_summaries(k, 40, 1)
+    raw, scaled = oracle.group_scores(q, summ, 40, 1)
+    qf = torch.from_numpy(bits_to_f64(q))
+    kf = torch.from_numpy(bits_to_f64(k))
+    ref = torch.einsum("bhd,bhtd->bht", qf, kf).numpy()
+    np.testing.assert_allclose(raw, ref, rtol=1e-13, atol=1e-12)
+    np.testing.assert_allclose(scaled, ref / math.sqrt(32), rtol=1e-13, atol=1e-12)
+
+
+def test_group_scores_pool_the_right_heads():
+    """GQA: query head h belongs to KV head h // G.  The group score with G heads
+    equals the score of one head holding the sum of that group's queries (exact
+    with integer inputs); a head-to-group mix-up fails this."""
+    w = small_workload(B=2, Hq=8, Hkv=2, D=16, T=48, Bs=8, dtype="bf16", seed=11)
+    x = integer_inputs(w)
+    q, k = as_numpy_bits(x["q"]), as_numpy_bits(x["k"])
+    summ = oracle.block_summaries(k, 48, 8)
+    raw, scaled = oracle.group_scores(q, summ, 48, 8)
+    qs = torch.from_numpy(bits_to_f64(q)).view(2, 2, 4, 16).sum(2).to(torch.bfloat16)
+    raw1, _ = oracle.group_scores(as_numpy_bits(qs), summ, 48, 8)
+    np.testing.assert_array_equal(raw, raw1)
+    np.testing.assert_allclose(scaled, raw / 4 / math.sqrt(16), rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------- top-k
+def brute_topk(scores, k):
+    """All k-subsets: maximum score sum, then the lexicographically smallest
+    sorted index tuple.  For distinct-or-tied scores this is exactly 'order by
+    (score desc, index asc) and take the first k'."""
+    n = len(scores)
+    best, best_t = None, None
+    for comb in itertools.combinations(range(n), k):
+        s = sum(scores[i] for i in comb)
+        if best is None or s > best or (s == best and comb < best_t):
+            best, best_t = s, comb
+    return list(best_t)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(3, 11))
+    # small integers: many exact ties; exact sums in fp64
+    scores = rng.integers(-3, 4, size=(4, n)).astype(np.float64)
+    for k in range(1, n + 1):
+        got = oracle.topk(scores, k)
+        for r in range(4):
+            assert list(got[r]) == brute_topk(list(scores[r]), k), (r, k, scores[r])
+
+
+def test_topk_clamps_k_and_treats_signed_zeros_as_equal():
+    s = np.array([[0.0, -0.0, -1.0, 2.0]])
+    assert list(oracle.topk(s, 10)[0]) == [0, 1, 2, 3]
+    s = np.array([[-0.0, 0.0, -1.0]])
+    assert list(oracle.topk(s, 1)[0]) == [0]
+
+
+# ----------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 1), (3, 3)])
+def test_dense_matches_library_sdpa(dtype, Hq, Hkv):
+    """Kinetics explainer §四 dense attention = torch SDPA (float64, GQA by
+    repeat_interleave); lse = torch.logsumexp of the scaled logits."""
+    w, q, k, v = rand_problem(B=2, Hq=Hq, Hkv=Hkv, D=32, T=77, Tcap=80, dtype=dtype, seed=Hq)
+    out, lse = oracle.attend_dense(q, k, v, 77)
+    ref, ref_lse = sdpa64(q, k, v, 77)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+def test_dense_explicit_scale():
+    w, q, k, v = rand_problem(B=1, Hq=2, Hkv=1, D=16, T=30, dtype="f32", seed=9)
+    out, lse = oracle.attend_dense(q, k, v, 30, sm_scale=0.3)
+    ref, ref_lse = sdpa64(q, k, v, 30, scale=0.3)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, atol=1e-12)
+
+
+def test_block_attention_matches_masked_sdpa():
+    """Attention over the selected blocks = SDPA with a mask that keeps exactly
+    the tokens of those blocks (partial last block included)."""
+    T, Bs = 70, 8                       # 9 blocks, the last holds 6 tokens
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=16, T=T, Tcap=72, dtype="bf16", seed=21)
+    rng = np.random.default_rng(0)
+    nb = oracle.nblocks(T, Bs)
+    idx = np.stack([np.stack([np.sort(rng.choice(nb, 4, replace=False)) for _ in range(2)])
+                    for _ in range(2)]).astype(np.int32)
+    idx[0, 0] = [0, 3, 7, 8]            # include the partial block
+    out, lse = oracle.attend_blocks(q, k, v, T, Bs, idx)
+    mask = np.zeros((2, 4, T), bool)
+    for b in range(2):
+        for h in range(4):
+            for j in idx[b, h // 2]:
+                mask[b, h, j * Bs:min((j + 1) * Bs, T)] = True
+    ref, ref_lse = sdpa64(q, k, v, T, mask=mask)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, atol=1e-12)
+
+
+def test_all_blocks_selected_is_dense():
+    w, q, k, v = rand_problem(B=1, Hq=2, Hkv=1, D=16, T=50, dtype="bf16", seed=4)
+    nb = oracle.nblocks(50, 16)
+    idx = np.arange(nb, dtype=np.int32)[None, None, :]
+    o1, l1 = oracle.attend_blocks(q, k, v, 50, 16, idx)
+    o2, l2 = oracle.attend_dense(q, k, v, 50)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+
+
+def test_single_token_selection_returns_its_value():
+    """Bs = 1, k = 1: the softmax over one token is 1, so out = v_t exactly and
+    lse = its logit."""
+    w, q, k, v = rand_problem(B=1, Hq=2, Hkv=1, D=16, T=20, dtype="f32", seed=8)
+    idx = np.array([[[13]]], np.int32)
+    out, lse = oracle.attend_blocks(q, k, v, 20, 1, idx)
+    np.testing.assert_array_equal(out[0, 0], v[0, 0, 13].astype(np.float64))
+    np.testing.assert_array_equal(out[0, 1], v[0, 0, 13].astype(np.float64))
+    logit = q[0, 0].astype(np.float64) @ k[0, 0, 13].astype(np.float64) / 4.0
+    assert abs(lse[0, 0] - logit) < 1e-12
+
+
+def test_equal_keys_give_mean_of_values():
+    """All keys equal: uniform weights, out = mean of the attended values and
+    lse = logit + ln(count)."""
+    w, q, k, v = rand_problem(B=1, Hq=2, Hkv=1, D=16, T=32, dtype="f32", seed=2)
+    k[:] = k[0, 0, 0]
+    tok = np.array([[1, 5, 9, 30]], np.int32)
+    out, lse = oracle.attend_tokens(q, k, v, 32, tok)
+    ref = v[0, 0, [1, 5, 9, 30]].astype(np.float64).mean(0)
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-14)
+    logit = q[0, 0].astype(np.float64) @ k[0, 0, 0].astype(np.float64) / 4.0
+    assert abs(lse[0, 0] - (logit + math.log(4))) < 1e-12
+
+
+def test_token_attention_matches_masked_sdpa():
+    """LessIsMore explainer §五: every head attends the one shared token set."""
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=16, T=40, dtype="bf16", seed=31)
+    tok = np.array([[0, 2, 3, 17, 39], [5, 6, 7, 8, 20]], np.int32)
+    out, lse = oracle.attend_tokens(q, k, v, 40, tok)
+    mask = np.zeros((2, 4, 40), bool)
+    for b in range(2):
+        mask[b, :, tok[b]] = True
+    ref, ref_lse = sdpa64(q, k, v, 40, mask=mask)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- votes
+def brute_vote(q64, k64, T, N, W):
+    """Python-sorted per-head picks, Counter tally, sorted ranking."""
+    B, Hq, D = q64.shape
+    Hkv = k64.shape[1]
+    G = Hq // Hkv
+    sets, tallies = [], []
+    for b in range(B):
+        if T <= N:
+            sets.append(list(range(T)))
+            tallies.append(Counter())
+            continue
+        C, Kv = T - W, N - W
+        tally = Counter()
+        for h in range(Hq):
+            lg = [float(np.dot(q64[b, h], k64[b, h // G, t])) for t in range(C)]
+            order = sorted(range(C), key=lambda t: (-lg[t], t))
+            tally.update(order[:Kv])
+        ranked = sorted(range(C), key=lambda t: (-tally[t], t))
+        sets.append(sorted(ranked[:Kv]) + list(range(C, T)))
+        tallies.append(tally)
+    return sets, tallies
+
+
+@pytest.mark.parametrize("T,N,W", [(40, 12, 3), (40, 12, 0), (33, 8, 2), (64, 16, 4)])
+@pytest.mark.parametrize("integer", [False, True])
+def test_votes_and_set_match_brute_force(T, N, W, integer):
+    """LessIsMore explainer §二/§五: equal votes per head, tally per token, rank by
+    votes (ties: lowest index), append the W most recent tokens."""
+    w = small_workload(B=2, Hq=4, Hkv=2, D=8, T=T, dtype="bf16", seed=T + N + W)
+    x = integer_inputs(w, -1, 1) if integer else make_inputs(w)
+    q, k = as_numpy_bits(x["q"]), as_numpy_bits(x["k"])
+    sel, vc = oracle.vote_select(q, k, T, N, W)
+    sets, tallies = brute_vote(bits_to_f64(q), bits_to_f64(k), T, N, W)
+    for b in range(2):
+        assert list(sel[b]) == sets[b]
+        for t in range(T):
+            assert vc[b, t] == tallies[b][t]
+
+
+def test_vote_window_equal_budget_is_local_attention():
+    """W = N: no voted tokens, the set is the last N tokens (the local-attention
+    pattern of the Kinetics explainer §五 and the 100 % window of the
+    LessIsMore explainer §四)."""
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=8, T=50, dtype="bf16", seed=1)
+    sel, vc = oracle.vote_select(q, k, 50, 10, 10)
+    assert sel.tolist() == [list(range(40, 50))] * 2
+    assert vc.sum() == 0
+
+
+def test_vote_short_context_is_dense():
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=8, T=30, dtype="bf16", seed=1)
+    sel, vc = oracle.vote_select(q, k, 30, 32, 8)
+    assert sel.tolist() == [list(range(30))] * 2 and vc.sum() == 0
+    sel, vc = oracle.vote_select(q, k, 30, 30, 8)
+    assert sel.tolist() == [list(range(30))] * 2
+
+
+def test_single_head_vote_is_token_topk():
+    """Hq = 1: the pooled ranking is that head's ranking, so the voted part is the
+    token-level top-(N-W) (numpy lexsort on (t, -logit))."""
+    w, q, k, v = rand_problem(B=2, Hq=1, Hkv=1, D=16, T=60, dtype="f32", seed=6)
+    N, W = 20, 5
+    sel, _ = oracle.vote_select(q, k, 60, N, W)
+    for b in range(2):
+        lg = k[b, 0, :55].astype(np.float64) @ q[b, 0].astype(np.float64)
+        order = np.lexsort((np.arange(55), -lg))
+        ref = sorted(order[:N - W].tolist()) + list(range(55, 60))
+        assert sel[b].tolist() == ref
+
+
+def test_vote_equals_block_topk_at_token_granularity():
+    """Hq = Hkv = 1, Bs = 1, W = 0, N = k: both selections are the token top-k."""
+    w, q, k, v = rand_problem(B=3, Hq=1, Hkv=1, D=16, T=45, dtype="bf16", seed=12)
+    sel, _ = oracle.vote_select(q, k, 45, 9, 0)
+    summ = oracle.block_summaries(k, 45, 1)
+    raw, _ = oracle.group_scores(q, summ, 45, 1)
+    blk = oracle.topk(raw, 9)
+    np.testing.assert_array_equal(sel, blk[:, 0, :])
+
+
+def test_budget_split_of_the_pages():
+    """2048-token budget with a 25 % recency share: 1536 voted history tokens
+    plus the 512 most recent (LessIsMore explainer §二, §三)."""
+    with open(GOLDEN) as f:
+        g = json.load(f)["budget_split"]
+    N = g["token_budget"]
+    W = int(round(N * g["recent_fraction"]))
+    assert (W, N - W) == (512, 1536)
+    assert N - W == int(round(N * g["voted_fraction"]))
+    w = small_workload(B=1, Hq=4, Hkv=2, D=8, T=3000, dtype="bf16", seed=2)
+    x = make_inputs(w)
+    sel, _ = oracle.vote_select(as_numpy_bits(x["q"]), as_numpy_bits(x["k"]), 3000, N, W)
+    s = sel[0]
+    assert len(s) == 2048 and np.all(np.diff(s) > 0)
+    assert (s < 3000 - W).sum() == 1536 and (s >= 3000 - W).sum() == 512
+
+
+# ----------------------------------------------------------------------------- byte accounting
+def test_kv_byte_accounting_matches_the_pages_sizes():
+    """Kinetics explainer §三 prints 3.5 GB (Qwen3-0.6B) and 8 GB (Qwen3-32B) of KV
+    cache at 32K tokens.  With 8 KV heads of dim 128 in bf16 (4096 B per token
+    per layer) that is 28 and 64 layers, the two models' layer counts; the
+    Kinetics news page's (2048, 32768) setting on 8 GPUs is 34.36 GB per GPU and
+    layer, the share benchmarked as the 256-sequence workload."""
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    per_tok = kv_bytes_per_token_per_layer(8, 128, 2)
+    assert per_tok == 4096
+    kv = g["kv_cache_at_32k"]
+    ctx = kv["context_tokens"]
+    assert kv["qwen3_0p6b_kv_gib"] * 2 ** 30 / (ctx * per_tok) == 28
+    assert kv["qwen3_32b_kv_gib"] * 2 ** 30 / (ctx * per_tok) == 64
+    ts = g["throughput_setting"]
+    per_gpu = ts["batch"] * ts["context_tokens"] * per_tok / ts["gpus_per_node"]
+    assert abs(per_gpu / 1e9 - 34.36) < 0.01
+    assert ts["batch"] // ts["gpus_per_node"] == 256
