@@ -1,0 +1,199 @@
+/*
+ * ksa.h -- C ABI of libksa: one decode step of block top-k sparse attention
+ * over a GQA KV cache, the vote-union (LessIsMore-style) shared token
+ * selection, and dense decode attention for comparison, on AMD MI355X
+ * (gfx950).
+ *
+ * Pages the operations follow (cited by page and section):
+ *   Kinetics explainer (news.43u.com.cn), section 五: block top-k attention --
+ *     history tokens are cut into fixed-size blocks, each block is summarised
+ *     by its mean key, the K' blocks most relevant to the query are chosen
+ *     and attention runs over their tokens only; the method works with a
+ *     paged KV cache.
+ *   Kinetics explainer, section 四: dense attention over every history token.
+ *   LessIsMore explainer (techwalker.com), section 二: each query head gets
+ *     the same number of votes, the per-token vote totals rank the tokens and
+ *     one ranked set serves every head; 75 % of the token budget goes to voted
+ *     history and 25 % to the most recent tokens.
+ *   LessIsMore explainer, section 五: a selection layer scores every token
+ *     for every head, aggregates the heads' picks, appends the most recent
+ *     tokens; sparse layers attend only that set, which is shared by all
+ *     heads of a GQA group (one KV read per group).
+ *
+ * Conventions for every entry point
+ *   - Buffer pointers are DEVICE pointers (hipMalloc'd or torch CUDA memory)
+ *     owned by the caller; the problem and selection structs are HOST memory
+ *     read during the call only.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns without synchronising.  The library never
+ *     allocates, frees or synchronises device memory and keeps no pointer
+ *     after a call returns.  Calls on different streams with disjoint outputs
+ *     and workspaces may run concurrently.
+ *   - Arguments are validated on the host before any launch.  On any status
+ *     other than KSA_OK nothing is launched and no output is written, except
+ *     KSA_ERR_HIP, which reports a failed launch (hipGetLastError).
+ *   - Index buffers are device data and are not validated: out-of-range or
+ *     duplicate indices are undefined behaviour.  NaN/Inf inputs are not
+ *     supported.
+ *   - Ranking ties are broken by the lowest index everywhere; every index
+ *     list is written in ascending order.
+ *   - No C++ exception crosses this interface.
+ *
+ * Layouts (row-major, last dimension contiguous):
+ *   q          [B, Hq, D]            KV dtype
+ *   k, v       [B, Hkv, T_cap, D]    KV dtype; token t of sequence b, KV head g
+ *   summaries  [B, Hkv, NB_cap, D]   KV dtype, NB_cap = ceil(T_cap / Bs)
+ *   out        [B, Hq, D]            fp32
+ *   lse        [B, Hq]               fp32, natural log (nullable)
+ * Query head h reads KV head h / (Hq / Hkv).  Block j of a sequence covers
+ * tokens [j*Bs, min((j+1)*Bs, T)); NB = ceil(T / Bs).
+ */
+#ifndef KSA_H
+#define KSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KSA_OK = 0,
+  KSA_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or parameter is out of range */
+  KSA_ERR_UNSUPPORTED = 2,      /* valid, but outside what this build handles */
+  KSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  KSA_ERR_HIP = 4               /* a HIP launch failed */
+} ksa_status;
+
+typedef enum { KSA_F32 = 0, KSA_BF16 = 1 } ksa_dtype;
+
+/* One decode step's shape.  T counts the valid cached tokens, the token being
+ * decoded included (its K/V are appended before the call).  Every sequence of
+ * the batch has the same T (the uniform-workload setting of the Kinetics news
+ * page, section on the Qwen3-0.6B throughput gain).
+ * Supported by this build: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8};
+ * dtype fp32 or bf16; B*Hkv*T_cap*D < 2^40. */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t num_q_heads;  /* Hq >= 1, a multiple of Hkv */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* D */
+  int32_t seq_len;      /* T, 1 <= T <= T_cap */
+  int32_t max_seq_len;  /* T_cap: token stride of k and v */
+  int32_t block_size;   /* Bs >= 1 (block top-k calls only; ignored elsewhere) */
+  ksa_dtype dtype;      /* element type of q, k, v and summaries */
+  float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(D) */
+} ksa_problem;
+
+typedef enum { KSA_SEL_BLOCKS = 0, KSA_SEL_TOKENS = 1 } ksa_sel_kind;
+
+/* What ksa_sparse_decode attends.
+ *   BLOCKS: idx is [B, Hkv, count] int32 -- for each (sequence, KV head) the
+ *           ids of `count` distinct blocks < NB, ascending (the output of
+ *           ksa_select_topk); all G query heads of the group attend them.
+ *   TOKENS: idx is [B, count] int32 -- for each sequence `count` distinct
+ *           token ids < T, ascending (the output of ksa_vote_select); every
+ *           query head of the sequence attends them. */
+typedef struct {
+  ksa_sel_kind kind;
+  const int32_t* idx; /* device pointer */
+  int32_t count;      /* >= 1 */
+} ksa_selection;
+
+/* ---------------------------------------------------------------------
+ * ksa_block_summaries -- mean key of each block (Kinetics explainer,
+ * section 五: every block is represented by its average).
+ * For blocks j in [first_block, first_block + num_blocks) of every
+ * (sequence, KV head): summaries[b,g,j,:] = mean over the block's n_j valid
+ * tokens of k[b,g,t,:], summed in fp64 in token order, divided by n_j in
+ * fp64, rounded once to nearest-even in the KV dtype.  Other blocks are not
+ * touched.  A decode step refreshes only the block holding token T-1
+ * (first_block = (T-1)/Bs, num_blocks = 1); a rebuild passes (0, NB).
+ * Requires 0 <= first_block, num_blocks >= 1, first_block + num_blocks <= NB.
+ * Needs no workspace. */
+ksa_status ksa_block_summaries(const ksa_problem* problem, const void* k, void* summaries,
+                               int32_t first_block, int32_t num_blocks, void* stream);
+
+/* ---------------------------------------------------------------------
+ * ksa_select_topk -- choose the K' most relevant blocks per (sequence, KV
+ * head) (Kinetics explainer, section 五).
+ * Relevance of block j to KV group g: the sum over the group's query heads h
+ * of q_h . summaries[b,g,j,:], accumulated in fp32; the k_eff = min(top_k, NB)
+ * blocks ranked first by (relevance desc, j asc) are written to
+ * block_idx [B, Hkv, k_eff] int32 in ascending order.
+ * block_scores (nullable) [B, Hkv, NB] fp32 receives sm_scale * relevance / G,
+ * the mean attention logit of the group against the summary.
+ * top_k >= 1.  NB must not exceed 15360.  workspace: ksa_workspace_bytes(
+ * problem, KSA_OP_SELECT_TOPK, top_k) bytes (may be 0 and NULL when that is 0). */
+ksa_status ksa_select_topk(const ksa_problem* problem, const void* q, const void* summaries,
+                           int32_t top_k, int32_t* block_idx, float* block_scores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * ksa_sparse_decode -- softmax attention of every query head over the
+ * selected tokens only (Kinetics explainer, section 五, for BLOCKS; the
+ * LessIsMore explainer, section 五, for TOKENS): for head h of group g,
+ * out[b,h,:] = sum_t p_t v[b,g,t,:], p = softmax_t(sm_scale * q_h . k[b,g,t,:])
+ * over the selected tokens t < T, accumulated in fp32; lse[b,h] = log of the
+ * softmax denominator plus the max logit (natural log).  Tokens of a
+ * selected block at or past T are skipped.
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_SPARSE_BLOCKS or
+ * KSA_OP_SPARSE_TOKENS, sel->count) bytes. */
+ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const void* k,
+                             const void* v, const ksa_selection* sel, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * ksa_vote_select -- the shared token set of the vote-union variant
+ * (LessIsMore explainer, sections 二 and 五), per sequence b, with
+ * N = token_budget and W = recent_window (the pages use W = N/4):
+ *   if T <= N: token_idx[b] = 0..T-1 and no vote is taken;
+ *   else, with history C = [0, T-W) and Kv = N - W:
+ *     every query head h (all Hq of them) picks the first Kv tokens of C by
+ *       (q_h . k[b,h/G,t,:] desc, t asc), scores accumulated in fp32;
+ *     votes[b,t] = number of heads that picked t (0 for t >= T-W);
+ *     the first Kv tokens of C by (votes desc, t asc), ascending, are
+ *       followed by T-W, ..., T-1.
+ * token_idx: [B, min(N, T)] int32.  votes (nullable): [B, T] uint8 (needs
+ * Hq <= 255); all zero when T <= N.
+ * Requires 0 <= W <= N, N >= 1.  T - W must not exceed 2^21.
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_VOTE_SELECT, token_budget). */
+ksa_status ksa_vote_select(const ksa_problem* problem, const void* q, const void* k,
+                           int32_t token_budget, int32_t recent_window, int32_t* token_idx,
+                           uint8_t* votes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * ksa_dense_decode -- exact softmax attention of every query head over all T
+ * cached tokens (Kinetics explainer, section 四); the comparison baseline.
+ * Outputs as ksa_sparse_decode.
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_DENSE, 0) bytes. */
+ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const void* k,
+                            const void* v, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Operations for ksa_workspace_bytes. */
+enum {
+  KSA_OP_SELECT_TOPK = 0,    /* param: top_k */
+  KSA_OP_SPARSE_BLOCKS = 1,  /* param: selection count (blocks per row) */
+  KSA_OP_SPARSE_TOKENS = 2,  /* param: selection count (tokens per sequence) */
+  KSA_OP_VOTE_SELECT = 3,    /* param: token_budget */
+  KSA_OP_DENSE = 4           /* param: unused */
+};
+
+/* Workspace bytes a call needs for this problem; a pure host function of its
+ * arguments (no device query).  Returns 0 when the call needs none, and
+ * SIZE_MAX when the arguments are invalid. */
+size_t ksa_workspace_bytes(const ksa_problem* problem, int32_t op, int32_t param);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ksa_status_string(ksa_status status);
+
+/* Library version, "major.minor.patch". */
+const char* ksa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KSA_H */

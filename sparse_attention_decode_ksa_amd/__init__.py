@@ -1,1 +1,285 @@
-"""Block top-k / vote-union sparse decode attention for MI355X (gfx950)."""
+"""Block top-k / vote-union sparse decode attention for AMD MI355X (gfx950).
+
+Thin Python binding over ``libksa.so`` (C ABI in ``include/ksa.h``).  It only
+marshals arguments: it checks tensor dtype, shape, contiguity and device,
+passes raw device pointers and the current HIP stream, and allocates the
+workspace the library asks for.  Every step of the computation runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback, and a missing or
+unloadable library raises :class:`KsaLibraryError` on first use.
+
+Function names match the C entry points: ``ksa_block_summaries``,
+``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_vote_select``,
+``ksa_dense_decode``, ``ksa_workspace_bytes``, ``ksa_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libksa.so")
+
+KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMALL, KSA_ERR_HIP = range(5)
+KSA_F32, KSA_BF16 = 0, 1
+KSA_SEL_BLOCKS, KSA_SEL_TOKENS = 0, 1
+(KSA_OP_SELECT_TOPK, KSA_OP_SPARSE_BLOCKS, KSA_OP_SPARSE_TOKENS, KSA_OP_VOTE_SELECT,
+ KSA_OP_DENSE) = range(5)
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode", "ksa_vote_select",
+            "ksa_dense_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+
+
+class KsaLibraryError(RuntimeError):
+    """libksa.so is missing or cannot be loaded."""
+
+
+class KsaError(RuntimeError):
+    """A libksa call returned a status other than KSA_OK."""
+
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s: %s" % (call, ksa_status_string(status)))
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``ksa_problem``."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class Selection(ctypes.Structure):
+    """Mirror of ``ksa_selection``."""
+    _fields_ = [("kind", ctypes.c_int32), ("idx", ctypes.c_void_p), ("count", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libksa.so once and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise KsaLibraryError(
+                "libksa.so not found at %s; build it with "
+                "`python -m sparse_attention_decode_ksa_amd.build`" % path)
+        try:
+            lib = ctypes.CDLL(path)
+        except OSError as e:
+            raise KsaLibraryError("cannot load %s: %s" % (path, e)) from e
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        PP = ctypes.POINTER(Problem)
+        lib.ksa_block_summaries.argtypes = [PP, P, P, I32, I32, P]
+        lib.ksa_select_topk.argtypes = [PP, P, P, I32, P, P, P, SZ, P]
+        lib.ksa_sparse_decode.argtypes = [PP, P, P, P, ctypes.POINTER(Selection), P, P, P, SZ, P]
+        lib.ksa_vote_select.argtypes = [PP, P, P, I32, I32, P, P, P, SZ, P]
+        lib.ksa_dense_decode.argtypes = [PP, P, P, P, P, P, P, SZ, P]
+        lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
+        lib.ksa_workspace_bytes.restype = SZ
+        lib.ksa_status_string.argtypes = [ctypes.c_int]
+        lib.ksa_status_string.restype = ctypes.c_char_p
+        lib.ksa_version.argtypes = []
+        lib.ksa_version.restype = ctypes.c_char_p
+        for name in ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
+                     "ksa_vote_select", "ksa_dense_decode"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def ksa_status_string(status: int) -> str:
+    return load_library().ksa_status_string(int(status)).decode()
+
+
+def ksa_version() -> str:
+    return load_library().ksa_version().decode()
+
+
+# ----------------------------------------------------------------------------- marshalling
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KSA_BF16
+    if t.dtype == torch.float32:
+        return KSA_F32
+    raise TypeError("KV dtype must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, seq_len: int, block_size: int = 1,
+                 sm_scale: float = 0.0) -> Problem:
+    """Problem for q [B,Hq,D] and k [B,Hkv,T_cap,D] with T = seq_len."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B,Hq,D] and k [B,Hkv,T_cap,D]")
+    B, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q %s and k %s disagree" % (tuple(q.shape), tuple(k.shape)))
+    return Problem(B, Hq, k.shape[1], D, int(seq_len), k.shape[2], int(block_size),
+                   _dtype_code(k), float(sm_scale))
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, call: str):
+    if status != KSA_OK:
+        raise KsaError(status, call)
+
+
+def ksa_workspace_bytes(problem: Problem, op: int, param: int) -> int:
+    n = load_library().ksa_workspace_bytes(ctypes.byref(problem), int(op), int(param))
+    if n == SIZE_MAX:
+        raise KsaError(KSA_ERR_INVALID_ARGUMENT, "ksa_workspace_bytes")
+    return n
+
+
+def _workspace(problem: Problem, op: int, param: int, device, workspace):
+    need = ksa_workspace_bytes(problem, op, param)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise KsaError(KSA_ERR_WORKSPACE_TOO_SMALL, "workspace")
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def nblocks(n: int, bs: int) -> int:
+    return (n + bs - 1) // bs
+
+
+# ----------------------------------------------------------------------------- entry points
+def ksa_block_summaries(k: torch.Tensor, summaries: torch.Tensor, seq_len: int, block_size: int,
+                        first_block: int = 0, num_blocks: Optional[int] = None,
+                        stream=None) -> torch.Tensor:
+    """Mean key of blocks [first_block, first_block + num_blocks) of every
+    (sequence, KV head), written into summaries [B,Hkv,ceil(T_cap/Bs),D]."""
+    lib = load_library()
+    B, Hkv, Tcap, D = k.shape
+    prob = Problem(B, Hkv, Hkv, D, int(seq_len), Tcap, int(block_size), _dtype_code(k), 0.0)
+    if num_blocks is None:
+        num_blocks = nblocks(seq_len, block_size) - first_block
+    pk = _dev(k, "k")
+    ps = _dev(summaries, "summaries", k.dtype, (B, Hkv, nblocks(Tcap, block_size), D))
+    _check(lib.ksa_block_summaries(ctypes.byref(prob), pk, ps, int(first_block), int(num_blocks),
+                                   _stream(stream)), "ksa_block_summaries")
+    return summaries
+
+
+def ksa_select_topk(q: torch.Tensor, summaries: torch.Tensor, seq_len: int, block_size: int,
+                    top_k: int, max_seq_len: Optional[int] = None, block_idx=None,
+                    block_scores=None, want_scores: bool = False, sm_scale: float = 0.0,
+                    workspace=None, stream=None):
+    """Top-k blocks per (sequence, KV head) -> block_idx [B,Hkv,min(k,NB)] int32
+    (and block_scores [B,Hkv,NB] fp32 when asked)."""
+    lib = load_library()
+    B, Hkv, nbcap, D = summaries.shape
+    Tcap = max_seq_len if max_seq_len is not None else nbcap * block_size
+    prob = Problem(B, q.shape[1], Hkv, D, int(seq_len), int(Tcap), int(block_size),
+                   _dtype_code(summaries), float(sm_scale))
+    nb = nblocks(seq_len, block_size)
+    keff = min(top_k, nb)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, keff), dtype=torch.int32, device=q.device)
+    if want_scores and block_scores is None:
+        block_scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_SELECT_TOPK, top_k, q.device, workspace)
+    _check(lib.ksa_select_topk(ctypes.byref(prob), _dev(q, "q", summaries.dtype, (B, prob.num_q_heads, D)),
+                               _dev(summaries, "summaries"), int(top_k),
+                               _dev(block_idx, "block_idx", torch.int32, (B, Hkv, keff)),
+                               _dev(block_scores, "block_scores", torch.float32, (B, Hkv, nb)),
+                               pws, nws, _stream(stream)), "ksa_select_topk")
+    return (block_idx, block_scores) if block_scores is not None else block_idx
+
+
+def ksa_sparse_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: int,
+                      idx: torch.Tensor, kind: int = KSA_SEL_BLOCKS, block_size: int = 1,
+                      out=None, lse=None, want_lse: bool = True, sm_scale: float = 0.0,
+                      workspace=None, stream=None):
+    """Attention of every query head over the selected blocks (kind BLOCKS,
+    idx [B,Hkv,count]) or the shared token list (kind TOKENS, idx [B,count]).
+    Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None)."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len, block_size, sm_scale)
+    B, Hq, D = q.shape
+    count = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ishape = (B, prob.num_kv_heads, count) if kind == KSA_SEL_BLOCKS else (B, count)
+    sel = Selection(int(kind), _dev(idx, "idx", torch.int32, ishape), int(count))
+    op = KSA_OP_SPARSE_BLOCKS if kind == KSA_SEL_BLOCKS else KSA_OP_SPARSE_TOKENS
+    ws, pws, nws = _workspace(prob, op, count, q.device, workspace)
+    _check(lib.ksa_sparse_decode(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
+                                 _dev(v, "v", k.dtype, k.shape), ctypes.byref(sel),
+                                 _dev(out, "out", torch.float32, (B, Hq, D)),
+                                 _dev(lse, "lse", torch.float32, (B, Hq)), pws, nws,
+                                 _stream(stream)), "ksa_sparse_decode")
+    return out, lse
+
+
+def ksa_vote_select(q: torch.Tensor, k: torch.Tensor, seq_len: int, token_budget: int,
+                    recent_window: int, token_idx=None, votes=None, want_votes: bool = False,
+                    workspace=None, stream=None):
+    """Shared token set [B, min(N,T)] int32 of the vote-union variant (and the
+    per-token votes [B,T] uint8 when asked)."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len)
+    B = q.shape[0]
+    n_out = min(token_budget, seq_len)
+    if token_idx is None:
+        token_idx = torch.empty((B, n_out), dtype=torch.int32, device=q.device)
+    if want_votes and votes is None:
+        votes = torch.empty((B, seq_len), dtype=torch.uint8, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_SELECT, token_budget, q.device, workspace)
+    _check(lib.ksa_vote_select(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
+                               int(token_budget), int(recent_window),
+                               _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
+                               _dev(votes, "votes", torch.uint8, (B, seq_len)), pws, nws,
+                               _stream(stream)), "ksa_vote_select")
+    return (token_idx, votes) if votes is not None else token_idx
+
+
+def ksa_dense_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: int, out=None,
+                     lse=None, want_lse: bool = True, sm_scale: float = 0.0, workspace=None,
+                     stream=None):
+    """Exact attention of every query head over all T tokens."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len, 1, sm_scale)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_DENSE, 0, q.device, workspace)
+    _check(lib.ksa_dense_decode(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
+                                _dev(v, "v", k.dtype, k.shape),
+                                _dev(out, "out", torch.float32, (B, Hq, D)),
+                                _dev(lse, "lse", torch.float32, (B, Hq)), pws, nws,
+                                _stream(stream)), "ksa_dense_decode")
+    return out, lse

@@ -1,0 +1,68 @@
+"""Build libksa.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Run as ``python -m sparse_attention_decode_ksa_amd.build``; the repository's
+``__graft_entry__.build()`` calls :func:`build_library` too.  Object files go to
+``_build/`` at the repository root; the shared library is written next to this
+file, where the Python binding loads it from.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libksa.so")
+OBJDIR = os.path.join(ROOT, "_build", "ksa")
+SOURCES = ["api.hip", "summaries.hip", "select.hip", "attention.hip", "vote.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libksa)")
+
+
+def compile_flags() -> list[str]:
+    return [
+        "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+        # packed-fp32 VALU forms are kept out of every kernel
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I" + os.path.join(ROOT, "include"),
+    ]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-8000:]))
+    return obj
+
+
+def build_library(jobs: int | None = None) -> str:
+    """Compile every source and link libksa.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-8000:]))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library())
+    sys.exit(0)

@@ -1,0 +1,203 @@
+// api.hip -- the extern "C" entry points of libksa (declared in
+// include/ksa.h): host-side argument validation, workspace sizing and launch
+// selection.  Validation is pure host code that runs before any HIP call, so
+// an invalid call launches nothing and writes nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include <new>
+
+#include "ksa_internal.h"
+
+namespace ksa {
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool supported_shape(const ksa_problem& p) {
+  if (p.head_dim != 64 && p.head_dim != 128) return false;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  if ((int64_t)p.batch * p.num_kv_heads * (int64_t)p.max_seq_len * p.head_dim >= kMaxElems)
+    return false;
+  return true;
+}
+
+// Checks the fields every call uses; INVALID for impossible shapes,
+// UNSUPPORTED for valid ones outside this build.
+ksa_status check_problem(const ksa_problem* p, bool needs_block_size) {
+  if (!p) return KSA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (p->num_q_heads % p->num_kv_heads != 0) return KSA_ERR_INVALID_ARGUMENT;
+  if (p->seq_len < 1 || p->max_seq_len < p->seq_len) return KSA_ERR_INVALID_ARGUMENT;
+  if (needs_block_size && p->block_size < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != KSA_F32 && p->dtype != KSA_BF16) return KSA_ERR_INVALID_ARGUMENT;
+  if (!(p->sm_scale == p->sm_scale) || isinf(p->sm_scale)) return KSA_ERR_INVALID_ARGUMENT;
+  if (!supported_shape(*p)) return KSA_ERR_UNSUPPORTED;
+  return KSA_OK;
+}
+
+Dims make_dims(const ksa_problem& p) {
+  Dims d;
+  d.B = p.batch;
+  d.Hq = p.num_q_heads;
+  d.Hkv = p.num_kv_heads;
+  d.G = p.num_q_heads / p.num_kv_heads;
+  d.D = p.head_dim;
+  d.T = p.seq_len;
+  d.Tcap = p.max_seq_len;
+  d.Bs = p.block_size >= 1 ? p.block_size : 1;
+  d.NB = ceil_div(d.T, d.Bs);
+  d.NBcap = ceil_div(d.Tcap, d.Bs);
+  d.dtype = p.dtype;
+  d.scale = p.sm_scale > 0.f ? p.sm_scale : 1.0f / sqrtf((float)p.head_dim);
+  return d;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+bool aligned4(const void* ptr) { return ((uintptr_t)ptr & 3u) == 0; }
+
+ksa_status from_hip(hipError_t e) { return e == hipSuccess ? KSA_OK : KSA_ERR_HIP; }
+
+size_t workspace_for(const ksa_problem& p, int32_t op, int32_t param) {
+  const Dims d = make_dims(p);
+  switch (op) {
+    case KSA_OP_SELECT_TOPK:
+      return 0;
+    case KSA_OP_SPARSE_BLOCKS:
+      return attention_workspace_bytes(d, plan_attention(d, (int64_t)param * d.Bs));
+    case KSA_OP_SPARSE_TOKENS:
+      return attention_workspace_bytes(d, plan_attention(d, param));
+    case KSA_OP_VOTE_SELECT:
+      // bound over every recent_window: W = 0 has the most candidates
+      return plan_vote(d, param, 0).total;
+    case KSA_OP_DENSE:
+      return attention_workspace_bytes(d, plan_attention(d, d.T));
+    default:
+      return SIZE_MAX;
+  }
+}
+
+}  // namespace
+}  // namespace ksa
+
+using namespace ksa;
+
+extern "C" {
+
+const char* ksa_version(void) { return "0.1.0"; }
+
+const char* ksa_status_string(ksa_status status) {
+  switch (status) {
+    case KSA_OK: return "KSA_OK: success";
+    case KSA_ERR_INVALID_ARGUMENT: return "KSA_ERR_INVALID_ARGUMENT: an argument is out of range";
+    case KSA_ERR_UNSUPPORTED: return "KSA_ERR_UNSUPPORTED: valid arguments outside what this build handles";
+    case KSA_ERR_WORKSPACE_TOO_SMALL: return "KSA_ERR_WORKSPACE_TOO_SMALL: workspace smaller than ksa_workspace_bytes()";
+    case KSA_ERR_HIP: return "KSA_ERR_HIP: a HIP kernel launch failed";
+    default: return "unknown ksa_status";
+  }
+}
+
+size_t ksa_workspace_bytes(const ksa_problem* problem, int32_t op, int32_t param) {
+  const bool blocks = op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS;
+  if (check_problem(problem, blocks) != KSA_OK) return SIZE_MAX;
+  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_DENSE) return SIZE_MAX;
+  if (op != KSA_OP_DENSE && param < 1) return SIZE_MAX;
+  return workspace_for(*problem, op, param);
+}
+
+ksa_status ksa_block_summaries(const ksa_problem* problem, const void* k, void* summaries,
+                               int32_t first_block, int32_t num_blocks, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!k || !summaries || !aligned16(k) || !aligned16(summaries)) return KSA_ERR_INVALID_ARGUMENT;
+  if (first_block < 0 || num_blocks < 1 || (int64_t)first_block + num_blocks > d.NB)
+    return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_block_summaries(d, k, summaries, first_block, num_blocks,
+                                         (hipStream_t)stream));
+}
+
+ksa_status ksa_select_topk(const ksa_problem* problem, const void* q, const void* summaries,
+                           int32_t top_k, int32_t* block_idx, float* block_scores, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !summaries || !block_idx || top_k < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(summaries) || !aligned4(block_idx) ||
+      (block_scores && !aligned4(block_scores)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.NB > kSelectMaxBlocks) return KSA_ERR_UNSUPPORTED;
+  if (workspace_bytes < workspace_for(*problem, KSA_OP_SELECT_TOPK, top_k))
+    return KSA_ERR_WORKSPACE_TOO_SMALL;
+  (void)workspace;
+  const int keff = top_k < d.NB ? top_k : d.NB;
+  return from_hip(launch_select_topk(d, q, summaries, keff, block_idx, block_scores,
+                                     (hipStream_t)stream));
+}
+
+ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const void* k,
+                             const void* v, const ksa_selection* sel, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!sel) return KSA_ERR_INVALID_ARGUMENT;
+  const bool blocks = sel->kind == KSA_SEL_BLOCKS;
+  if (!blocks && sel->kind != KSA_SEL_TOKENS) return KSA_ERR_INVALID_ARGUMENT;
+  ksa_status st = check_problem(problem, blocks);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !v || !out || !sel->idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(out) || !aligned4(sel->idx) ||
+      (lse && !aligned4(lse)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (sel->count < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (blocks && sel->count > d.NB) return KSA_ERR_INVALID_ARGUMENT;
+  if (!blocks && sel->count > d.T) return KSA_ERR_INVALID_ARGUMENT;
+  if (blocks && (int64_t)sel->count * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
+  const int64_t ltot = blocks ? (int64_t)sel->count * d.Bs : sel->count;
+  const AttnPlan plan = plan_attention(d, ltot);
+  const size_t need = attention_workspace_bytes(d, plan);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_attention(d, blocks ? 0 : 1, q, k, v, sel->idx, sel->count, out, lse,
+                                   workspace, plan, (hipStream_t)stream));
+}
+
+ksa_status ksa_vote_select(const ksa_problem* problem, const void* q, const void* k,
+                           int32_t token_budget, int32_t recent_window, int32_t* token_idx,
+                           uint8_t* votes, void* workspace, size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, false);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned4(token_idx)) return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;  // vote counts are bytes
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan plan = plan_vote(d, token_budget, recent_window);
+  if (workspace_bytes < plan.total) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.total && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_vote_select(d, q, k, token_budget, recent_window, token_idx, votes,
+                                     workspace, plan, (hipStream_t)stream));
+}
+
+ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const void* k,
+                            const void* v, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, false);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !v || !out) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(out) || (lse && !aligned4(lse)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  const AttnPlan plan = plan_attention(d, d.T);
+  const size_t need = attention_workspace_bytes(d, plan);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_attention(d, 2, q, k, v, nullptr, 0, out, lse, workspace, plan,
+                                   (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,378 @@
+// attention.hip -- decode attention of every query head over a token list of
+// its KV head: the selected blocks (Kinetics explainer, section 五), one token
+// set shared by every head of a sequence (LessIsMore explainer, section 五),
+// or the dense range [0, T) (Kinetics explainer, section 四).
+//
+// Work decomposition.  A (sequence b, KV head g) row's token list is a
+// sequence of "virtual positions" p = 0..L-1 (block list: p -> token
+// idx[p / Bs] * Bs + p % Bs; token list: p -> idx[p]; dense: p -> p).  It is
+// cut into chunks of CH positions.  `splits` workgroups share a row; each
+// covers a contiguous run of chunks and its waves take the run's chunks
+// round-robin.
+//
+// Inside a wave, a group of LPT lanes (a "slot") holds one token row: each
+// lane owns 16 bytes (8 bf16 or 4 fp32 channels) of K and V, so one 16-byte
+// load per lane reads 64/LPT consecutive-position rows and a Bs-aligned block
+// of 16 bf16 tokens is four fully used 1 KB loads.  All G query heads of the
+// group are handled by the same lanes, so each K/V byte is read once per
+// group (the GQA sharing the LessIsMore explainer's kernel relies on).
+//
+// Numerics.  q is pre-scaled by sm_scale*log2(e); logits accumulate in fp32
+// (bf16 x bf16 products are exact), the per-slot online softmax keeps
+// (m, l, acc) in the log2 domain with hardware exp2, and P stays fp32 for the
+// P.V accumulation.  States are merged slot -> wave -> workgroup -> split in
+// a fixed order, so results are bitwise repeatable.
+//
+// Pipelining.  While a wave computes chunk c it has the K/V loads of its next
+// chunk and the index loads of the chunk after that in flight.
+#include <float.h>
+
+#include "ksa_device.h"
+#include "ksa_internal.h"
+
+namespace ksa {
+namespace {
+
+constexpr int kMaxWaves = 8;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  int count;       // idx entries per row (block list) or per sequence (token list)
+  Dims d;
+  int ltot;        // virtual positions per row
+  int bs_shift;    // log2(Bs) when Bs is a power of two, else -1
+  int splits, cps;
+  float qscale;    // sm_scale * log2(e)
+  float* out;
+  float* lse;
+  float* part_acc; // [rows, splits, G, D]
+  float* part_ml;  // [rows, splits, G, 2]
+};
+
+template <int KIND, int CH, int SPW, int NI>
+__device__ __forceinline__ void resolve_chunk(const AttnArgs& a, int row, int b, int slot, int c,
+                                              int* tok, bool* ok) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int p = c * CH + i * SPW + slot;
+    if constexpr (KIND == 2) {
+      ok[i] = p < a.d.T;
+      tok[i] = ok[i] ? p : 0;
+    } else if constexpr (KIND == 1) {
+      ok[i] = p < a.ltot;
+      tok[i] = ok[i] ? a.idx[(int64_t)b * a.count + p] : 0;
+    } else {
+      ok[i] = p < a.ltot;
+      int q, r;
+      if (a.bs_shift >= 0) {
+        q = p >> a.bs_shift;
+        r = p & ((1 << a.bs_shift) - 1);
+      } else {
+        q = p / a.d.Bs;
+        r = p - q * a.d.Bs;
+      }
+      const int blk = ok[i] ? a.idx[(int64_t)row * a.count + q] : 0;
+      const int t = blk * a.d.Bs + r;
+      ok[i] = ok[i] && t < a.d.T;
+      tok[i] = ok[i] ? t : 0;
+    }
+  }
+}
+
+template <typename T, int D, int G, int KIND>
+__global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a) {
+  constexpr int EPL = KV<T>::EPL;
+  constexpr int LPT = D / EPL;
+  constexpr int SPW = 64 / LPT;
+  constexpr int NI = kLoadsPerChunk;
+  constexpr int CH = SPW * NI;
+  __shared__ float s_m[kMaxWaves][G];
+  __shared__ float s_l[kMaxWaves][G];
+  __shared__ float s_acc[kMaxWaves][G][D];
+
+  const Dims& d = a.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int slot = lane / LPT, li = lane % LPT;
+  const int split = blockIdx.x % a.splits;
+  const int row = blockIdx.x / a.splits;
+  const int b = row / d.Hkv, g = row - b * d.Hkv;
+  const int64_t kvrow = (int64_t)row * d.Tcap * D + li * EPL;
+  const T* kbase = (const T*)a.k + kvrow;
+  const T* vbase = (const T*)a.v + kvrow;
+
+  float qv[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    KV<T>::widen(ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL), qv[h]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
+  }
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -FLT_MAX;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int nchunks = (a.ltot + CH - 1) / CH;
+  const int c_begin = split * a.cps;
+  const int c_end = min(c_begin + a.cps, nchunks);
+  int c = c_begin + wave;
+  if (c < c_end) {
+    int tok[NI];
+    bool ok[NI];
+    resolve_chunk<KIND, CH, SPW, NI>(a, row, b, slot, c, tok, ok);
+    uint4 kr[NI], vr[NI];
+    bool okr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kr[i] = ld16(kbase + (int64_t)tok[i] * D);
+      vr[i] = ld16(vbase + (int64_t)tok[i] * D);
+      okr[i] = ok[i];
+    }
+    int cn = c + nw;
+    if (cn < c_end) resolve_chunk<KIND, CH, SPW, NI>(a, row, b, slot, cn, tok, ok);
+    for (; c < c_end; c += nw) {
+      uint4 kc[NI], vc[NI];
+      bool okc[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        kc[i] = kr[i];
+        vc[i] = vr[i];
+        okc[i] = okr[i];
+      }
+      if (cn < c_end) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          kr[i] = ld16(kbase + (int64_t)tok[i] * D);
+          vr[i] = ld16(vbase + (int64_t)tok[i] * D);
+          okr[i] = ok[i];
+        }
+      }
+      const int cnn = cn + nw;
+      if (cnn < c_end) resolve_chunk<KIND, CH, SPW, NI>(a, row, b, slot, cnn, tok, ok);
+      cn = cnn;
+
+      // logits of the NI tokens for every head of the group
+      float s[NI][G];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float f[EPL];
+        KV<T>::widen(kc[i], f);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
+          s[i][h] = group_sum<LPT>(p);
+        }
+      }
+      // online softmax update, once per chunk
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mx = m[h];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          if (okc[i]) mx = fmaxf(mx, s[i][h]);
+        const float alpha = fast_exp2(m[h] - mx);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const float p = okc[i] ? fast_exp2(s[i][h] - mx) : 0.f;
+          s[i][h] = p;
+          ps += p;
+        }
+        l[h] = fmaf(l[h], alpha, ps);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        m[h] = mx;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float f[EPL];
+        KV<T>::widen(vc[i], f);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[i][h], f[e], acc[h][e]);
+      }
+    }
+  }
+
+  // merge the wave's slots (lanes li, li+LPT, ... hold the same channels)
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(m[h], off);
+      const float lo = __shfl_xor(l[h], off);
+      const float M = fmaxf(m[h], mo);
+      const float sa = fast_exp2(m[h] - M), sb = fast_exp2(mo - M);
+      l[h] = l[h] * sa + lo * sb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * sa + __shfl_xor(acc[h][e], off) * sb;
+      m[h] = M;
+    }
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (li == 0) {
+        s_m[wave][h] = m[h];
+        s_l[wave][h] = l[h];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h][li * EPL + e] = acc[h][e];
+    }
+  }
+  __syncthreads();
+
+  // merge the waves; write the row's output or this split's partial state
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+    const int h = o / D, e = o - (o / D) * D;
+    float M = -FLT_MAX;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float sc = fast_exp2(s_m[w][h] - M);
+      L = fmaf(s_l[w][h], sc, L);
+      A = fmaf(s_acc[w][h][e], sc, A);
+    }
+    if (a.splits == 1) {
+      const int64_t oh = (int64_t)b * d.Hq + g * G + h;
+      a.out[oh * D + e] = A / L;
+      if (e == 0 && a.lse) a.lse[oh] = (M + log2f(L)) * kLn2;
+    } else {
+      const int64_t pi = ((int64_t)row * a.splits + split) * G + h;
+      a.part_acc[pi * D + e] = A;
+      if (e == 0) {
+        a.part_ml[pi * 2] = M;
+        a.part_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Fixed-order merge of the split partial states of each row.
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_acc,
+                                                         const float* __restrict__ part_ml,
+                                                         int splits, Dims d, float* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  const int row = blockIdx.x;
+  const int b = row / d.Hkv, g = row - b * d.Hkv;
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+    const int h = o / D, e = o - (o / D) * D;
+    const int64_t p0 = (int64_t)row * splits * G + h;
+    float M = -FLT_MAX;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(p0 + (int64_t)s * G) * 2]);
+    float L = 0.f, A = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const int64_t pi = p0 + (int64_t)s * G;
+      const float sc = fast_exp2(part_ml[pi * 2] - M);
+      L = fmaf(part_ml[pi * 2 + 1], sc, L);
+      A = fmaf(part_acc[pi * D + e], sc, A);
+    }
+    const int64_t oh = (int64_t)b * d.Hq + g * G + h;
+    out[oh * D + e] = A / L;
+    if (e == 0 && lse) lse[oh] = (M + log2f(L)) * kLn2;
+  }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStream_t s) {
+  const int rows = a.d.B * a.d.Hkv;
+  const dim3 grid(rows * p.splits), block(p.nw * 64);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 0>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 1>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 2>), grid, block, 0, s, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(rows), dim3(256), 0, s, a.part_acc, a.part_ml,
+                     p.splits, a.d, a.out, a.lse);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_g(const AttnArgs& a, int kind, const AttnPlan& p, hipStream_t s) {
+  switch (a.d.G) {
+    case 1: return launch_typed<T, D, 1>(a, kind, p, s);
+    case 2: return launch_typed<T, D, 2>(a, kind, p, s);
+    case 4: return launch_typed<T, D, 4>(a, kind, p, s);
+    default: return launch_typed<T, D, 8>(a, kind, p, s);
+  }
+}
+
+}  // namespace
+
+AttnPlan plan_attention(const Dims& d, int64_t tokens_per_row) {
+  const int ch = chunk_tokens(d);
+  const int64_t chunks = (tokens_per_row + ch - 1) / ch;
+  const int64_t rows = (int64_t)d.B * d.Hkv;
+  const int64_t kTargetWaves = 4096;  // 256 CUs x 16 resident waves
+  const int64_t kMinChunksPerWave = 4;
+  const int64_t want = (kTargetWaves + rows - 1) / rows;
+  const int64_t useful = chunks / kMinChunksPerWave > 1 ? chunks / kMinChunksPerWave : 1;
+  const int64_t wpr = want < useful ? want : useful;
+  int nw = 1;
+  while (nw < kMaxWaves && nw * 2 <= wpr) nw *= 2;
+  int64_t splits = (wpr + nw - 1) / nw;
+  if (splits < 1) splits = 1;
+  int64_t cps = (chunks + splits - 1) / splits;
+  if (cps < 1) cps = 1;
+  splits = (chunks + cps - 1) / cps;
+  if (splits < 1) splits = 1;
+  return AttnPlan{nw, (int)splits, (int)cps, ch};
+}
+
+size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p) {
+  if (p.splits <= 1) return 0;
+  const size_t rows = (size_t)d.B * d.Hkv;
+  return rows * p.splits * d.G * (size_t)(d.D + 2) * sizeof(float);
+}
+
+hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
+                            const int32_t* idx, int count, float* out, float* lse, void* workspace,
+                            const AttnPlan& plan, hipStream_t stream) {
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.idx = idx;
+  a.count = count;
+  a.d = d;
+  a.ltot = kind == 0 ? count * d.Bs : (kind == 1 ? count : d.T);
+  a.bs_shift = -1;
+  if (kind == 0 && (d.Bs & (d.Bs - 1)) == 0) {
+    int sh = 0;
+    while ((1 << sh) < d.Bs) ++sh;
+    a.bs_shift = sh;
+  }
+  a.splits = plan.splits;
+  a.cps = plan.cps;
+  a.qscale = d.scale * kLog2e;
+  a.out = out;
+  a.lse = lse;
+  const size_t rows = (size_t)d.B * d.Hkv;
+  a.part_acc = (float*)workspace;
+  a.part_ml = workspace ? (float*)workspace + rows * plan.splits * d.G * d.D : nullptr;
+  if (d.dtype == KSA_BF16) {
+    if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);
+    return launch_g<uint16_t, 128>(a, kind, plan, stream);
+  }
+  if (d.D == 64) return launch_g<float, 64>(a, kind, plan, stream);
+  return launch_g<float, 128>(a, kind, plan, stream);
+}
+
+}  // namespace ksa

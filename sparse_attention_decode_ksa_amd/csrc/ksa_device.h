@@ -1,0 +1,129 @@
+// ksa_device.h -- device-side helpers for the gfx950 kernels of libksa:
+// 16-byte KV loads and widening, 64-wide wavefront reductions through DPP,
+// order-preserving 32-bit keys for fp32 scores, and wave/block scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ksa {
+
+// ---------------------------------------------------------------- KV types
+// A lane always moves 16 bytes: 8 bf16 (raw uint16 bit patterns) or 4 fp32.
+template <typename T>
+struct KV;
+
+template <>
+struct KV<uint16_t> {
+  static constexpr int EPL = 8;
+  // bf16 -> fp32 is exact: the bf16 bits are the fp32's upper half.
+  __device__ __forceinline__ static void widen(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xffff0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xffff0000u);
+    f[4] = __uint_as_float(u.z << 16);
+    f[5] = __uint_as_float(u.z & 0xffff0000u);
+    f[6] = __uint_as_float(u.w << 16);
+    f[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+};
+
+template <>
+struct KV<float> {
+  static constexpr int EPL = 4;
+  __device__ __forceinline__ static void widen(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ---------------------------------------------------------------- DPP
+// Lane permutations inside a 16-lane row (gfx9 DPP controls).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of LPT lanes (LPT in {8, 16, 32}); every lane
+// of the group receives the group's sum.
+template <int LPT>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPT == 8 || LPT == 16 || LPT == 32, "lanes per token");
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  if constexpr (LPT >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (LPT >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------- keys
+// Order-preserving map of an fp32 score to uint32: larger score -> larger
+// key; -0 is folded onto +0 so that equal scores give equal keys.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- scans
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the workgroup (blockDim.x a multiple of 64,
+// at most 1024 threads).  `scratch` holds 17 uint64 in LDS.  Returns the
+// exclusive prefix and writes the workgroup total to *total.  Contains
+// barriers: every thread of the workgroup must call it.
+__device__ __forceinline__ uint64_t block_excl_scan64(uint64_t x, uint64_t* scratch,
+                                                      uint64_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  uint64_t incl = wave_incl_scan64(x);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t w = lane < nwaves ? scratch[lane] : 0;
+    uint64_t wi = wave_incl_scan64(w);
+    if (lane < nwaves) scratch[lane] = wi - w;
+    if (lane == 63) scratch[16] = wi;
+  }
+  __syncthreads();
+  uint64_t r = scratch[wave] + incl - x;
+  *total = scratch[16];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace ksa

@@ -1,0 +1,67 @@
+// ksa_internal.h -- shapes, launch plans and launcher declarations shared by
+// the host side of libksa (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ksa.h"
+
+namespace ksa {
+
+// Problem shape with derived sizes.
+struct Dims {
+  int B, Hq, Hkv, G, D, T, Tcap, Bs, NB, NBcap;
+  int dtype;    // KSA_F32 or KSA_BF16
+  float scale;  // softmax scale
+};
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Elements one lane moves in one 16-byte load.
+inline int elems_per_lane(int dtype) { return dtype == KSA_F32 ? 4 : 8; }
+// Lanes that together hold one token row of D elements.
+inline int lanes_per_token(const Dims& d) { return d.D / elems_per_lane(d.dtype); }
+// Token rows one wave covers with one 16-byte load per lane.
+inline int slots_per_wave(const Dims& d) { return 64 / lanes_per_token(d); }
+
+// 16-byte loads per lane per chunk for K (and again for V) in the attention
+// kernels; a chunk is slots_per_wave * kLoadsPerChunk tokens.
+constexpr int kLoadsPerChunk = 4;
+inline int chunk_tokens(const Dims& d) { return slots_per_wave(d) * kLoadsPerChunk; }
+
+// Attention launch: `splits` workgroups of `nw` waves per (sequence, KV
+// head) row; each workgroup covers `cps` chunks of the row's token list.
+struct AttnPlan {
+  int nw, splits, cps, chunk;
+};
+AttnPlan plan_attention(const Dims& d, int64_t tokens_per_row);
+size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p);
+
+// Attention over a row-wise token list.  kind: 0 = selected blocks,
+// 1 = shared token list, 2 = dense range [0, T).
+hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
+                            const int32_t* idx, int count, float* out, float* lse,
+                            void* workspace, const AttnPlan& plan, hipStream_t stream);
+
+hipError_t launch_block_summaries(const Dims& d, const void* k, void* summaries, int first_block,
+                                  int num_blocks, hipStream_t stream);
+
+constexpr int kSelectMaxBlocks = 15360;  // keys live in LDS (60 KB)
+hipError_t launch_select_topk(const Dims& d, const void* q, const void* summaries, int keff,
+                              int32_t* block_idx, float* block_scores, hipStream_t stream);
+
+// Vote-union selection.
+struct VotePlan {
+  int hist;        // C = T - W history tokens (candidates)
+  int words;       // 32-token words per head bitmask
+  int kv;          // N - W picks per head
+  size_t keys_off, bits_off, total;
+};
+VotePlan plan_vote(const Dims& d, int N, int W);
+hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N, int W,
+                              int32_t* token_idx, uint8_t* votes, void* workspace,
+                              const VotePlan& plan, hipStream_t stream);
+
+}  // namespace ksa

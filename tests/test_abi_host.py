@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+entry point include/ksa.h declares, sizes workspaces as a pure function, and
+rejects invalid arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_decode_ksa_amd as ksa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ksa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ksa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_operations():
+    names = declared_functions()
+    for n in ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode", "ksa_vote_select",
+              "ksa_dense_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version"):
+        assert n in names
+    assert set(names) == set(ksa.EXPORTED)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ksa.load_library()
+    raw = ctypes.CDLL(ksa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert re.fullmatch(r"\d+\.\d+\.\d+", ksa.ksa_version())
+    assert lib is ksa.load_library()
+
+
+def test_status_strings():
+    for s in range(5):
+        assert ksa.ksa_status_string(s).startswith("KSA_")
+    assert "unknown" in ksa.ksa_status_string(99)
+
+
+def P(B=2, Hq=4, Hkv=2, D=64, T=1024, Tcap=1024, Bs=16, dtype=ksa.KSA_F32, scale=0.0):
+    return ksa.Problem(B, Hq, Hkv, D, T, Tcap, Bs, dtype, scale)
+
+
+def test_workspace_sizing_is_pure_and_validates():
+    lib = ksa.load_library()
+    p = P()
+    a = ksa.ksa_workspace_bytes(p, ksa.KSA_OP_DENSE, 0)
+    assert a == ksa.ksa_workspace_bytes(p, ksa.KSA_OP_DENSE, 0)
+    assert ksa.ksa_workspace_bytes(p, ksa.KSA_OP_SELECT_TOPK, 8) == 0
+    # the vote workspace holds fp32-sized keys for every (b, h, history token) plus bitmasks
+    p4 = P(B=16, Hq=32, Hkv=8, D=128, T=20000, Tcap=20000, dtype=ksa.KSA_BF16)
+    assert ksa.ksa_workspace_bytes(p4, ksa.KSA_OP_VOTE_SELECT, 2048) >= 16 * 32 * 20000 * 4
+    # T <= N needs no workspace
+    assert ksa.ksa_workspace_bytes(P(T=100, Tcap=100), ksa.KSA_OP_VOTE_SELECT, 2048) == 0
+    bad = [P(Hq=3, Hkv=2), P(T=0), P(Tcap=10, T=20), P(Bs=0), P(B=0)]
+    for b in bad:
+        n = lib.ksa_workspace_bytes(ctypes.byref(b), ksa.KSA_OP_SPARSE_BLOCKS, 4)
+        assert n == ksa.SIZE_MAX
+    assert lib.ksa_workspace_bytes(ctypes.byref(p), 17, 1) == ksa.SIZE_MAX
+    assert lib.ksa_workspace_bytes(None, ksa.KSA_OP_DENSE, 0) == ksa.SIZE_MAX
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    lib = ksa.load_library()
+    null = None
+    p = P()
+    E = ksa.KSA_ERR_INVALID_ARGUMENT
+    U = ksa.KSA_ERR_UNSUPPORTED
+    W = ksa.KSA_ERR_WORKSPACE_TOO_SMALL
+    # summaries: block range outside [0, NB)
+    assert lib.ksa_block_summaries(ctypes.byref(p), FAKE, FAKE, 60, 5, null) == E
+    assert lib.ksa_block_summaries(ctypes.byref(p), FAKE, FAKE, -1, 1, null) == E
+    assert lib.ksa_block_summaries(ctypes.byref(p), FAKE, FAKE, 0, 0, null) == E
+    assert lib.ksa_block_summaries(ctypes.byref(p), null, FAKE, 0, 1, null) == E
+    assert lib.ksa_block_summaries(ctypes.byref(p), ctypes.c_void_p(0x10002), FAKE, 0, 1, null) == E
+    assert lib.ksa_block_summaries(None, FAKE, FAKE, 0, 1, null) == E
+    # select: k <= 0, Hq not a multiple of Hkv, unsupported D / G
+    assert lib.ksa_select_topk(ctypes.byref(p), FAKE, FAKE, 0, FAKE, null, null, 0, null) == E
+    assert lib.ksa_select_topk(ctypes.byref(P(Hq=3)), FAKE, FAKE, 4, FAKE, null, null, 0, null) == E
+    assert lib.ksa_select_topk(ctypes.byref(P(D=96)), FAKE, FAKE, 4, FAKE, null, null, 0, null) == U
+    assert lib.ksa_select_topk(ctypes.byref(P(Hq=6, Hkv=2)), FAKE, FAKE, 4, FAKE, null, null, 0, null) == U
+    assert lib.ksa_select_topk(ctypes.byref(P(T=20000, Tcap=20000, Bs=1)), FAKE, FAKE, 4, FAKE,
+                               null, null, 0, null) == U
+    # sparse: bad kind, count out of range, workspace too small
+    sel = ksa.Selection(7, FAKE, 4)
+    assert lib.ksa_sparse_decode(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(sel), FAKE, null,
+                                 null, 0, null) == E
+    sel = ksa.Selection(ksa.KSA_SEL_BLOCKS, FAKE, 65)  # NB = 64
+    assert lib.ksa_sparse_decode(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(sel), FAKE, null,
+                                 null, 0, null) == E
+    sel = ksa.Selection(ksa.KSA_SEL_TOKENS, FAKE, 0)
+    assert lib.ksa_sparse_decode(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(sel), FAKE, null,
+                                 null, 0, null) == E
+    big = P(B=1, Hq=8, Hkv=1, D=128, T=65536, Tcap=65536, dtype=ksa.KSA_BF16)
+    need = ksa.ksa_workspace_bytes(big, ksa.KSA_OP_DENSE, 0)
+    assert need > 0
+    assert lib.ksa_dense_decode(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, null, FAKE, need - 1,
+                                null) == W
+    # vote: W > N, N < 1, too many heads
+    p4 = P(B=1, Hq=4, Hkv=2, D=64, T=100, Tcap=100)
+    assert lib.ksa_vote_select(ctypes.byref(p4), FAKE, FAKE, 10, 11, FAKE, null, null, 0, null) == E
+    assert lib.ksa_vote_select(ctypes.byref(p4), FAKE, FAKE, 0, 0, FAKE, null, null, 0, null) == E
+    assert lib.ksa_vote_select(ctypes.byref(p4), FAKE, FAKE, 10, -1, FAKE, null, null, 0, null) == E
+    p5 = P(B=1, Hq=256, Hkv=256, D=64, T=100, Tcap=100)
+    assert lib.ksa_vote_select(ctypes.byref(p5), FAKE, FAKE, 10, 2, FAKE, null, null, 0, null) == U
+    need = ksa.ksa_workspace_bytes(p4, ksa.KSA_OP_VOTE_SELECT, 10)
+    assert lib.ksa_vote_select(ctypes.byref(p4), FAKE, FAKE, 10, 2, FAKE, null, FAKE, need - 1,
+                               null) == W
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64)
+    k = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        ksa.ksa_dense_decode(q, k, k, 16)
