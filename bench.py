@@ -1,18 +1,30 @@
-"""Benchmark of one decode step of block top-k sparse attention on one MI355X.
+"""Benchmark of one decode step of sparse attention on one MI355X.
 
-One step = the whole hot path for one layer over one batch: refresh the summary
-of the block holding the newest token, score and select the top-k blocks of
-every (sequence, KV head), and attend the selected blocks with every query
-head.  Steps cycle over `--layers` independent KV caches (distinct seeds), so
-that the bytes a step touches were not touched by the previous steps and the
+Block top-k workloads (c2 default, c3, c5): one step = refresh the summary of
+the block holding the newest token, score and select the top-k blocks of every
+(sequence, KV head), and attend the selected blocks with every query head.
+Vote-union workload (c4): one step = the selection layer's vote (all heads
+score every history token, votes are pooled, the recency window appended) and
+the attention over the shared set; the sparse-layer step (attention over a
+set chosen earlier) is reported beside it.
+
+Steps cycle over several independent KV caches ("layers", distinct seeds) so
+that a step's bytes were not touched by the steps just before it and the
 256 MB Infinity Cache does not serve them.  Inputs are resident in HBM before
-timing starts.  The dense decode of the same shape is timed the same way.
+timing starts.  Dense decode of the same shape is timed the same way.
 
-Prints ONE JSON line (rank 0) with the throughput (sequences x steps per
-second), the roofline of the dominant kernel (the sparse attention call), and
-the fp64 oracle timed on the host as a CPU baseline.
+Each layer's step is captured once into a HIP graph (the C calls are launched
+on the capturing stream) and replayed; graph replay is checked to reproduce
+the eager step's outputs bit for bit.  Timed regions (each bracketed by
+torch.cuda.synchronize() and HIP events on the stream the kernels run on):
+  1. K whole steps back to back (graph replays)  -> value, ms_per_step
+  2. K launches of the dominant call alone        -> roofline.achieved
+  3. dense decode steps                           -> dense, speedup_vs_dense
+  4. K whole steps launched eagerly               -> eager_ms_per_step
+Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+    python bench.py --copy-probe      # a plain 1 GiB copy, to calibrate HBM counters
 """
 from __future__ import annotations
 
@@ -42,6 +54,8 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain copy of 1 GiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -53,13 +67,61 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "gbps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+class Runner:
+    """Prepared C calls: ctypes arguments built once, so a step costs a few
+    microseconds of host time and the GPU never waits on Python."""
+
+    def __init__(self, lib, ksa):
+        self.lib, self.ksa = lib, ksa
+
+    def run(self, call):
+        fn, a = call
+        st = fn(*a)
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (fn.__name__, self.ksa.ksa_status_string(st)))
+
+
+def timed(torch, stream, n, body):
+    """Time n calls of body(i) between two events; returns ms per call."""
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        body(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each (sequence, KV head) row is independent; see DESIGN.md for how it would shard).",
-              file=sys.stderr)
+              "(every (sequence, KV head) row is independent; DESIGN.md describes how it "
+              "would shard).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import numpy as np
     import torch
@@ -69,18 +131,24 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lib = ksa.load_library()
+    R = Runner(lib, ksa)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
-    if w.plant == "tokens":
-        raise SystemExit("the vote-union workload is measured with --workload c4 in a later build")
-    B, Hq, Hkv, D, T, Bs, K = w.B, w.Hq, w.Hkv, w.D, w.T, w.Bs, w.top_k
-    NB = (T + Bs - 1) // Bs
-    keff = min(K, NB)
+    vote = w.plant == "tokens"
+    B, Hq, Hkv, D, T = w.B, w.Hq, w.Hkv, w.D, w.T
     elt = 2 if w.dtype == "bf16" else 4
-    kv_layer_bytes = 2 * B * Hkv * w.cap * D * elt
-    # bytes one step touches: the summaries and the selected K/V rows
-    touched = B * Hkv * (NB + 2 * keff * Bs) * D * elt
+    rows = B * Hkv
+    if vote:
+        N, W = w.token_budget, w.recent_window
+        n_sel = min(N, T)
+        Bs, K, NB, keff = 1, 0, T, 0
+        touched = rows * (T - W) * D * elt + 2 * rows * n_sel * D * elt
+    else:
+        Bs, K = w.Bs, w.top_k
+        NB = (T + Bs - 1) // Bs
+        keff = min(K, NB)
+        touched = rows * (NB + 2 * keff * Bs) * D * elt
     layers = args.layers or max(4, min(8, math.ceil(1.0e9 / touched)))
 
     # ---------------------------------------------------------------- inputs (resident in HBM)
@@ -88,97 +156,121 @@ def main():
     L = []
     for l in range(layers):
         x = make_inputs(w, device=dev, seed=w.seed * 1000 + l)
-        s = torch.empty((B, Hkv, NB, D), dtype=x["k"].dtype, device=dev)
-        ksa.ksa_block_summaries(x["k"], s, T, Bs)  # prefill: every block
-        L.append(dict(q=x["q"], k=x["k"], v=x["v"], s=s,
-                      idx=torch.empty((B, Hkv, keff), dtype=torch.int32, device=dev),
-                      out=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
-                      lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
-                      dout=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
-                      dlse=torch.empty((B, Hq), dtype=torch.float32, device=dev)))
+        x["out"] = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        x["lse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        x["dout"] = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        x["dlse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        if vote:
+            x["idx"] = torch.empty((B, n_sel), dtype=torch.int32, device=dev)
+        else:
+            x["s"] = torch.empty((B, Hkv, NB, D), dtype=x["k"].dtype, device=dev)
+            ksa.ksa_block_summaries(x["k"], x["s"], T, Bs)  # prefill: every block
+            x["idx"] = torch.empty((B, Hkv, keff), dtype=torch.int32, device=dev)
+        L.append(x)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
     # ---------------------------------------------------------------- prepared C calls
     prob = ksa.Problem(B, Hq, Hkv, D, T, w.cap, Bs, ksa.KSA_BF16 if elt == 2 else ksa.KSA_F32, 0.0)
     pp = ctypes.byref(prob)
-    ws_attn = ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SPARSE_BLOCKS, keff)
+    if vote:
+        ws_sel = ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_VOTE_SELECT, N)
+        ws_attn = ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SPARSE_TOKENS, n_sel)
+    else:
+        ws_sel = ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SELECT_TOPK, K)
+        ws_attn = ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SPARSE_BLOCKS, keff)
     ws_dense = ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_DENSE, 0)
-    ws = torch.empty(max(ws_attn, ws_dense, 16), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    wsel = ksa.new_workspace(ws_sel, dev)
+    wat = ksa.new_workspace(max(ws_attn, ws_dense), dev)
+    stream = torch.cuda.Stream(device=dev)  # every call and every capture runs here
     sp = ctypes.c_void_p(stream.cuda_stream)
     V = lambda t: ctypes.c_void_p(t.data_ptr())
     last_block = (T - 1) // Bs
-    calls = []
     for x in L:
-        sel = ksa.Selection(ksa.KSA_SEL_BLOCKS, V(x["idx"]).value, keff)
-        x["sel"] = sel
-        calls.append((
-            (lib.ksa_block_summaries, (pp, V(x["k"]), V(x["s"]), last_block, 1, sp)),
-            (lib.ksa_select_topk, (pp, V(x["q"]), V(x["s"]), K, V(x["idx"]), None, None, 0, sp)),
-            (lib.ksa_sparse_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]), ctypes.byref(sel),
-                                     V(x["out"]), V(x["lse"]), V(ws), ws.numel(), sp)),
-            (lib.ksa_dense_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]), V(x["dout"]),
-                                    V(x["dlse"]), V(ws), ws.numel(), sp)),
-        ))
+        kind = ksa.KSA_SEL_TOKENS if vote else ksa.KSA_SEL_BLOCKS
+        x["sel"] = ksa.Selection(kind, V(x["idx"]).value, n_sel if vote else keff)
+        attn = (lib.ksa_sparse_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]), ctypes.byref(x["sel"]),
+                                        V(x["out"]), V(x["lse"]), V(wat), wat.numel(), sp))
+        dense = (lib.ksa_dense_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]), V(x["dout"]),
+                                        V(x["dlse"]), V(wat), wat.numel(), sp))
+        if vote:
+            select = [(lib.ksa_vote_select, (pp, V(x["q"]), V(x["k"]), N, W, V(x["idx"]), None,
+                                             V(wsel), wsel.numel(), sp))]
+        else:
+            select = [(lib.ksa_block_summaries, (pp, V(x["k"]), V(x["s"]), last_block, 1, sp)),
+                      (lib.ksa_select_topk, (pp, V(x["q"]), V(x["s"]), K, V(x["idx"]), None,
+                                             V(wsel), wsel.numel(), sp))]
+        x["calls"] = dict(select=select, attn=attn, dense=dense)
 
-    def run(fn, a):
-        st = fn(*a)
-        if st != 0:
-            raise RuntimeError("%s failed: %s" % (fn.__name__, ksa.ksa_status_string(st)))
+    def step(i):
+        c = L[i % layers]["calls"]
+        for s_ in c["select"]:
+            R.run(s_)
+        R.run(c["attn"])
 
-    n_ev = args.steps
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    def attn_only(i):
+        R.run(L[i % layers]["calls"]["attn"])
 
-    def sparse_steps(n, timed):
-        for i in range(n):
-            c = calls[i % layers]
-            run(*c[0])
-            run(*c[1])
-            if timed:
-                ev_a[i].record(stream)
-            run(*c[2])
-            if timed:
-                ev_b[i].record(stream)
+    def select_only(i):
+        for s_ in L[i % layers]["calls"]["select"]:
+            R.run(s_)
 
-    # ---------------------------------------------------------------- sparse step
-    sparse_steps(args.warmup, False)
+    def dense_only(i):
+        R.run(L[i % layers]["calls"]["dense"])
+
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    sparse_steps(args.steps, True)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
-    attn_avg_ms = float(np.mean(attn_ms))
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        ms_eager = timed(torch, stream, args.steps, step)            # region 4
 
-    # ---------------------------------------------------------------- dense step
-    for i in range(min(3, args.dense_steps)):
-        run(*calls[i % layers][3])
-    torch.cuda.synchronize()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for i in range(args.dense_steps):
-        run(*calls[i % layers][3])
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dense_ms = d0.elapsed_time(d1) / args.dense_steps
+        # graphs: one step per layer, and one whole cycle over the layers
+        ref = [(x["out"].clone(), x["lse"].clone(), x["idx"].clone()) for x in L]
 
-    # ---------------------------------------------------------------- bytes
-    rows = B * Hkv
-    tok_sel = keff * Bs
-    attn_bytes = (rows * tok_sel * D * elt * 2            # selected K and V rows
-                  + B * Hq * D * elt                      # q
-                  + rows * keff * 4                       # block ids
-                  + B * Hq * (D + 1) * 4)                 # out + lse
-    select_bytes = rows * NB * D * elt + B * Hq * D * elt + rows * keff * 4
-    summ_bytes = rows * (T - last_block * Bs) * D * elt + rows * D * elt
-    step_bytes = attn_bytes + select_bytes + summ_bytes
-    dense_bytes = rows * T * D * elt * 2 + B * Hq * D * elt + B * Hq * (D + 1) * 4
-    achieved_gbps = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+        def capture(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+            return g
+
+        g_step = [capture(lambda l=l: step(l)) for l in range(layers)]
+        g_cycle = capture(lambda: [step(l) for l in range(layers)])
+        g_attn = capture(lambda: [attn_only(l) for l in range(layers)])
+        for x in L:
+            x["out"].zero_(), x["lse"].zero_(), x["idx"].zero_()
+        g_cycle.replay()
+        torch.cuda.synchronize()
+        for l, x in enumerate(L):
+            assert torch.equal(x["out"], ref[l][0]) and torch.equal(x["lse"], ref[l][1]) \
+                and torch.equal(x["idx"], ref[l][2]), "graph replay differs from the eager step"
+
+        full, rest = divmod(args.steps, layers)
+
+        def graph_steps(i):
+            if i < full:
+                g_cycle.replay()
+            else:
+                g_step[i - full].replay()
+
+        ms_step = timed(torch, stream, full + rest, graph_steps) * (full + rest) / args.steps  # 1
+        ms_attn = timed(torch, stream, max(full, 1), lambda i: g_attn.replay()) / layers      # 2
+        ms_select = timed(torch, stream, args.steps, select_only)
+        dense_only(0)
+        ms_dense = timed(torch, stream, args.dense_steps, dense_only)  # region 3
+
+    # ---------------------------------------------------------------- algorithmic bytes
+    q_bytes = B * Hq * D * elt
+    out_bytes = B * Hq * (D + 1) * 4
+    if vote:
+        attn_bytes = rows * n_sel * D * elt * 2 + q_bytes + B * n_sel * 4 + out_bytes
+        select_bytes = rows * (T - W) * D * elt + q_bytes + B * n_sel * 4
+    else:
+        attn_bytes = rows * keff * Bs * D * elt * 2 + q_bytes + rows * keff * 4 + out_bytes
+        select_bytes = (rows * NB * D * elt + q_bytes + rows * keff * 4            # scoring + ids
+                        + rows * (T - last_block * Bs) * D * elt + rows * D * elt)  # summary refresh
+    step_bytes = attn_bytes + select_bytes
+    dense_bytes = rows * T * D * elt * 2 + q_bytes + out_bytes
+    achieved = attn_bytes / (ms_attn * 1e-3) / 1e9
 
     traffic = None
     tr_path = os.path.join(ROOT, "profiles", "traffic_sparse_decode_%s.json" % w.name)
@@ -195,60 +287,71 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         x = L[0]
-        n_seq = B
+        n_seq = B if not vote else min(B, 4)
         sl = slice(0, n_seq)
         qn, kn, vn = as_numpy_bits(x["q"][sl]), as_numpy_bits(x["k"][sl]), as_numpy_bits(x["v"][sl])
-        summ = oracle.block_summaries(kn, T, Bs)  # prefill, untimed
+        if not vote:
+            summ = oracle.block_summaries(kn, T, Bs)  # prefill, untimed
         reps, tcpu = 0, 0.0
         while tcpu < args.cpu_seconds and reps < 50:
             c0 = time.time()
-            oracle.block_summaries(kn, T, Bs, first_block=last_block, num_blocks=1, out=summ)
-            raw, _ = oracle.group_scores(qn, summ, T, Bs, Tcap=w.cap)
-            sel = oracle.topk(raw, K)
-            oracle.attend_blocks(qn, kn, vn, T, Bs, sel)
+            if vote:
+                tok, _ = oracle.vote_select(qn, kn, T, N, W)
+                oracle.attend_tokens(qn, kn, vn, T, tok)
+            else:
+                oracle.block_summaries(kn, T, Bs, first_block=last_block, num_blocks=1, out=summ)
+                raw, _ = oracle.group_scores(qn, summ, T, Bs, Tcap=w.cap)
+                oracle.attend_blocks(qn, kn, vn, T, Bs, oracle.topk(raw, K))
             tcpu += time.time() - c0
             reps += 1
         threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-        cpu = {"value": n_seq * reps / tcpu, "unit": "seqs*steps/s", "cores": threads,
+        cpu = {"value": round(n_seq * reps / tcpu, 2), "unit": "seqs*steps/s", "cores": threads,
                "kind": "oracle",
-               "sample": "%d full steps of all %d sequences of %s (fp64 C oracle, OpenMP), "
-                         "inputs copied from the GPU" % (reps, n_seq, w.name)}
+               "sample": "%d full steps of %d of the %d sequences of %s (fp64 C oracle, OpenMP), "
+                         "inputs copied from the GPU" % (reps, n_seq, B, w.name)}
 
     value = B / (ms_step * 1e-3)
-    dense_value = B / (dense_ms * 1e-3)
+    cfg = {"workload": "%s: %s" % (w.name, w.description), "batch": B, "q_heads": Hq,
+           "kv_heads": Hkv, "head_dim": D, "context": T, "layers_cycled": layers}
+    if vote:
+        cfg.update(token_budget=N, recent_window=W)
+        dom = "ksa_sparse_decode (shared token set)"
+    else:
+        cfg.update(block_size=Bs, top_k_blocks=K)
+        dom = "ksa_sparse_decode (selected blocks, split-K online softmax)"
     line = {
-        "metric": "sparse decode seqs*steps/s per layer (block top-k), with achieved HBM GB/s "
-                  "(% of peak) vs dense",
+        "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
         "value": round(value, 1),
         "unit": "seqs*steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "eager_ms_per_step": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if elt == 2 else "f32",
-        "data": "synthetic (seeded N(0,1) K/V/q with planted blocks and outlier channels)",
-        "config": {"workload": "%s: %s" % (w.name, w.description), "batch": B,
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "context": T,
-                   "block_size": Bs, "top_k_blocks": K, "layers_cycled": layers,
-                   "kv_bytes_per_layer": kv_layer_bytes},
+        "data": "synthetic (seeded N(0,1) K/V/q with planted structure)",
+        "config": cfg,
+        "step_bytes": step_bytes,
         "step_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "step_bytes": step_bytes,
-        "dense": {"ms_per_step": round(dense_ms, 5), "value": round(dense_value, 1),
-                  "gbps": round(dense_bytes / (dense_ms * 1e-3) / 1e9, 1)},
-        "speedup_vs_dense": round(dense_ms / ms_step, 3),
-        "roofline": {"kernel": "ksa_sparse_decode (block attention, split-K online softmax)",
-                     "bound": "hbm", "achieved": round(achieved_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "avg_launch_ms": round(attn_avg_ms, 5),
+        "select": {"ms_eager": round(ms_select, 5),
+                   "gbps": round(select_bytes / (ms_select * 1e-3) / 1e9, 1)},
+        "dense": {"ms_per_step": round(ms_dense, 5), "value": round(B / (ms_dense * 1e-3), 1),
+                  "gbps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)},
+        "speedup_vs_dense": round(ms_dense / ms_step, 3),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(ms_attn, 5),
                      "bytes_per_launch": attn_bytes},
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 2),
     }
+    if vote:
+        line["sparse_layer_step"] = {"ms": round(ms_attn, 5), "value": round(B / (ms_attn * 1e-3), 1),
+                                     "speedup_vs_dense": round(ms_dense / ms_attn, 3)}
     print(json.dumps(line), flush=True)
 
 

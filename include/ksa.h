@@ -35,6 +35,10 @@
  *   - Index buffers are device data and are not validated: out-of-range or
  *     duplicate indices are undefined behaviour.  NaN/Inf inputs are not
  *     supported.
+ *   - Workspaces: a call that needs one takes `workspace` (device memory,
+ *     16-byte aligned, contents irrelevant) of at least ksa_workspace_bytes()
+ *     bytes; it is scratch for that call only.  Concurrent calls need
+ *     distinct workspaces.
  *   - Ranking ties are broken by the lowest index everywhere; every index
  *     list is written in ascending order.
  *   - No C++ exception crosses this interface.
@@ -73,7 +77,7 @@ typedef enum { KSA_F32 = 0, KSA_BF16 = 1 } ksa_dtype;
  * the batch has the same T (the uniform-workload setting of the Kinetics news
  * page, section on the Qwen3-0.6B throughput gain).
  * Supported by this build: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8};
- * dtype fp32 or bf16; B*Hkv*T_cap*D < 2^40. */
+ * dtype fp32 or bf16; B*Hkv*T_cap*D < 2^40; B*Hkv <= 16384. */
 typedef struct {
   int32_t batch;        /* B >= 1 */
   int32_t num_q_heads;  /* Hq >= 1, a multiple of Hkv */
@@ -125,7 +129,7 @@ ksa_status ksa_block_summaries(const ksa_problem* problem, const void* k, void* 
  * block_scores (nullable) [B, Hkv, NB] fp32 receives sm_scale * relevance / G,
  * the mean attention logit of the group against the summary.
  * top_k >= 1.  NB must not exceed 15360.  workspace: ksa_workspace_bytes(
- * problem, KSA_OP_SELECT_TOPK, top_k) bytes (may be 0 and NULL when that is 0). */
+ * problem, KSA_OP_SELECT_TOPK, top_k) bytes (B*Hkv*NB*4: one key per block). */
 ksa_status ksa_select_topk(const ksa_problem* problem, const void* q, const void* summaries,
                            int32_t top_k, int32_t* block_idx, float* block_scores,
                            void* workspace, size_t workspace_bytes, void* stream);

@@ -21,7 +21,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libksa.so")
+# KSA_LIB selects another build of the same library (variant builds for tuning)
+LIB_PATH = os.environ.get("KSA_LIB", os.path.join(_HERE, "libksa.so"))
 
 KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMALL, KSA_ERR_HIP = range(5)
 KSA_F32, KSA_BF16 = 0, 1
@@ -159,10 +160,15 @@ def ksa_workspace_bytes(problem: Problem, op: int, param: int) -> int:
     return n
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A device workspace of at least nbytes (its contents do not matter)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
 def _workspace(problem: Problem, op: int, param: int, device, workspace):
     need = ksa_workspace_bytes(problem, op, param)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        workspace = new_workspace(need, device)
     elif workspace.numel() * workspace.element_size() < need:
         raise KsaError(KSA_ERR_WORKSPACE_TOO_SMALL, "workspace")
     return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()

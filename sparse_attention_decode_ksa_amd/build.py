@@ -36,7 +36,7 @@ def compile_flags() -> list[str]:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I" + os.path.join(ROOT, "include"),
-    ]
+    ] + os.environ.get("KSA_EXTRA_FLAGS", "").split()
 
 
 def _compile(src: str) -> str:
@@ -48,19 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(jobs: int | None = None) -> str:
-    """Compile every source and link libksa.so; returns its path."""
+def build_library(jobs: int | None = None, out: str | None = None, objdir: str | None = None) -> str:
+    """Compile every source and link libksa.so (or `out`); returns its path.
+    KSA_EXTRA_FLAGS adds hipcc flags (e.g. -D tuning macros for a variant build)."""
+    global OBJDIR
+    lib_out = out or LIB
+    if objdir:
+        OBJDIR = objdir
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib_out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-8000:]))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_out)
+    return lib_out
 
 
 if __name__ == "__main__":

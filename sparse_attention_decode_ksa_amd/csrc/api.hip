@@ -20,6 +20,7 @@ bool supported_shape(const ksa_problem& p) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if ((int64_t)p.batch * p.num_kv_heads * (int64_t)p.max_seq_len * p.head_dim >= kMaxElems)
     return false;
+  if ((int64_t)p.batch * p.num_kv_heads > kMaxRows) return false;
   return true;
 }
 
@@ -64,16 +65,16 @@ size_t workspace_for(const ksa_problem& p, int32_t op, int32_t param) {
   const Dims d = make_dims(p);
   switch (op) {
     case KSA_OP_SELECT_TOPK:
-      return 0;
+      return select_workspace_bytes(d);
     case KSA_OP_SPARSE_BLOCKS:
-      return attention_workspace_bytes(d, plan_attention(d, (int64_t)param * d.Bs));
+      return attention_workspace_bytes(d, plan_attention(d, 0, (int64_t)param * d.Bs));
     case KSA_OP_SPARSE_TOKENS:
-      return attention_workspace_bytes(d, plan_attention(d, param));
+      return attention_workspace_bytes(d, plan_attention(d, 1, param));
     case KSA_OP_VOTE_SELECT:
       // bound over every recent_window: W = 0 has the most candidates
       return plan_vote(d, param, 0).total;
     case KSA_OP_DENSE:
-      return attention_workspace_bytes(d, plan_attention(d, d.T));
+      return attention_workspace_bytes(d, plan_attention(d, 2, d.T));
     default:
       return SIZE_MAX;
   }
@@ -130,11 +131,11 @@ ksa_status ksa_select_topk(const ksa_problem* problem, const void* q, const void
       (block_scores && !aligned4(block_scores)))
     return KSA_ERR_INVALID_ARGUMENT;
   if (d.NB > kSelectMaxBlocks) return KSA_ERR_UNSUPPORTED;
-  if (workspace_bytes < workspace_for(*problem, KSA_OP_SELECT_TOPK, top_k))
-    return KSA_ERR_WORKSPACE_TOO_SMALL;
-  (void)workspace;
+  const size_t need = workspace_for(*problem, KSA_OP_SELECT_TOPK, top_k);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
   const int keff = top_k < d.NB ? top_k : d.NB;
-  return from_hip(launch_select_topk(d, q, summaries, keff, block_idx, block_scores,
+  return from_hip(launch_select_topk(d, q, summaries, keff, block_idx, block_scores, workspace,
                                      (hipStream_t)stream));
 }
 
@@ -156,7 +157,7 @@ ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const vo
   if (!blocks && sel->count > d.T) return KSA_ERR_INVALID_ARGUMENT;
   if (blocks && (int64_t)sel->count * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
   const int64_t ltot = blocks ? (int64_t)sel->count * d.Bs : sel->count;
-  const AttnPlan plan = plan_attention(d, ltot);
+  const AttnPlan plan = plan_attention(d, blocks ? 0 : 1, ltot);
   const size_t need = attention_workspace_bytes(d, plan);
   if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
   if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
@@ -192,7 +193,7 @@ ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const voi
   if (!q || !k || !v || !out) return KSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(out) || (lse && !aligned4(lse)))
     return KSA_ERR_INVALID_ARGUMENT;
-  const AttnPlan plan = plan_attention(d, d.T);
+  const AttnPlan plan = plan_attention(d, 2, d.T);
   const size_t need = attention_workspace_bytes(d, plan);
   if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
   if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;

@@ -23,9 +23,12 @@
 // P.V accumulation.  States are merged slot -> wave -> workgroup -> split in
 // a fixed order, so results are bitwise repeatable.
 //
-// Pipelining.  While a wave computes chunk c it has the K/V loads of its next
-// chunk and the index loads of the chunk after that in flight.
+// Pipelining.  The workgroup's slice of the index list is staged in LDS once;
+// while a wave computes one chunk, the K/V loads of its next
+// kPrefetchChunks chunks are in flight (a ring of register buffers).
 #include <float.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "ksa_device.h"
 #include "ksa_internal.h"
@@ -34,6 +37,16 @@ namespace ksa {
 namespace {
 
 constexpr int kMaxWaves = 8;
+// chunks whose K/V loads are in flight while a wave computes another
+#ifndef KSA_ATTN_PREFETCH
+#define KSA_ATTN_PREFETCH 1
+#endif
+constexpr int kPrefetchChunks = KSA_ATTN_PREFETCH;
+// K/V rows are streamed once per call: nontemporal loads keep them from
+// displacing reusable lines in L2 and the Infinity Cache.
+#ifndef KSA_NT_LOADS
+#define KSA_NT_LOADS 1
+#endif
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -54,9 +67,11 @@ struct AttnArgs {
   float* part_ml;  // [rows, splits, G, 2]
 };
 
+// Token ids of the NI rows a lane loads for chunk c.  Indices of the
+// workgroup's range are staged in LDS (s_idx, entries from e0 on).
 template <int KIND, int CH, int SPW, int NI>
-__device__ __forceinline__ void resolve_chunk(const AttnArgs& a, int row, int b, int slot, int c,
-                                              int* tok, bool* ok) {
+__device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_idx, int e0, int slot,
+                                              int c, int* tok, bool* ok) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int p = c * CH + i * SPW + slot;
@@ -65,7 +80,8 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, int row, int b,
       tok[i] = ok[i] ? p : 0;
     } else if constexpr (KIND == 1) {
       ok[i] = p < a.ltot;
-      tok[i] = ok[i] ? a.idx[(int64_t)b * a.count + p] : 0;
+      const int at = min(max(p - e0, 0), kIdxStage - 1);  // in range whenever ok
+      tok[i] = ok[i] ? s_idx[at] : 0;
     } else {
       ok[i] = p < a.ltot;
       int q, r;
@@ -76,11 +92,84 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, int row, int b,
         q = p / a.d.Bs;
         r = p - q * a.d.Bs;
       }
-      const int blk = ok[i] ? a.idx[(int64_t)row * a.count + q] : 0;
+      const int at = min(max(q - e0, 0), kIdxStage - 1);  // in range whenever ok
+      const int blk = ok[i] ? s_idx[at] : 0;
       const int t = blk * a.d.Bs + r;
       ok[i] = ok[i] && t < a.d.T;
       tok[i] = ok[i] ? t : 0;
     }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 ld_kv(const T* p) {
+#if KSA_NT_LOADS
+  return ld16_stream(p);
+#else
+  return ld16(p);
+#endif
+}
+
+template <typename T, int D, int KIND, int CH, int SPW, int NI>
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, const int* s_idx, int e0, int slot,
+                                           int c, const T* kbase, const T* vbase, uint4* kr,
+                                           uint4* vr, bool* okr) {
+  int tok[NI];
+  resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, e0, slot, c, tok, okr);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    kr[i] = ld_kv(kbase + (int64_t)tok[i] * D);
+    vr[i] = ld_kv(vbase + (int64_t)tok[i] * D);
+  }
+}
+
+template <typename T, int D, int G, int NI, int LPT>
+__device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], const uint4* kc,
+                                              const uint4* vc, const bool* okc, float* m, float* l,
+                                              float (&acc)[G][KV<T>::EPL]) {
+  constexpr int EPL = KV<T>::EPL;
+  // logits of the NI tokens for every head of the group
+  float s[NI][G];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float f[EPL];
+    KV<T>::widen(kc[i], f);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
+      s[i][h] = group_sum<LPT>(p);
+    }
+  }
+  // online softmax update, once per chunk
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = m[h];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (okc[i]) mx = fmaxf(mx, s[i][h]);
+    const float alpha = fast_exp2(m[h] - mx);
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float p = okc[i] ? fast_exp2(s[i][h] - mx) : 0.f;
+      s[i][h] = p;
+      ps += p;
+    }
+    l[h] = fmaf(l[h], alpha, ps);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+    m[h] = mx;
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float f[EPL];
+    KV<T>::widen(vc[i], f);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[i][h], f[e], acc[h][e]);
   }
 }
 
@@ -91,9 +180,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
   constexpr int SPW = 64 / LPT;
   constexpr int NI = kLoadsPerChunk;
   constexpr int CH = SPW * NI;
+  constexpr int P = kPrefetchChunks;
   __shared__ float s_m[kMaxWaves][G];
   __shared__ float s_l[kMaxWaves][G];
   __shared__ float s_acc[kMaxWaves][G][D];
+  __shared__ int s_idx[kIdxStage];
 
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -105,6 +196,27 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
   const int64_t kvrow = (int64_t)row * d.Tcap * D + li * EPL;
   const T* kbase = (const T*)a.k + kvrow;
   const T* vbase = (const T*)a.v + kvrow;
+
+  const int nchunks = (a.ltot + CH - 1) / CH;
+  const int c_begin = split * a.cps;
+  const int c_end = min(c_begin + a.cps, nchunks);
+
+  // stage this workgroup's slice of the index list in LDS
+  int e0 = 0;
+  if constexpr (KIND != 2) {
+    int e1;
+    const int32_t* src;
+    if constexpr (KIND == 0) {
+      e0 = (c_begin * CH) / d.Bs;
+      e1 = min(a.count, (c_end * CH + d.Bs - 1) / d.Bs);
+      src = a.idx + (int64_t)row * a.count;
+    } else {
+      e0 = c_begin * CH;
+      e1 = min(a.ltot, c_end * CH);
+      src = a.idx + (int64_t)b * a.count;
+    }
+    for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
+  }
 
   float qv[G][EPL];
 #pragma unroll
@@ -122,88 +234,34 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
+  if constexpr (KIND != 2) __syncthreads();
 
-  const int nchunks = (a.ltot + CH - 1) / CH;
-  const int c_begin = split * a.cps;
-  const int c_end = min(c_begin + a.cps, nchunks);
-  int c = c_begin + wave;
-  if (c < c_end) {
-    int tok[NI];
-    bool ok[NI];
-    resolve_chunk<KIND, CH, SPW, NI>(a, row, b, slot, c, tok, ok);
-    uint4 kr[NI], vr[NI];
-    bool okr[NI];
+  const int c0 = c_begin + wave;
+  const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
+  uint4 kb[P][NI], vb[P][NI];
+  bool okb[P][NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kr[i] = ld16(kbase + (int64_t)tok[i] * D);
-      vr[i] = ld16(vbase + (int64_t)tok[i] * D);
-      okr[i] = ok[i];
-    }
-    int cn = c + nw;
-    if (cn < c_end) resolve_chunk<KIND, CH, SPW, NI>(a, row, b, slot, cn, tok, ok);
-    for (; c < c_end; c += nw) {
-      uint4 kc[NI], vc[NI];
-      bool okc[NI];
+  for (int s = 0; s < P; ++s)
+    if (s < my_n)
+      load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, e0, slot, c0 + s * nw, kbase, vbase, kb[s],
+                                          vb[s], okb[s]);
+  for (int j0 = 0; j0 < my_n; j0 += P) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kc[i] = kr[i];
-        vc[i] = vr[i];
-        okc[i] = okr[i];
-      }
-      if (cn < c_end) {
+    for (int s = 0; s < P; ++s) {
+      const int j = j0 + s;
+      if (j < my_n) {
+        uint4 kc[NI], vc[NI];
+        bool okc[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          kr[i] = ld16(kbase + (int64_t)tok[i] * D);
-          vr[i] = ld16(vbase + (int64_t)tok[i] * D);
-          okr[i] = ok[i];
+          kc[i] = kb[s][i];
+          vc[i] = vb[s][i];
+          okc[i] = okb[s][i];
         }
-      }
-      const int cnn = cn + nw;
-      if (cnn < c_end) resolve_chunk<KIND, CH, SPW, NI>(a, row, b, slot, cnn, tok, ok);
-      cn = cnn;
-
-      // logits of the NI tokens for every head of the group
-      float s[NI][G];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float f[EPL];
-        KV<T>::widen(kc[i], f);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float p = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
-          s[i][h] = group_sum<LPT>(p);
-        }
-      }
-      // online softmax update, once per chunk
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mx = m[h];
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-          if (okc[i]) mx = fmaxf(mx, s[i][h]);
-        const float alpha = fast_exp2(m[h] - mx);
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const float p = okc[i] ? fast_exp2(s[i][h] - mx) : 0.f;
-          s[i][h] = p;
-          ps += p;
-        }
-        l[h] = fmaf(l[h], alpha, ps);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
-        m[h] = mx;
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float f[EPL];
-        KV<T>::widen(vc[i], f);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[i][h], f[e], acc[h][e]);
+        if (j + P < my_n)
+          load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, e0, slot, c0 + (j + P) * nw, kbase, vbase,
+                                              kb[s], vb[s], okb[s]);
+        compute_chunk<T, D, G, NI, LPT>(qv, kc, vc, okc, m, l, acc);
       }
     }
   }
@@ -316,7 +374,7 @@ hipError_t launch_g(const AttnArgs& a, int kind, const AttnPlan& p, hipStream_t 
 
 }  // namespace
 
-AttnPlan plan_attention(const Dims& d, int64_t tokens_per_row) {
+AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   const int ch = chunk_tokens(d);
   const int64_t chunks = (tokens_per_row + ch - 1) / ch;
   const int64_t rows = (int64_t)d.B * d.Hkv;
@@ -328,8 +386,21 @@ AttnPlan plan_attention(const Dims& d, int64_t tokens_per_row) {
   int nw = 1;
   while (nw < kMaxWaves && nw * 2 <= wpr) nw *= 2;
   int64_t splits = (wpr + nw - 1) / nw;
+  // Tuning override "waves,splits" for launch-shape sweeps (read per call).
+  if (const char* env = getenv("KSA_ATTN_PLAN")) {
+    int enw = 0, esp = 0;
+    if (sscanf(env, "%d,%d", &enw, &esp) == 2 && enw >= 1 && enw <= kMaxWaves && esp >= 1) {
+      nw = enw;
+      splits = esp;
+    }
+  }
   if (splits < 1) splits = 1;
   int64_t cps = (chunks + splits - 1) / splits;
+  // a workgroup's index slice must fit the LDS stage
+  int64_t cap = INT64_MAX;
+  if (kind == 1) cap = kIdxStage / ch;
+  if (kind == 0) cap = ((int64_t)(kIdxStage - 2) * d.Bs) / ch;
+  if (cps > cap) cps = cap;
   if (cps < 1) cps = 1;
   splits = (chunks + cps - 1) / cps;
   if (splits < 1) splits = 1;
@@ -366,7 +437,7 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
   a.lse = lse;
   const size_t rows = (size_t)d.B * d.Hkv;
   a.part_acc = (float*)workspace;
-  a.part_ml = workspace ? (float*)workspace + rows * plan.splits * d.G * d.D : nullptr;
+  a.part_ml = workspace ? a.part_acc + rows * plan.splits * d.G * d.D : nullptr;
   if (d.dtype == KSA_BF16) {
     if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);
     return launch_g<uint16_t, 128>(a, kind, plan, stream);

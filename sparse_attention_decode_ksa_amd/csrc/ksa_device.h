@@ -41,6 +41,13 @@ struct KV<float> {
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte load with the nontemporal (streaming) cache hint, for data read
+// once per call.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // ---------------------------------------------------------------- DPP

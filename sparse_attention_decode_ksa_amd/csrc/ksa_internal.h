@@ -19,6 +19,8 @@ struct Dims {
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+constexpr int kMaxRows = 16384;  // B * Hkv: the top-k grid's row count stays far below 2^31
+
 // Elements one lane moves in one 16-byte load.
 inline int elems_per_lane(int dtype) { return dtype == KSA_F32 ? 4 : 8; }
 // Lanes that together hold one token row of D elements.
@@ -28,7 +30,12 @@ inline int slots_per_wave(const Dims& d) { return 64 / lanes_per_token(d); }
 
 // 16-byte loads per lane per chunk for K (and again for V) in the attention
 // kernels; a chunk is slots_per_wave * kLoadsPerChunk tokens.
-constexpr int kLoadsPerChunk = 4;
+#ifndef KSA_ATTN_LOADS
+#define KSA_ATTN_LOADS 4
+#endif
+constexpr int kLoadsPerChunk = KSA_ATTN_LOADS;
+// index entries a workgroup stages in LDS
+constexpr int kIdxStage = 2048;
 inline int chunk_tokens(const Dims& d) { return slots_per_wave(d) * kLoadsPerChunk; }
 
 // Attention launch: `splits` workgroups of `nw` waves per (sequence, KV
@@ -36,7 +43,8 @@ inline int chunk_tokens(const Dims& d) { return slots_per_wave(d) * kLoadsPerChu
 struct AttnPlan {
   int nw, splits, cps, chunk;
 };
-AttnPlan plan_attention(const Dims& d, int64_t tokens_per_row);
+// kind: 0 = selected blocks, 1 = shared token list, 2 = dense range
+AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row);
 size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p);
 
 // Attention over a row-wise token list.  kind: 0 = selected blocks,
@@ -49,8 +57,10 @@ hipError_t launch_block_summaries(const Dims& d, const void* k, void* summaries,
                                   int num_blocks, hipStream_t stream);
 
 constexpr int kSelectMaxBlocks = 15360;  // keys live in LDS (60 KB)
+size_t select_workspace_bytes(const Dims& d);
 hipError_t launch_select_topk(const Dims& d, const void* q, const void* summaries, int keff,
-                              int32_t* block_idx, float* block_scores, hipStream_t stream);
+                              int32_t* block_idx, float* block_scores, void* workspace,
+                              hipStream_t stream);
 
 // Vote-union selection.
 struct VotePlan {

@@ -58,6 +58,8 @@ __device__ __forceinline__ void store_mean<float>(float* dst, const double* acc,
   st16(dst, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+constexpr int kBatch = 16;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void block_summaries_kernel(const T* __restrict__ k,
                                                               T* __restrict__ summ, Dims d,
@@ -78,12 +80,21 @@ __global__ __launch_bounds__(256) void block_summaries_kernel(const T* __restric
   double acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
-#pragma unroll 4
-  for (int t = 0; t < n; ++t) {
-    float f[EPL];
-    KV<T>::widen(ld16(kp + (int64_t)t * D), f);
+  // all of a batch's loads are issued before the in-order fp64 sum consumes them
+#pragma unroll 1
+  for (int t0 = 0; t0 < n; t0 += kBatch) {
+    uint4 r[kBatch];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += (double)f[e];
+    for (int u = 0; u < kBatch; ++u) r[u] = ld16(kp + (int64_t)min(t0 + u, n - 1) * D);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (t0 + u < n) {
+        float f[EPL];
+        KV<T>::widen(r[u], f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += (double)f[e];
+      }
+    }
   }
   store_mean<T>(summ + (bg * d.NBcap + j) * D + li * EPL, acc, n);
 }

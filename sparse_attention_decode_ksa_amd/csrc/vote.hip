@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
 
   uint4 kr[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) kr[i] = ld16(kb + (int64_t)min(c0 * CH + i * SPW + slot, hist - 1) * D);
+  for (int i = 0; i < NI; ++i)
+    kr[i] = ld16_stream(kb + (int64_t)min(c0 * CH + i * SPW + slot, hist - 1) * D);
   for (int c = c0; c < c1; ++c) {
     uint4 kc[NI];
 #pragma unroll
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
     if (c + 1 < c1) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        kr[i] = ld16(kb + (int64_t)min((c + 1) * CH + i * SPW + slot, hist - 1) * D);
+        kr[i] = ld16_stream(kb + (int64_t)min((c + 1) * CH + i * SPW + slot, hist - 1) * D);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -325,7 +326,7 @@ VotePlan plan_vote(const Dims& d, int N, int W) {
   const size_t rows = (size_t)d.B * d.Hq;
   p.keys_off = 0;
   const size_t keys_bytes = rows * (size_t)p.hist * sizeof(uint32_t);
-  p.bits_off = (keys_bytes + 255) & ~(size_t)255;
+  p.bits_off = (p.keys_off + keys_bytes + 255) & ~(size_t)255;
   p.total = p.bits_off + rows * (size_t)p.words * sizeof(uint32_t);
   if (d.T <= N) p.total = 0;
   return p;

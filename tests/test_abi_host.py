@@ -51,13 +51,14 @@ def test_workspace_sizing_is_pure_and_validates():
     p = P()
     a = ksa.ksa_workspace_bytes(p, ksa.KSA_OP_DENSE, 0)
     assert a == ksa.ksa_workspace_bytes(p, ksa.KSA_OP_DENSE, 0)
-    assert ksa.ksa_workspace_bytes(p, ksa.KSA_OP_SELECT_TOPK, 8) == 0
+    # selection keeps one uint32 key per block
+    assert ksa.ksa_workspace_bytes(p, ksa.KSA_OP_SELECT_TOPK, 8) == 2 * 2 * 64 * 4
     # the vote workspace holds fp32-sized keys for every (b, h, history token) plus bitmasks
     p4 = P(B=16, Hq=32, Hkv=8, D=128, T=20000, Tcap=20000, dtype=ksa.KSA_BF16)
     assert ksa.ksa_workspace_bytes(p4, ksa.KSA_OP_VOTE_SELECT, 2048) >= 16 * 32 * 20000 * 4
     # T <= N needs no workspace
     assert ksa.ksa_workspace_bytes(P(T=100, Tcap=100), ksa.KSA_OP_VOTE_SELECT, 2048) == 0
-    bad = [P(Hq=3, Hkv=2), P(T=0), P(Tcap=10, T=20), P(Bs=0), P(B=0)]
+    bad = [P(Hq=3, Hkv=2), P(T=0), P(Tcap=10, T=20), P(Bs=0), P(B=0), P(B=16385, Hq=1, Hkv=1)]
     for b in bad:
         n = lib.ksa_workspace_bytes(ctypes.byref(b), ksa.KSA_OP_SPARSE_BLOCKS, 4)
         assert n == ksa.SIZE_MAX

@@ -330,3 +330,54 @@ def test_workload_c4_sampled():
         check_votes(votes[sl].cpu().numpy(), idx[sl].cpu().numpy(), lg, N, W)
         ro, rl = oracle.attend_tokens(qb, kb, vb, w.T, idx[sl].cpu().numpy())
         check_attention(out[sl].cpu().numpy(), lse[sl].cpu().numpy(), ro, rl)
+
+
+def test_hip_graph_replay_matches_eager_calls():
+    """The block top-k step captured in a HIP graph (the C calls launched on the
+    capturing stream) and replayed several times, with new queries copied in
+    and eager work in between, matches eager calls every time.  The selection
+    workspace's counters are zero-filled once and must stay consistent."""
+    w = small_workload(B=8, Hq=16, Hkv=8, D=128, T=4000, Bs=16, dtype="bf16", top_k=32, seed=21)
+    q, k, v = gpu_inputs(w)
+    s = run_summaries(k, w)
+    idx = torch.empty((w.B, w.Hkv, w.top_k), dtype=torch.int32, device=DEV)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=DEV)
+    prob = ksa.make_problem(q, k, w.T, w.Bs)
+    wsel = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SELECT_TOPK, w.top_k), DEV)
+    wat = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SPARSE_BLOCKS, w.top_k), DEV)
+    stream = torch.cuda.Stream()
+    qbuf = q.clone()
+
+    def step():
+        ksa.ksa_block_summaries(k, s, w.T, w.Bs, first_block=(w.T - 1) // w.Bs, num_blocks=1,
+                                stream=stream)
+        ksa.ksa_select_topk(qbuf, s, w.T, w.Bs, w.top_k, block_idx=idx, workspace=wsel, stream=stream)
+        ksa.ksa_sparse_decode(qbuf, k, v, w.T, idx, ksa.KSA_SEL_BLOCKS, block_size=w.Bs, out=out,
+                              lse=lse, workspace=wat, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()                      # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    for rep in range(4):
+        newq = torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype)
+        qbuf.copy_(newq)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        got = (idx.clone(), out.clone(), lse.clone())
+        # eager reference on the same inputs, with fresh buffers
+        e_idx = ksa.ksa_select_topk(newq, s, w.T, w.Bs, w.top_k)
+        e_out, e_lse = ksa.ksa_sparse_decode(newq, k, v, w.T, e_idx, ksa.KSA_SEL_BLOCKS, block_size=w.Bs)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], e_idx), rep
+        assert torch.equal(got[1], e_out) and torch.equal(got[2], e_lse), rep
+    # the last replay also agrees with the oracle
+    ro, rl = oracle.attend_blocks(np_bits(qbuf), np_bits(k), np_bits(v), w.T, w.Bs, idx.cpu().numpy())
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
