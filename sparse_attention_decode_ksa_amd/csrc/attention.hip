@@ -30,6 +30,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "ksa_device.h"
 #include "ksa_internal.h"
 
@@ -173,6 +175,39 @@ __device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], 
   }
 }
 
+// Merges the per-wave softmax states of a workgroup (staged in LDS) and
+// writes the row's output, or this split's partial state when the row is
+// split over several workgroups.  Fixed order: bitwise repeatable.
+template <int D, int G>
+__device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, int g, int split,
+                                            int nw, const float (*s_m)[G], const float (*s_l)[G],
+                                            const float (*s_acc)[G][D]) {
+  const Dims& d = a.d;
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+    const int h = o / D, e = o - (o / D) * D;
+    float M = -FLT_MAX;
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float sc = fast_exp2(s_m[w][h] - M);
+      L = fmaf(s_l[w][h], sc, L);
+      A = fmaf(s_acc[w][h][e], sc, A);
+    }
+    if (a.splits == 1) {
+      const int64_t oh = (int64_t)b * d.Hq + g * G + h;
+      a.out[oh * D + e] = A / L;
+      if (e == 0 && a.lse) a.lse[oh] = (M + log2f(L)) * kLn2;
+    } else {
+      const int64_t pi = ((int64_t)row * a.splits + split) * G + h;
+      a.part_acc[pi * D + e] = A;
+      if (e == 0) {
+        a.part_ml[pi * 2] = M;
+        a.part_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 template <typename T, int D, int G, int KIND>
 __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a) {
   constexpr int EPL = KV<T>::EPL;
@@ -294,30 +329,210 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
   }
   __syncthreads();
 
-  // merge the waves; write the row's output or this split's partial state
-  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
-    const int h = o / D, e = o - (o / D) * D;
-    float M = -FLT_MAX;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, A = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float sc = fast_exp2(s_m[w][h] - M);
-      L = fmaf(s_l[w][h], sc, L);
-      A = fmaf(s_acc[w][h][e], sc, A);
-    }
-    if (a.splits == 1) {
-      const int64_t oh = (int64_t)b * d.Hq + g * G + h;
-      a.out[oh * D + e] = A / L;
-      if (e == 0 && a.lse) a.lse[oh] = (M + log2f(L)) * kLn2;
+  merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA variant for bf16, D = 128 and G in {4, 8}.  Per chunk of 16 tokens:
+//  * QK^T on v_mfma_f32_16x16x32_bf16: A = 16 token rows x 32 dims of K (lane
+//    l holds token l%16, dims 8*(l/16).. of the slice, loaded straight from
+//    HBM into that layout), B = the same 32 dims of the group's G query heads
+//    (zero columns past G), four MFMAs cover D = 128.  The bf16 products are
+//    exact and accumulate in fp32; the fp32 logits are scaled afterwards.
+//  * Softmax in the MFMA output layout (lane l: head l%16, tokens 4*(l/16)..):
+//    one running max and sum per head for the whole wave, cross-lane steps by
+//    xor-16/32 shuffles.
+//  * The weights P (fp32) and the rescale factors go through a wave-private
+//    LDS tile to the V layout (16 lanes per token row, as in the VALU kernel),
+//    where P.V accumulates on VALU in fp32.
+// Softmax state is per wave rather than per slot, so the slots of a wave are
+// merged by plain sums.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {u.x, u.y, u.z, u.w};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Orders this wave's LDS accesses around the point for the compiler; the
+// hardware executes a wave's LDS instructions in order.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int G, int KIND>
+__global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int EPL = 8;
+  constexpr int LPT = 16;
+  constexpr int SPW = 4;
+  constexpr int NI = 4;
+  constexpr int CH = 16;
+  static_assert(CH == SPW * NI, "chunk of the VALU kernel");
+  __shared__ float s_m[kMaxWaves][G];
+  __shared__ float s_l[kMaxWaves][G];
+  __shared__ float s_acc[kMaxWaves][G][D];
+  __shared__ int s_idx[kIdxStage];
+  __shared__ float s_p[kMaxWaves][CH + 1][8];  // rows 0..15: P[token][head]; row 16: rescale
+
+  const Dims& d = a.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;  // MFMA: row/column and k-group / row quad
+  const int slot = kg, li = r;             // V layout: token slot and 16-byte piece
+  const int split = blockIdx.x % a.splits;
+  const int row = blockIdx.x / a.splits;
+  const int b = row / d.Hkv, g = row - b * d.Hkv;
+  const int64_t kvrow = (int64_t)row * d.Tcap * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + kvrow + 8 * kg;
+  const uint16_t* vbase = (const uint16_t*)a.v + kvrow + li * EPL;
+
+  const int nchunks = (a.ltot + CH - 1) / CH;
+  const int c_begin = split * a.cps;
+  const int c_end = min(c_begin + a.cps, nchunks);
+
+  int e0 = 0;
+  if constexpr (KIND != 2) {
+    int e1;
+    const int32_t* src;
+    if constexpr (KIND == 0) {
+      e0 = (c_begin * CH) / d.Bs;
+      e1 = min(a.count, (c_end * CH + d.Bs - 1) / d.Bs);
+      src = a.idx + (int64_t)row * a.count;
     } else {
-      const int64_t pi = ((int64_t)row * a.splits + split) * G + h;
-      a.part_acc[pi * D + e] = A;
-      if (e == 0) {
-        a.part_ml[pi * 2] = M;
-        a.part_ml[pi * 2 + 1] = L;
-      }
+      e0 = c_begin * CH;
+      e1 = min(a.ltot, c_end * CH);
+      src = a.idx + (int64_t)b * a.count;
     }
+    for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
   }
+
+  // B operand: the group's queries, column n = head r (zero past G)
+  bf16x8_t qop[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (r < G) u = ld16((const uint16_t*)a.q + ((int64_t)b * d.Hq + g * G + r) * D + 32 * i + 8 * kg);
+    qop[i] = as_bf16x8(u);
+  }
+  float m = -FLT_MAX, lsum = 0.f;  // softmax state of head r (MFMA layout)
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  if constexpr (KIND != 2) __syncthreads();
+
+  const int c0 = c_begin + wave;
+  const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
+  float(*pt)[8] = s_p[wave];
+
+  // loads of one chunk: K in the MFMA A layout, V in the row layout
+  auto load = [&](int c, uint4* kr, uint4* vr, bool& okk) {
+    int tk[1];
+    bool ok1[1];
+    resolve_chunk<KIND, CH, 1, 1>(a, s_idx, e0, r, c, tk, ok1);  // position c*16 + r
+    okk = ok1[0];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = ld_kv(kbase + (int64_t)tk[0] * D + 32 * i);
+    int tv[NI];
+    bool okv[NI];
+    resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, e0, slot, c, tv, okv);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = ld_kv(vbase + (int64_t)tv[i] * D);
+  };
+
+  uint4 kb[NI], vb[NI];
+  bool okb = false;
+  if (my_n > 0) load(c0, kb, vb, okb);
+  for (int j = 0; j < my_n; ++j) {
+    uint4 kc[NI], vc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kc[i] = kb[i];
+      vc[i] = vb[i];
+    }
+    const bool okc = okb;
+    if (j + 1 < my_n) load(c0 + (j + 1) * nw, kb, vb, okb);
+
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[i]), qop[i], S, 0, 0, 0);
+    const uint64_t vm = __ballot(okc);  // bit t (t < 16): chunk token t is attended
+    float sv[4];
+    bool val[4];
+    float mloc = -FLT_MAX;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      sv[jj] = S[jj] * a.qscale;
+      val[jj] = (vm >> (4 * kg + jj)) & 1ull;
+      if (val[jj]) mloc = fmaxf(mloc, sv[jj]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float mnew = fmaxf(m, mloc);
+    const float alpha = fast_exp2(m - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      sv[jj] = val[jj] ? fast_exp2(sv[jj] - mnew) : 0.f;
+      ps += sv[jj];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    lsum = fmaf(lsum, alpha, ps);
+    m = mnew;
+    if (r < G) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) pt[4 * kg + jj][r] = sv[jj];
+      if (kg == 0) pt[CH][r] = alpha;
+    }
+    wave_lds_fence();
+    float al[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) al[h] = pt[CH][h];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float pv[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[h] = pt[4 * i + slot][h];
+      float f[EPL];
+      KV<uint16_t>::widen(vc[i], f);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], f[e], acc[h][e]);
+    }
+    wave_lds_fence();
+  }
+
+  // slots share the wave's softmax state: their accumulators simply add up
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      acc[h][e] += __shfl_xor(acc[h][e], 16);
+      acc[h][e] += __shfl_xor(acc[h][e], 32);
+    }
+  if (lane < G) {
+    s_m[wave][lane] = m;
+    s_l[wave][lane] = lsum;
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h][li * EPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
 }
 
 // Fixed-order merge of the split partial states of each row.
@@ -346,14 +561,27 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   }
 }
 
+#ifndef KSA_MFMA
+#define KSA_MFMA 1
+#endif
+
 template <typename T, int D, int G>
 hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStream_t s) {
   const int rows = a.d.B * a.d.Hkv;
   const dim3 grid(rows * p.splits), block(p.nw * 64);
-  switch (kind) {
-    case 0: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 0>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 1>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 2>), grid, block, 0, s, a); break;
+  constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
+  if constexpr (mfma) {
+    switch (kind) {
+      case 0: hipLaunchKernelGGL((attn_mfma_kernel<G, 0>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((attn_mfma_kernel<G, 1>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_mfma_kernel<G, 2>), grid, block, 0, s, a); break;
+    }
+  } else {
+    switch (kind) {
+      case 0: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 0>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 1>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 2>), grid, block, 0, s, a); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
