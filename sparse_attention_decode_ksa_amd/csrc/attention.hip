@@ -339,6 +339,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
 //    HBM into that layout), B = the same 32 dims of the group's G query heads
 //    (zero columns past G), four MFMAs cover D = 128.  The bf16 products are
 //    exact and accumulate in fp32; the fp32 logits are scaled afterwards.
+//    (Loading K coalesced and transposing it through LDS was measured slower
+//    here: the extra LDS round trip per chunk costs more than it saves at the
+//    8-12 waves per CU these kernels run with.)
 //  * Softmax in the MFMA output layout (lane l: head l%16, tokens 4*(l/16)..):
 //    one running max and sum per head for the whole wave, cross-lane steps by
 //    xor-16/32 shuffles.
@@ -347,22 +350,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
 //    where P.V accumulates on VALU in fp32.
 // Softmax state is per wave rather than per slot, so the slots of a wave are
 // merged by plain sums.
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = {u.x, u.y, u.z, u.w};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// Orders this wave's LDS accesses around the point for the compiler; the
-// hardware executes a wave's LDS instructions in order.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 template <int G, int KIND>
 __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = 128;

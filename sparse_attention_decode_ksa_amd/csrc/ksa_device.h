@@ -78,6 +78,34 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// ---------------------------------------------------------------- MFMA
+// Operand types of v_mfma_f32_16x16x32_bf16.  Lane layout (checked on the
+// GPU): A lane l holds row l%16, k-elements 8*(l/16)..+8; B lane l holds
+// column l%16, the same k-elements; C lane l holds column l%16, rows
+// 4*(l/16)..+4.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {u.x, u.y, u.z, u.w};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// K tile transpose through LDS.  A 16-token x 256-byte K tile is loaded with
+// coalesced row-layout loads (lane = 16 * token-slot + piece) and re-read in
+// the MFMA A layout (lane = 16 * k-group + token).  Token t's 16-byte piece c
+// lives at slot t*16 + (c ^ t): both the row-layout writes and the A-layout
+// reads then touch 16 distinct 16-byte slots per 16 lanes (no bank conflict).
+__device__ __forceinline__ int ktile_slot(int t, int c) { return t * 16 + (c ^ t); }
+
+// Orders this wave's LDS accesses around the point for the compiler; the
+// hardware executes a wave's LDS instructions in order.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------- keys
 // Order-preserving map of an fp32 score to uint32: larger score -> larger
 // key; -0 is folded onto +0 so that equal scores give equal keys.

@@ -67,7 +67,7 @@ struct VotePlan {
   int hist;        // C = T - W history tokens (candidates)
   int words;       // 32-token words per head bitmask
   int kv;          // N - W picks per head
-  size_t keys_off, bits_off, total;
+  size_t keys_off, bits_off, votes_off, vhist_off, total;
 };
 VotePlan plan_vote(const Dims& d, int N, int W);
 hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N, int W,

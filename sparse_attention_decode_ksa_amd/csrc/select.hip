@@ -25,8 +25,14 @@
 namespace ksa {
 namespace {
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 8;
+#ifndef KSA_SCORE_THREADS
+#define KSA_SCORE_THREADS 256
+#endif
+#ifndef KSA_SCORE_UNROLL
+#define KSA_SCORE_UNROLL 8
+#endif
+constexpr int kScoreThreads = KSA_SCORE_THREADS;  // per scoring workgroup
+constexpr int kScoreUnroll = KSA_SCORE_UNROLL;    // summaries in flight per lane
 constexpr int kTopkThreads = 256;  // one workgroup per row; also the histogram size
 
 // Relevance of a tile of blocks of one row.  Every LPT-lane group issues all

@@ -5,21 +5,25 @@
 // picks and appends the most recent tokens).
 //
 // Per sequence b with history C = [0, T-W) and Kv = N - W picks per head:
-//  1. vote_scores: every (b, KV head g) row streams its keys once; the G
-//     query heads of the group score each history token in fp32 (lanes and
-//     loads as in the attention kernel) and store order-preserving uint32
-//     keys [B, Hq, C] in the workspace.
-//  2. vote_head_select: one workgroup per (b, h) finds, by MSB-first radix
-//     select on the keys, the Kv-th largest key and how many keys equal to it
-//     are taken (lowest token ids first), and writes the head's picks as a
-//     bitmask [B, Hq, ceil(C/32)] words.
-//  3. vote_set: one workgroup per b counts, for every history token, the
-//     heads whose bitmask has it (its vote total), finds the vote threshold
-//     with a histogram over 0..Hq, and compacts the first Kv tokens by
-//     (votes desc, t asc) in ascending order with one workgroup scan; the W
-//     recent tokens follow.  Votes are written out as uint8 when asked for.
+//  1. vote_scores: every (b, KV head g) row streams its history keys once;
+//     the G query heads of the group score every token in fp32 (MFMA for
+//     bf16 D=128 groups of 4 and 8, VALU otherwise) and store
+//     order-preserving uint32 keys [B, Hq, C] in the workspace.
+//  2. vote_head_select: one workgroup per (b, h), the head's keys held in LDS
+//     when they fit, finds the Kv-th largest key and how many keys equal to
+//     it are taken (lowest token ids first) by a bucket search over the
+//     head's key range, and writes the head's picks as a bitmask
+//     [B, Hq, ceil(C/32)].
+//  3. vote_count: one lane per history token sums its bit over the Hq heads
+//     (its vote total), stores it, and adds it to a per-sequence histogram of
+//     vote totals.
+//  4. vote_set: one workgroup per b reads the histogram, finds the vote
+//     threshold, and compacts the first Kv tokens by (votes desc, t asc) in
+//     ascending order with one workgroup scan; the W recent tokens follow.
 // Everything after the fp32 scores is exact integer work.
 #include <float.h>
+
+#include <type_traits>
 
 #include "ksa_device.h"
 #include "ksa_internal.h"
@@ -29,10 +33,12 @@ namespace {
 
 constexpr int kScoreWaves = 4;
 constexpr int kScoreChunksPerWave = 8;
-constexpr int kHeadThreads = 512;
+constexpr int kHeadThreads = 1024;
+constexpr int kHeadLdsKeys = 36864;  // keys a head-select workgroup keeps in LDS (144 KB)
+constexpr int kCountThreads = 256;
 constexpr int kSetThreads = 1024;
 
-// ------------------------------------------------------------------ 1
+// ------------------------------------------------------------------ 1 (VALU)
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
     const T* __restrict__ q, const T* __restrict__ k, Dims d, int hist,
@@ -93,128 +99,244 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
   }
 }
 
+// ------------------------------------------------------------------ 1 (MFMA)
+// bf16, D = 128, G in {4, 8}: per chunk of 16 tokens, K rows are loaded with
+// coalesced row-layout loads, re-read in the MFMA A layout from a
+// wave-private swizzled LDS tile, and S = K Q^T runs on four
+// v_mfma_f32_16x16x32_bf16; lane l then holds head l%16's logits of tokens
+// 4*(l/16).. and writes their keys.
+template <int G>
+__global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Dims d, int hist,
+    uint32_t* __restrict__ keys) {
+  constexpr int D = 128;
+  constexpr int CH = 16;
+  __shared__ uint4 s_k[kScoreWaves][CH * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;  // MFMA row / k-group; also row layout piece / slot
+  const int row = blockIdx.y;
+  const int b = row / d.Hkv, g = row - b * d.Hkv;
+  const uint16_t* kb = k + (int64_t)row * d.Tcap * D + 8 * r;
+
+  const int nchunks = (hist + CH - 1) / CH;
+  const int c0 = (blockIdx.x * kScoreWaves + wave) * kScoreChunksPerWave;
+  const int c1 = min(c0 + kScoreChunksPerWave, nchunks);
+  if (c0 >= c1) return;
+  bf16x8_t qop[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (r < G) u = ld16(q + ((int64_t)b * d.Hq + g * G + r) * D + 32 * i + 8 * kg);
+    qop[i] = as_bf16x8(u);
+  }
+  uint32_t* kout = keys + ((int64_t)b * d.Hq + g * G + (r < G ? r : 0)) * hist;
+  uint4* kt = s_k[wave];
+
+  // row layout: load i, lane (slot kg, piece r) reads token 4i + kg of the chunk
+  uint4 kr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kr[i] = ld16_stream(kb + (int64_t)min(c0 * CH + 4 * i + kg, hist - 1) * D);
+  for (int c = c0; c < c1; ++c) {
+    uint4 kc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kc[i] = kr[i];
+    if (c + 1 < c1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kr[i] = ld16_stream(kb + (int64_t)min((c + 1) * CH + 4 * i + kg, hist - 1) * D);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kt[ktile_slot(4 * i + kg, r)] = kc[i];
+    wave_lds_fence();
+    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kt[ktile_slot(r, 4 * i + kg)]), qop[i], S,
+                                                  0, 0, 0);
+    wave_lds_fence();
+    if (r < G) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = c * CH + 4 * kg + j;
+        if (t < hist) kout[t] = order_key(S[j]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ 2
+// Per (b, h): the Kv largest keys among the head's `hist` keys, as a bitmask.
+// Bucket search on the key range (as in select.hip): buckets
+// (key - lo) >> shift over the current range [lo, hi], one LDS histogram per
+// pass, until the threshold bucket holds exactly the keys still needed (all
+// taken) or a single key value (lowest token ids first).  The first
+// workgroup of each sequence also clears that sequence's vote histogram,
+// which vote_count fills after this kernel.
+template <bool kLdsKeys>
 __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
-    const uint32_t* __restrict__ keys, int hist, int kv, int words, uint32_t* __restrict__ bits) {
+    const uint32_t* __restrict__ keys, int hist, int kv, int words, int Hq,
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist) {
+  extern __shared__ uint32_t lkeys[];  // the head's keys (kLdsKeys)
   __shared__ uint32_t hbin[256];
+  __shared__ uint32_t red[2][kHeadThreads / 64];
+  __shared__ uint32_t shv[3];
   __shared__ uint64_t scan_scratch[17];
-  __shared__ uint32_t sh_digit, sh_above, sh_bin;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t hr = blockIdx.x;  // b * Hq + h
-  const uint32_t* kr = keys + hr * hist;
+  if (hr % Hq == 0)
+    for (int i = tid; i < 256; i += kHeadThreads) vhist[(hr / Hq) * 256 + i] = 0u;
   uint32_t* br = bits + hr * words;
   if (kv == 0) {  // the whole budget is the recency window: no picks
     for (int w = tid; w < words; w += kHeadThreads) br[w] = 0u;
     return;
   }
+  const uint32_t* kr = keys + hr * hist;
 
-  uint32_t prefix = 0, mask = 0, remaining = (uint32_t)kv, eq_total = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int t = tid; t < hist; t += kHeadThreads) {
+    const uint32_t key = kr[t];
+    if (kLdsKeys) lkeys[t] = key;
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = kmin;
+    red[1][wave] = kmax;
+  }
+  __syncthreads();
+  uint32_t lo = red[0][0], hi = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kHeadThreads / 64; ++w) {
+    lo = min(lo, red[0][w]);
+    hi = max(hi, red[1][w]);
+  }
+
+  uint32_t remaining = (uint32_t)kv;
+  uint32_t quota, thr;
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kHeadThreads) hbin[i] = 0;
+  for (;;) {
+    const uint32_t span = hi - lo;
+    if (span == 0) {
+      thr = lo;
+      quota = remaining;
+      break;
+    }
+    const int nbits = 32 - __clz(span);
+    const int shift = nbits > 8 ? nbits - 8 : 0;
+    if (tid < 256) hbin[tid] = 0;
     __syncthreads();
     for (int t = tid; t < hist; t += kHeadThreads) {
-      const uint32_t key = kr[t];
-      if ((key & mask) == prefix) atomicAdd(&hbin[(key >> shift) & 255u], 1u);
+      const uint32_t key = kLdsKeys ? lkeys[t] : kr[t];
+      if (key >= lo && key <= hi) atomicAdd(&hbin[(key - lo) >> shift], 1u);
     }
     __syncthreads();
-    if (tid < 64) {
-      const int top = 255 - 4 * tid;
+    if (wave == 0) {
+      const int top = 255 - 4 * lane;
       const uint32_t c0 = hbin[top], c1 = hbin[top - 1], c2 = hbin[top - 2], c3 = hbin[top - 3];
       const uint32_t s = c0 + c1 + c2 + c3;
       const uint32_t incl = wave_incl_scan(s);
       const uint32_t excl = incl - s;
       if (excl < remaining && remaining <= incl) {
-        uint32_t c = excl;
-        int dig;
-        uint32_t bin;
+        uint32_t c = excl, n;
+        int bk;
         if (c + c0 >= remaining) {
-          dig = top; bin = c0;
+          bk = top; n = c0;
         } else if ((c += c0) + c1 >= remaining) {
-          dig = top - 1; bin = c1;
+          bk = top - 1; n = c1;
         } else if ((c += c1) + c2 >= remaining) {
-          dig = top - 2; bin = c2;
+          bk = top - 2; n = c2;
         } else {
           c += c2;
-          dig = top - 3; bin = c3;
+          bk = top - 3; n = c3;
         }
-        sh_digit = (uint32_t)dig;
-        sh_above = c;
-        sh_bin = bin;
+        shv[0] = (uint32_t)bk;
+        shv[1] = c;
+        shv[2] = n;
       }
     }
     __syncthreads();
-    prefix |= sh_digit << shift;
-    mask |= 255u << shift;
-    remaining -= sh_above;
-    eq_total = sh_bin;  // after the last pass: number of keys equal to the threshold
-    __syncthreads();
-  }
-  const uint32_t thr = prefix;
-  const int lane = tid & 63;
-  if (eq_total == remaining) {
-    // every key equal to the threshold is taken: membership is key >= thr
-    for (int t0 = 0; t0 < hist; t0 += kHeadThreads) {
-      const int t = t0 + tid;
-      const bool sel = t < hist && kr[min(t, hist - 1)] >= thr;
-      const uint64_t bal = __ballot(sel);
-      if (lane == 0 && (t >> 5) < words) br[t >> 5] = (uint32_t)bal;
-      if (lane == 32 && (t >> 5) < words) br[t >> 5] = (uint32_t)(bal >> 32);
+    const uint32_t bk = shv[0], above = shv[1], n = shv[2];
+    remaining -= above;
+    const uint64_t blo = (uint64_t)lo + ((uint64_t)bk << shift);
+    const uint64_t bhi = (uint64_t)lo + (((uint64_t)bk + 1) << shift) - 1;
+    lo = (uint32_t)blo;
+    hi = bhi < (uint64_t)hi ? (uint32_t)bhi : hi;
+    if (n == remaining) {
+      thr = lo;
+      quota = 0xFFFFFFFFu;
+      break;
     }
-  } else {
-    // only the lowest-index `remaining` of the equal keys are taken
-    uint32_t carry = 0;
-    for (int t0 = 0; t0 < hist; t0 += kHeadThreads) {
-      const int t = t0 + tid;
-      const uint32_t key = t < hist ? kr[t] : 0u;
+  }
+
+  // membership bitmask in token order (lanes 0 and 32 of each wave store a word)
+  uint32_t carry = 0;
+  for (int t0 = 0; t0 < hist; t0 += kHeadThreads) {
+    const int t = t0 + tid;
+    const uint32_t key = t < hist ? (kLdsKeys ? lkeys[t] : kr[t]) : 0u;
+    bool sel;
+    if (quota == 0xFFFFFFFFu) {
+      sel = t < hist && key >= thr;
+    } else {
       const bool eq = t < hist && key == thr;
       uint64_t tot;
       const uint32_t before = carry + (uint32_t)block_excl_scan64(eq ? 1 : 0, scan_scratch, &tot);
-      const bool sel = t < hist && (key > thr || (eq && before < remaining));
-      const uint64_t bal = __ballot(sel);
-      if (lane == 0 && (t >> 5) < words) br[t >> 5] = (uint32_t)bal;
-      if (lane == 32 && (t >> 5) < words) br[t >> 5] = (uint32_t)(bal >> 32);
+      sel = t < hist && (key > thr || (eq && before < quota));
       carry += (uint32_t)tot;
     }
+    const uint64_t bal = __ballot(sel);
+    if (lane == 0 && (t >> 5) < words) br[t >> 5] = (uint32_t)bal;
+    if (lane == 32 && (t >> 5) < words) br[t >> 5] = (uint32_t)(bal >> 32);
   }
 }
 
 // ------------------------------------------------------------------ 3
-__device__ __forceinline__ void word_votes(const uint32_t* __restrict__ bits, int64_t stride,
-                                           int Hq, int w, uint32_t* cnt) {
-#pragma unroll
-  for (int i = 0; i < 32; ++i) cnt[i] = 0;
-  for (int h = 0; h < Hq; ++h) {
-    const uint32_t x = bits[(int64_t)h * stride + w];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) cnt[i] += (x >> i) & 1u;
+__global__ __launch_bounds__(kCountThreads) void vote_count_kernel(
+    const uint32_t* __restrict__ bits, int Hq, int hist, int words, int T,
+    uint8_t* __restrict__ votes8, uint8_t* __restrict__ votes, uint32_t* __restrict__ vhist) {
+  __shared__ uint32_t lh[256];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * kCountThreads + tid;
+  lh[tid] = 0u;  // kCountThreads == 256 bins
+  __syncthreads();
+  if (t < hist) {
+    const uint32_t* bb = bits + (int64_t)b * Hq * words + (t >> 5);
+    const int bit = t & 31;
+    uint32_t cnt = 0;
+#pragma unroll 8
+    for (int h = 0; h < Hq; ++h) cnt += (bb[(int64_t)h * words] >> bit) & 1u;
+    votes8[(int64_t)b * hist + t] = (uint8_t)cnt;
+    if (votes) votes[(int64_t)b * T + t] = (uint8_t)cnt;
+    atomicAdd(&lh[cnt], 1u);
   }
+  __syncthreads();
+  if (lh[tid]) atomicAdd(&vhist[b * 256 + tid], lh[tid]);
 }
 
+// ------------------------------------------------------------------ 4
 __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
-    const uint32_t* __restrict__ bits, int Hq, int T, int hist, int words, int kv, int N, int W,
-    int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
-  __shared__ uint32_t vbin[256];
+    const uint8_t* __restrict__ votes8, const uint32_t* __restrict__ vhist, int T, int hist, int kv,
+    int N, int W, int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
   __shared__ uint64_t scan_scratch[17];
   __shared__ uint32_t sh_v, sh_above;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const uint32_t* bb = bits + (int64_t)b * Hq * words;
-
-  for (int i = tid; i < 256; i += kSetThreads) vbin[i] = 0;
-  __syncthreads();
-  for (int w = tid; w < words; w += kSetThreads) {
-    uint32_t cnt[32];
-    word_votes(bb, words, Hq, w, cnt);
-    const int nt = min(32, hist - w * 32);
-    for (int i = 0; i < nt; ++i) atomicAdd(&vbin[cnt[i]], 1u);
+  int32_t* out = token_idx + (int64_t)b * N;
+  for (int i = tid; i < W; i += kSetThreads) {
+    out[kv + i] = hist + i;
+    if (votes) votes[(int64_t)b * T + hist + i] = 0;
   }
-  __syncthreads();
+  if (kv == 0) return;  // uniform: the whole workgroup leaves
   // vote threshold v*: count(votes > v*) < kv <= count(votes >= v*)
   if (tid < 64) {
     const int top = 255 - 4 * tid;
-    const uint32_t c0 = vbin[top], c1 = vbin[top - 1], c2 = vbin[top - 2], c3 = vbin[top - 3];
+    const uint32_t* vh = vhist + b * 256;
+    const uint32_t c0 = vh[top], c1 = vh[top - 1], c2 = vh[top - 2], c3 = vh[top - 3];
     const uint32_t s = c0 + c1 + c2 + c3;
     const uint32_t incl = wave_incl_scan(s);
     const uint32_t excl = incl - s;
@@ -236,51 +358,32 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
       sh_above = c;
     }
   }
-  if (tid == 0 && kv == 0) {  // nothing is voted in: no count exceeds 256
-    sh_v = 256u;
-    sh_above = 0u;
-  }
   __syncthreads();
   const uint32_t vthr = sh_v;
   const uint32_t take_eq = (uint32_t)kv - sh_above;
 
-  // ascending compaction over contiguous word runs
-  const int per = (words + kSetThreads - 1) / kSetThreads;
-  const int wa = min(tid * per, words), wb = min(wa + per, words);
+  // ascending compaction over contiguous runs of tokens
+  const uint8_t* vb = votes8 + (int64_t)b * hist;
+  const int per = (hist + kSetThreads - 1) / kSetThreads;
+  const int ta = min(tid * per, hist), tb = min(ta + per, hist);
   uint32_t n_gt = 0, n_eq = 0;
-  for (int w = wa; w < wb; ++w) {
-    uint32_t cnt[32];
-    word_votes(bb, words, Hq, w, cnt);
-    const int nt = min(32, hist - w * 32);
-    for (int i = 0; i < nt; ++i) {
-      n_gt += cnt[i] > vthr;
-      n_eq += cnt[i] == vthr;
-    }
+  for (int t = ta; t < tb; ++t) {
+    const uint32_t v = vb[t];
+    n_gt += v > vthr;
+    n_eq += v == vthr;
   }
   uint64_t total;
   const uint64_t before = block_excl_scan64(((uint64_t)n_gt << 32) | n_eq, scan_scratch, &total);
   uint32_t gt_before = (uint32_t)(before >> 32), eq_before = (uint32_t)before;
-  int32_t* out = token_idx + (int64_t)b * N;
-  uint8_t* vout = votes ? votes + (int64_t)b * T : nullptr;
-  for (int w = wa; w < wb; ++w) {
-    uint32_t cnt[32];
-    word_votes(bb, words, Hq, w, cnt);
-    const int nt = min(32, hist - w * 32);
-    for (int i = 0; i < nt; ++i) {
-      const int t = w * 32 + i;
-      if (vout) vout[t] = (uint8_t)cnt[i];
-      if (cnt[i] > vthr) {
-        out[gt_before + min(eq_before, take_eq)] = t;
-        ++gt_before;
-      } else if (cnt[i] == vthr) {
-        if (eq_before < take_eq) out[gt_before + eq_before] = t;
-        ++eq_before;
-      }
+  for (int t = ta; t < tb; ++t) {
+    const uint32_t v = vb[t];
+    if (v > vthr) {
+      out[gt_before + min(eq_before, take_eq)] = t;
+      ++gt_before;
+    } else if (v == vthr) {
+      if (eq_before < take_eq) out[gt_before + eq_before] = t;
+      ++eq_before;
     }
-  }
-  for (int i = tid; i < W; i += kSetThreads) {
-    out[kv + i] = hist + i;
-    if (vout) vout[hist + i] = 0;
   }
 }
 
@@ -293,6 +396,10 @@ __global__ void vote_all_kernel(int T, int32_t* __restrict__ token_idx, uint8_t*
   }
 }
 
+#ifndef KSA_MFMA
+#define KSA_MFMA 1
+#endif
+
 template <typename T, int D, int G>
 hipError_t launch_scores(const Dims& d, const void* q, const void* k, int hist, uint32_t* keys,
                          hipStream_t s) {
@@ -300,8 +407,14 @@ hipError_t launch_scores(const Dims& d, const void* q, const void* k, int hist, 
   const int nchunks = (hist + ch - 1) / ch;
   const int per_wg = kScoreWaves * kScoreChunksPerWave;
   const dim3 grid((nchunks + per_wg - 1) / per_wg, d.B * d.Hkv);
-  hipLaunchKernelGGL((vote_scores_kernel<T, D, G>), grid, dim3(kScoreWaves * 64), 0, s,
-                     (const T*)q, (const T*)k, d, hist, keys);
+  constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
+  if constexpr (mfma) {
+    hipLaunchKernelGGL((vote_scores_mfma_kernel<G>), grid, dim3(kScoreWaves * 64), 0, s,
+                       (const uint16_t*)q, (const uint16_t*)k, d, hist, keys);
+  } else {
+    hipLaunchKernelGGL((vote_scores_kernel<T, D, G>), grid, dim3(kScoreWaves * 64), 0, s,
+                       (const T*)q, (const T*)k, d, hist, keys);
+  }
   return hipGetLastError();
 }
 
@@ -316,6 +429,8 @@ hipError_t launch_scores_g(const Dims& d, const void* q, const void* k, int hist
   }
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 VotePlan plan_vote(const Dims& d, int N, int W) {
@@ -325,9 +440,10 @@ VotePlan plan_vote(const Dims& d, int N, int W) {
   p.kv = N - W;
   const size_t rows = (size_t)d.B * d.Hq;
   p.keys_off = 0;
-  const size_t keys_bytes = rows * (size_t)p.hist * sizeof(uint32_t);
-  p.bits_off = (p.keys_off + keys_bytes + 255) & ~(size_t)255;
-  p.total = p.bits_off + rows * (size_t)p.words * sizeof(uint32_t);
+  p.bits_off = align256(rows * (size_t)p.hist * sizeof(uint32_t));
+  p.votes_off = align256(p.bits_off + rows * (size_t)p.words * sizeof(uint32_t));
+  p.vhist_off = align256(p.votes_off + (size_t)d.B * p.hist);
+  p.total = p.vhist_off + (size_t)d.B * 256 * sizeof(uint32_t);
   if (d.T <= N) p.total = 0;
   return p;
 }
@@ -340,8 +456,11 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
                        token_idx, votes);
     return hipGetLastError();
   }
-  uint32_t* keys = (uint32_t*)((char*)workspace + plan.keys_off);
-  uint32_t* bits = (uint32_t*)((char*)workspace + plan.bits_off);
+  char* ws = (char*)workspace;
+  uint32_t* keys = (uint32_t*)(ws + plan.keys_off);
+  uint32_t* bits = (uint32_t*)(ws + plan.bits_off);
+  uint8_t* votes8 = (uint8_t*)(ws + plan.votes_off);
+  uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
   hipError_t e;
   if (d.dtype == KSA_BF16)
     e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, keys, stream)
@@ -350,12 +469,28 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
     e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, keys, stream)
                   : launch_scores_g<float, 128>(d, q, k, plan.hist, keys, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vote_head_select_kernel, dim3(d.B * d.Hq), dim3(kHeadThreads), 0, stream,
-                     keys, plan.hist, plan.kv, plan.words, bits);
+  if (plan.hist <= kHeadLdsKeys) {
+    const size_t lds = (size_t)plan.hist * sizeof(uint32_t);
+    if (lds > 65536) {
+      e = hipFuncSetAttribute((const void*)vote_head_select_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(vote_head_select_kernel<true>, dim3(d.B * d.Hq), dim3(kHeadThreads), lds,
+                       stream, keys, plan.hist, plan.kv, plan.words, d.Hq, bits, vhist);
+  } else {
+    hipLaunchKernelGGL(vote_head_select_kernel<false>, dim3(d.B * d.Hq), dim3(kHeadThreads), 0,
+                       stream, keys, plan.hist, plan.kv, plan.words, d.Hq, bits, vhist);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vote_set_kernel, dim3(d.B), dim3(kSetThreads), 0, stream, bits, d.Hq, d.T,
-                     plan.hist, plan.words, plan.kv, N, W, token_idx, votes);
+  hipLaunchKernelGGL(vote_count_kernel, dim3((plan.hist + kCountThreads - 1) / kCountThreads, d.B),
+                     dim3(kCountThreads), 0, stream, bits, d.Hq, plan.hist, plan.words, d.T, votes8,
+                     votes, vhist);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vote_set_kernel, dim3(d.B), dim3(kSetThreads), 0, stream, votes8, vhist, d.T,
+                     plan.hist, plan.kv, N, W, token_idx, votes);
   return hipGetLastError();
 }
 
