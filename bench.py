@@ -56,6 +56,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of 1 GiB (counter calibration)")
+    ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                          "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv files "
+                         "(workload run, then the --copy-probe run) into "
+                         "profiles/traffic_sparse_decode_<workload>.json")
     return ap.parse_args()
 
 
@@ -65,6 +70,53 @@ def source_hash(paths):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+ATTN_SOURCES = ("attention.hip", "ksa_device.h", "ksa_internal.h")
+
+
+def attn_source_hash():
+    return source_hash([os.path.join(ROOT, "sparse_attention_decode_ksa_amd", "csrc", n)
+                        for n in ATTN_SOURCES])
+
+
+def counter_summary(args):
+    """HBM bytes per launch of the sparse attention kernel from rocprofv3 --pmc
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the same
+    counter reads for a plain copy of 1 GiB (bytes moved / counter bytes)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, want):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if want(r["Kernel_Name"])]
+        return statistics.median(vals), len(vals)
+
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.counter_summary
+
+    def is_sparse(name):
+        # the block-sparse attention kernel (KIND 0) of either variant
+        base = name.replace("ksa::(anonymous namespace)::", "")
+        return (base.startswith("void attn_partial_kernel<") or base.startswith("void attn_mfma_kernel<")) \
+            and base.split(">(")[0].endswith(", 0")
+
+    copy = lambda n: n == "__amd_rocclr_copyBuffer"
+    f_kib, nf = per_kernel(fetch_csv, is_sparse)
+    w_kib, nw_ = per_kernel(write_csv, is_sparse)
+    cf_kib, _ = per_kernel(cfetch_csv, copy)
+    cw_kib, _ = per_kernel(cwrite_csv, copy)
+    gib = float(1 << 30)
+    f_scale, w_scale = gib / (cf_kib * 1024.0), gib / (cw_kib * 1024.0)
+    out = {"workload": args.workload, "kernel": "ksa_sparse_decode, selected blocks",
+           "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+           "dispatches": [nf, nw_], "copy_1GiB_fetch_kib": cf_kib, "copy_1GiB_write_kib": cw_kib,
+           "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6),
+           "bytes_per_launch": int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale)),
+           "source_hash": attn_source_hash()}
+    path = os.path.join(ROOT, "profiles", "traffic_sparse_decode_%s.json" % args.workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def copy_probe():
@@ -121,6 +173,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.counter_summary:
+        counter_summary(args)
         return
 
     import numpy as np
@@ -277,9 +332,7 @@ def main():
     if os.path.exists(tr_path):
         with open(tr_path) as f:
             tr = json.load(f)
-        cur = source_hash([os.path.join(ROOT, "sparse_attention_decode_ksa_amd", "csrc", n)
-                           for n in ("attention.hip", "ksa_device.h", "ksa_internal.h")])
-        if tr.get("source_hash") == cur:
+        if tr.get("source_hash") == attn_source_hash():
             traffic = tr.get("bytes_per_launch")
 
     # ---------------------------------------------------------------- CPU baseline (oracle)

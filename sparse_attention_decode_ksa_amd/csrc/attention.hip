@@ -593,24 +593,26 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   const int ch = chunk_tokens(d);
   const int64_t chunks = (tokens_per_row + ch - 1) / ch;
   const int64_t rows = (int64_t)d.B * d.Hkv;
-  const int64_t kTargetWaves = 4096;  // 256 CUs x 16 resident waves
-  const int64_t kMinChunksPerWave = 4;
-  const int64_t want = (kTargetWaves + rows - 1) / rows;
-  const int64_t useful = chunks / kMinChunksPerWave > 1 ? chunks / kMinChunksPerWave : 1;
-  const int64_t wpr = want < useful ? want : useful;
+  const int64_t kCUs = 256;              // MI355X compute units
+  const int64_t kMinChunksPerWave = 8;   // keeps each wave's pipeline busy past its fill
+  // Fewest splits that still give every CU a workgroup (a split costs a merge),
+  // as long as each split keeps real work.
+  int64_t splits = (kCUs + rows - 1) / rows;
+  const int64_t max_splits = chunks / kMinChunksPerWave > 1 ? chunks / kMinChunksPerWave : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t cps = (chunks + splits - 1) / splits;
   int nw = 1;
-  while (nw < kMaxWaves && nw * 2 <= wpr) nw *= 2;
-  int64_t splits = (wpr + nw - 1) / nw;
+  while (nw < kMaxWaves && (int64_t)nw * 2 * kMinChunksPerWave <= cps) nw *= 2;
   // Tuning override "waves,splits" for launch-shape sweeps (read per call).
   if (const char* env = getenv("KSA_ATTN_PLAN")) {
     int enw = 0, esp = 0;
     if (sscanf(env, "%d,%d", &enw, &esp) == 2 && enw >= 1 && enw <= kMaxWaves && esp >= 1) {
       nw = enw;
       splits = esp;
+      cps = (chunks + splits - 1) / splits;
     }
   }
-  if (splits < 1) splits = 1;
-  int64_t cps = (chunks + splits - 1) / splits;
   // a workgroup's index slice must fit the LDS stage
   int64_t cap = INT64_MAX;
   if (kind == 1) cap = kIdxStage / ch;
