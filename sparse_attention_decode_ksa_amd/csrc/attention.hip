@@ -208,8 +208,36 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
   }
 }
 
+// Stages the index slice a workgroup (row, split) needs in LDS; returns the
+// first staged entry.  No barrier: the caller syncs before reading s_idx.
+template <int KIND, int CH>
+__device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int split, int* s_idx) {
+  if constexpr (KIND == 2) return 0;
+  const Dims& d = a.d;
+  const int nchunks = (a.ltot + CH - 1) / CH;
+  const int c_begin = split * a.cps;
+  const int c_end = min(c_begin + a.cps, nchunks);
+  int e0, e1;
+  const int32_t* src;
+  if constexpr (KIND == 0) {
+    e0 = (c_begin * CH) / d.Bs;
+    e1 = min(a.count, (c_end * CH + d.Bs - 1) / d.Bs);
+    src = a.idx + (int64_t)row * a.count;
+  } else {
+    const int b = row / d.Hkv;
+    e0 = c_begin * CH;
+    e1 = min(a.ltot, c_end * CH);
+    src = a.idx + (int64_t)b * a.count;
+  }
+  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
+  return e0;
+}
+
+// Attention of one row (or one split of it) on VALU; the row's index slice is
+// staged in s_idx (entries from e0 on).  `sync` waits for the staging.
 template <typename T, int D, int G, int KIND>
-__global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int split, const int* s_idx,
+                                              int e0, bool sync) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int SPW = 64 / LPT;
@@ -219,14 +247,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
   __shared__ float s_m[kMaxWaves][G];
   __shared__ float s_l[kMaxWaves][G];
   __shared__ float s_acc[kMaxWaves][G][D];
-  __shared__ int s_idx[kIdxStage];
 
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const int slot = lane / LPT, li = lane % LPT;
-  const int split = blockIdx.x % a.splits;
-  const int row = blockIdx.x / a.splits;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const int64_t kvrow = (int64_t)row * d.Tcap * D + li * EPL;
   const T* kbase = (const T*)a.k + kvrow;
@@ -235,23 +260,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
   const int nchunks = (a.ltot + CH - 1) / CH;
   const int c_begin = split * a.cps;
   const int c_end = min(c_begin + a.cps, nchunks);
-
-  // stage this workgroup's slice of the index list in LDS
-  int e0 = 0;
-  if constexpr (KIND != 2) {
-    int e1;
-    const int32_t* src;
-    if constexpr (KIND == 0) {
-      e0 = (c_begin * CH) / d.Bs;
-      e1 = min(a.count, (c_end * CH + d.Bs - 1) / d.Bs);
-      src = a.idx + (int64_t)row * a.count;
-    } else {
-      e0 = c_begin * CH;
-      e1 = min(a.ltot, c_end * CH);
-      src = a.idx + (int64_t)b * a.count;
-    }
-    for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
-  }
 
   float qv[G][EPL];
 #pragma unroll
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  if constexpr (KIND != 2) __syncthreads();
+  if (sync) __syncthreads();
 
   const int c0 = c_begin + wave;
   const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
@@ -332,6 +340,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
   merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
 }
 
+// For G <= 2 the register budget is held at 128 per lane, so that two
+// 512-thread workgroups (16 waves) fit on a CU.
+template <typename T, int D, int G, int KIND>
+__global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_partial_kernel(AttnArgs a) {
+  constexpr int CH = (64 / (D / KV<T>::EPL)) * kLoadsPerChunk;
+  __shared__ int s_idx[kIdxStage];
+  const int split = blockIdx.x % a.splits;
+  const int row = blockIdx.x / a.splits;
+  const int e0 = stage_indices<KIND, CH>(a, row, split, s_idx);
+  attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, e0, KIND != 2);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA variant for bf16, D = 128 and G in {4, 8}.  Per chunk of 16 tokens:
 //  * QK^T on v_mfma_f32_16x16x32_bf16: A = 16 token rows x 32 dims of K (lane
@@ -350,8 +370,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_partial_kernel(AttnArgs a
 //    where P.V accumulates on VALU in fp32.
 // Softmax state is per wave rather than per slot, so the slots of a wave are
 // merged by plain sums.
+// Attention of one row (or one split of it) with MFMA QK^T (bf16, D = 128,
+// G in {4, 8}); indices staged as for attn_row_valu.
 template <int G, int KIND>
-__global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int split, const int* s_idx,
+                                              int e0, bool sync) {
   constexpr int D = 128;
   constexpr int EPL = 8;
   constexpr int LPT = 16;
@@ -362,7 +385,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   __shared__ float s_m[kMaxWaves][G];
   __shared__ float s_l[kMaxWaves][G];
   __shared__ float s_acc[kMaxWaves][G][D];
-  __shared__ int s_idx[kIdxStage];
   __shared__ float s_p[kMaxWaves][CH + 1][8];  // rows 0..15: P[token][head]; row 16: rescale
 
   const Dims& d = a.d;
@@ -370,8 +392,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   const int nw = blockDim.x >> 6;
   const int r = lane & 15, kg = lane >> 4;  // MFMA: row/column and k-group / row quad
   const int slot = kg, li = r;             // V layout: token slot and 16-byte piece
-  const int split = blockIdx.x % a.splits;
-  const int row = blockIdx.x / a.splits;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const int64_t kvrow = (int64_t)row * d.Tcap * D;
   const uint16_t* kbase = (const uint16_t*)a.k + kvrow + 8 * kg;
@@ -380,22 +400,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   const int nchunks = (a.ltot + CH - 1) / CH;
   const int c_begin = split * a.cps;
   const int c_end = min(c_begin + a.cps, nchunks);
-
-  int e0 = 0;
-  if constexpr (KIND != 2) {
-    int e1;
-    const int32_t* src;
-    if constexpr (KIND == 0) {
-      e0 = (c_begin * CH) / d.Bs;
-      e1 = min(a.count, (c_end * CH + d.Bs - 1) / d.Bs);
-      src = a.idx + (int64_t)row * a.count;
-    } else {
-      e0 = c_begin * CH;
-      e1 = min(a.ltot, c_end * CH);
-      src = a.idx + (int64_t)b * a.count;
-    }
-    for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
-  }
 
   // B operand: the group's queries, column n = head r (zero past G)
   bf16x8_t qop[4];
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  if constexpr (KIND != 2) __syncthreads();
+  if (sync) __syncthreads();
 
   const int c0 = c_begin + wave;
   const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
@@ -520,6 +524,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   }
   __syncthreads();
   merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
+}
+
+template <int G, int KIND>
+__global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
+  __shared__ int s_idx[kIdxStage];
+  const int split = blockIdx.x % a.splits;
+  const int row = blockIdx.x / a.splits;
+  const int e0 = stage_indices<KIND, 16>(a, row, split, s_idx);
+  attn_row_mfma<G, KIND>(a, row, split, s_idx, e0, KIND != 2);
 }
 
 // Fixed-order merge of the split partial states of each row.

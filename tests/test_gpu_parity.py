@@ -381,3 +381,26 @@ def test_hip_graph_replay_matches_eager_calls():
     # the last replay also agrees with the oracle
     ro, rl = oracle.attend_blocks(np_bits(qbuf), np_bits(k), np_bits(v), w.T, w.Bs, idx.cpu().numpy())
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("T,Bs,k", [(4000, 1, 300), (15360, 1, 1000), (9000, 2, 77)])
+def test_select_topk_large_block_counts(T, Bs, k):
+    """Rows of 4000, 15360 (the supported maximum) and 4500 blocks exercise the
+    top-k kernel's larger register tiles."""
+    w = small_workload(B=2, Hq=4, Hkv=2, D=64, T=T, Bs=Bs, dtype="bf16", top_k=k, seed=T)
+    q, k_, v = gpu_inputs(w)
+    s = run_summaries(k_, w)
+    idx = ksa.ksa_select_topk(q, s, w.T, w.Bs, w.top_k)
+    raw, _ = oracle.group_scores(np_bits(q), np_bits(s), w.T, w.Bs)
+    check_block_selection(idx.cpu().numpy().reshape(4, -1), raw.reshape(4, -1), w.top_k)
+
+
+def test_vote_select_history_longer_than_lds():
+    """More than 36864 history tokens: the per-head selection streams its keys
+    from the workspace instead of holding them in LDS."""
+    w = small_workload(B=1, Hq=8, Hkv=2, D=64, T=40000, dtype="bf16", seed=40)
+    q, k, v = gpu_inputs(w)
+    idx, votes = ksa.ksa_vote_select(q, k, w.T, 4096, 1024, want_votes=True)
+    torch.cuda.synchronize()
+    lg = oracle.head_logits(np_bits(q), np_bits(k), w.T)
+    check_votes(votes.cpu().numpy(), idx.cpu().numpy(), lg, 4096, 1024)
