@@ -3,6 +3,10 @@
 Block top-k workloads (c2 default, c3, c5): one step = refresh the summary of
 the block holding the newest token, score and select the top-k blocks of every
 (sequence, KV head), and attend the selected blocks with every query head.
+--path fused (default) times that step as one ksa_block_topk_decode launch;
+--path calls times it as ksa_block_summaries + ksa_select_topk +
+ksa_sparse_decode.  The other path is timed beside it and its outputs are
+checked to be bitwise the same.
 Vote-union workload (c4): one step = the selection layer's vote (all heads
 score every history token, votes are pooled, the recency window appended) and
 the attention over the shared set; the sparse-layer step (attention over a
@@ -19,11 +23,12 @@ the eager step's outputs bit for bit.  Timed regions (each bracketed by
 torch.cuda.synchronize() and HIP events on the stream the kernels run on):
   1. K whole steps back to back (graph replays)  -> value, ms_per_step
   2. K launches of the dominant call alone        -> roofline.achieved
+     (for the fused path the step is that one call)
   3. dense decode steps                           -> dense, speedup_vs_dense
   4. K whole steps launched eagerly               -> eager_ms_per_step
 Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--path fused|calls]
     python bench.py --copy-probe      # a plain 1 GiB copy, to calibrate HBM counters
 """
 from __future__ import annotations
@@ -50,6 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--path", default="fused", choices=["fused", "calls"],
+                    help="block top-k step as one fused launch or as the three separate calls")
     ap.add_argument("--layers", type=int, default=0, help="KV caches cycled over (0: auto)")
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,18 +79,29 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-ATTN_SOURCES = ("attention.hip", "ksa_device.h", "ksa_internal.h")
+# sources of the kernel each traffic record covers
+KERNEL_SOURCES = {
+    "sparse_decode": ("attention.hip", "ksa_attention.h", "ksa_device.h", "ksa_internal.h"),
+    "block_topk_decode": ("decode_step.hip", "ksa_attention.h", "ksa_topk.h", "ksa_device.h",
+                          "ksa_internal.h"),
+}
 
 
-def attn_source_hash():
+def kernel_source_hash(kernel):
     return source_hash([os.path.join(ROOT, "sparse_attention_decode_ksa_amd", "csrc", n)
-                        for n in ATTN_SOURCES])
+                        for n in KERNEL_SOURCES[kernel]])
+
+
+def traffic_kernel(args):
+    return "block_topk_decode" if args.path == "fused" and args.workload != "c4" else "sparse_decode"
 
 
 def counter_summary(args):
-    """HBM bytes per launch of the sparse attention kernel from rocprofv3 --pmc
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the same
-    counter reads for a plain copy of 1 GiB (bytes moved / counter bytes)."""
+    """HBM bytes per launch of the timed path's dominant kernel (the fused step
+    kernel, or the sparse attention kernel of the separate calls) from
+    rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for a plain copy of 1 GiB (bytes moved /
+    counter bytes)."""
     import csv
     import statistics
 
@@ -94,11 +112,16 @@ def counter_summary(args):
 
     fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.counter_summary
 
+    kernel = traffic_kernel(args)
+
     def is_sparse(name):
-        # the block-sparse attention kernel (KIND 0) of either variant
         base = name.replace("ksa::(anonymous namespace)::", "")
+        if kernel == "block_topk_decode":
+            return base.startswith("void block_topk_decode_kernel<")
+        # the sparse attention kernel over a block (KIND 0) or token (KIND 1) list
+        kind = "1" if args.workload == "c4" else "0"
         return (base.startswith("void attn_partial_kernel<") or base.startswith("void attn_mfma_kernel<")) \
-            and base.split(">(")[0].endswith(", 0")
+            and base.split(">(")[0].endswith(", " + kind)
 
     copy = lambda n: n == "__amd_rocclr_copyBuffer"
     f_kib, nf = per_kernel(fetch_csv, is_sparse)
@@ -107,13 +130,15 @@ def counter_summary(args):
     cw_kib, _ = per_kernel(cwrite_csv, copy)
     gib = float(1 << 30)
     f_scale, w_scale = gib / (cf_kib * 1024.0), gib / (cw_kib * 1024.0)
-    out = {"workload": args.workload, "kernel": "ksa_sparse_decode, selected blocks",
+    names = {"block_topk_decode": "ksa_block_topk_decode (fused step)",
+             "sparse_decode": "ksa_sparse_decode"}
+    out = {"workload": args.workload, "kernel": names[kernel],
            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
            "dispatches": [nf, nw_], "copy_1GiB_fetch_kib": cf_kib, "copy_1GiB_write_kib": cw_kib,
            "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6),
            "bytes_per_launch": int(round(f_kib * 1024 * f_scale + w_kib * 1024 * w_scale)),
-           "source_hash": attn_source_hash()}
-    path = os.path.join(ROOT, "profiles", "traffic_sparse_decode_%s.json" % args.workload)
+           "source_hash": kernel_source_hash(kernel)}
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, args.workload))
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -221,6 +246,9 @@ def main():
             x["s"] = torch.empty((B, Hkv, NB, D), dtype=x["k"].dtype, device=dev)
             ksa.ksa_block_summaries(x["k"], x["s"], T, Bs)  # prefill: every block
             x["idx"] = torch.empty((B, Hkv, keff), dtype=torch.int32, device=dev)
+            # outputs of the path that is not the timed one
+            x["out2"], x["lse2"] = torch.empty_like(x["out"]), torch.empty_like(x["lse"])
+            x["idx2"] = torch.empty_like(x["idx"])
         L.append(x)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
@@ -241,6 +269,7 @@ def main():
     sp = ctypes.c_void_p(stream.cuda_stream)
     V = lambda t: ctypes.c_void_p(t.data_ptr())
     last_block = (T - 1) // Bs
+    fused_path = args.path == "fused" and not vote
     for x in L:
         kind = ksa.KSA_SEL_TOKENS if vote else ksa.KSA_SEL_BLOCKS
         x["sel"] = ksa.Selection(kind, V(x["idx"]).value, n_sel if vote else keff)
@@ -251,20 +280,41 @@ def main():
         if vote:
             select = [(lib.ksa_vote_select, (pp, V(x["q"]), V(x["k"]), N, W, V(x["idx"]), None,
                                              V(wsel), wsel.numel(), sp))]
+            fused = None
         else:
+            # the separate calls write the *2 buffers when the fused step is timed
+            o, l_, i_ = ((x["out2"], x["lse2"], x["idx2"]) if fused_path
+                         else (x["out"], x["lse"], x["idx"]))
+            x["sel"] = ksa.Selection(kind, V(i_).value, keff)
+            attn = (lib.ksa_sparse_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]),
+                                            ctypes.byref(x["sel"]), V(o), V(l_), V(wat),
+                                            wat.numel(), sp))
             select = [(lib.ksa_block_summaries, (pp, V(x["k"]), V(x["s"]), last_block, 1, sp)),
-                      (lib.ksa_select_topk, (pp, V(x["q"]), V(x["s"]), K, V(x["idx"]), None,
+                      (lib.ksa_select_topk, (pp, V(x["q"]), V(x["s"]), K, V(i_), None,
                                              V(wsel), wsel.numel(), sp))]
-        x["calls"] = dict(select=select, attn=attn, dense=dense)
+            o, l_, i_ = ((x["out"], x["lse"], x["idx"]) if fused_path
+                         else (x["out2"], x["lse2"], x["idx2"]))
+            fused = (lib.ksa_block_topk_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]), V(x["s"]), K,
+                                                 1, V(i_), V(o), V(l_), sp))
+        x["calls"] = dict(select=select, attn=attn, dense=dense, fused=fused)
 
-    def step(i):
+    def calls_step(i):
         c = L[i % layers]["calls"]
         for s_ in c["select"]:
             R.run(s_)
         R.run(c["attn"])
 
+    def fused_step(i):
+        R.run(L[i % layers]["calls"]["fused"])
+
+    step = fused_step if fused_path else calls_step
+    other_step = None if vote else (calls_step if fused_path else fused_step)
+
     def attn_only(i):
-        R.run(L[i % layers]["calls"]["attn"])
+        if fused_path:
+            fused_step(i)
+        else:
+            R.run(L[i % layers]["calls"]["attn"])
 
     def select_only(i):
         for s_ in L[i % layers]["calls"]["select"]:
@@ -288,6 +338,15 @@ def main():
                 fn()
             return g
 
+        if other_step is not None:
+            # the other path on the same inputs gives bitwise the same step
+            for l, x in enumerate(L):
+                other_step(l)
+            torch.cuda.synchronize()
+            for l, x in enumerate(L):
+                assert torch.equal(x["idx2"], x["idx"]) and torch.equal(x["out2"], x["out"]) \
+                    and torch.equal(x["lse2"], x["lse"]), "fused step and separate calls differ"
+            g_other = capture(lambda: [other_step(l) for l in range(layers)])
         g_step = [capture(lambda l=l: step(l)) for l in range(layers)]
         g_cycle = capture(lambda: [step(l) for l in range(layers)])
         g_attn = capture(lambda: [attn_only(l) for l in range(layers)])
@@ -310,6 +369,9 @@ def main():
         ms_step = timed(torch, stream, full + rest, graph_steps) * (full + rest) / args.steps  # 1
         ms_attn = timed(torch, stream, max(full, 1), lambda i: g_attn.replay()) / layers      # 2
         ms_select = timed(torch, stream, args.steps, select_only)
+        ms_other = None
+        if other_step is not None:
+            ms_other = timed(torch, stream, max(full, 1), lambda i: g_other.replay()) / layers
         dense_only(0)
         ms_dense = timed(torch, stream, args.dense_steps, dense_only)  # region 3
 
@@ -325,14 +387,16 @@ def main():
                         + rows * (T - last_block * Bs) * D * elt + rows * D * elt)  # summary refresh
     step_bytes = attn_bytes + select_bytes
     dense_bytes = rows * T * D * elt * 2 + q_bytes + out_bytes
-    achieved = attn_bytes / (ms_attn * 1e-3) / 1e9
+    dom_bytes = step_bytes if fused_path else attn_bytes
+    achieved = dom_bytes / (ms_attn * 1e-3) / 1e9
 
     traffic = None
-    tr_path = os.path.join(ROOT, "profiles", "traffic_sparse_decode_%s.json" % w.name)
+    tk = traffic_kernel(args)
+    tr_path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (tk, w.name))
     if os.path.exists(tr_path):
         with open(tr_path) as f:
             tr = json.load(f)
-        if tr.get("source_hash") == attn_source_hash():
+        if tr.get("source_hash") == kernel_source_hash(tk):
             traffic = tr.get("bytes_per_launch")
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
@@ -370,8 +434,9 @@ def main():
         cfg.update(token_budget=N, recent_window=W)
         dom = "ksa_sparse_decode (shared token set)"
     else:
-        cfg.update(block_size=Bs, top_k_blocks=K)
-        dom = "ksa_sparse_decode (selected blocks, split-K online softmax)"
+        cfg.update(block_size=Bs, top_k_blocks=K, path=args.path)
+        dom = ("ksa_block_topk_decode (refresh + score + top-k + attention, one launch)"
+               if fused_path else "ksa_sparse_decode (selected blocks, split-K online softmax)")
     line = {
         "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
         "value": round(value, 1),
@@ -398,10 +463,14 @@ def main():
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "avg_launch_ms": round(ms_attn, 5),
-                     "bytes_per_launch": attn_bytes},
+                     "bytes_per_launch": dom_bytes},
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 2),
     }
+    if other_step is not None:
+        line["other_path"] = {"path": "calls" if fused_path else "fused",
+                              "ms_per_step": round(ms_other, 5),
+                              "speedup_vs_dense": round(ms_dense / ms_other, 3)}
     if vote:
         line["sparse_layer_step"] = {"ms": round(ms_attn, 5), "value": round(B / (ms_attn * 1e-3), 1),
                                      "speedup_vs_dense": round(ms_dense / ms_attn, 3)}

@@ -176,6 +176,32 @@ ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const voi
                             const void* v, float* out, float* lse, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * ksa_block_topk_decode -- one whole decode step of block top-k attention
+ * (Kinetics explainer, section 五) in a single launch, one workgroup per
+ * (sequence, KV head):
+ *   1. if refresh_last_block != 0: the summary of block (T-1)/Bs is
+ *      recomputed and written to summaries, exactly as
+ *      ksa_block_summaries(first_block = (T-1)/Bs, num_blocks = 1) does; the
+ *      other blocks' summaries are read as given;
+ *   2. the blocks are ranked as in ksa_select_topk(top_k) (same fp32
+ *      relevance, same ties); the k_eff = min(top_k, NB) ids are written,
+ *      ascending, to block_idx [B, Hkv, k_eff] int32 when it is not NULL;
+ *   3. out [B, Hq, D] fp32 and lse [B, Hq] fp32 (nullable) are the attention
+ *      of ksa_sparse_decode over those blocks.
+ * summaries and block_idx are bitwise those of the three separate calls; out
+ * and lse are too whenever ksa_sparse_decode would run one split of 8 waves
+ * per row for this shape, and otherwise differ only in the fp32 order of the
+ * final merge.  All rows run in one grid of B*Hkv workgroups, so the call is
+ * meant for batches with at least a few hundred (sequence, KV head) rows.
+ * Limits (else KSA_ERR_UNSUPPORTED): NB <= 4096, k_eff <= 2048,
+ * k_eff * Bs < 2^30, and Bs <= 64 when refresh_last_block is set.
+ * Needs no workspace. */
+ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, const void* k,
+                                 const void* v, void* summaries, int32_t top_k,
+                                 int32_t refresh_last_block, int32_t* block_idx, float* out,
+                                 float* lse, void* stream);
+
 /* Operations for ksa_workspace_bytes. */
 enum {
   KSA_OP_SELECT_TOPK = 0,    /* param: top_k */

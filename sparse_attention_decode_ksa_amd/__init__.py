@@ -8,8 +8,9 @@ library's HIP kernels; there is no CPU or PyTorch fallback, and a missing or
 unloadable library raises :class:`KsaLibraryError` on first use.
 
 Function names match the C entry points: ``ksa_block_summaries``,
-``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_vote_select``,
-``ksa_dense_decode``, ``ksa_workspace_bytes``, ``ksa_status_string``.
+``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode``,
+``ksa_vote_select``, ``ksa_dense_decode``, ``ksa_workspace_bytes``,
+``ksa_status_string``.
 """
 from __future__ import annotations
 
@@ -31,8 +32,9 @@ KSA_SEL_BLOCKS, KSA_SEL_TOKENS = 0, 1
  KSA_OP_DENSE) = range(5)
 SIZE_MAX = ctypes.c_size_t(-1).value
 
-EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode", "ksa_vote_select",
-            "ksa_dense_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
+            "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode",
+            "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
 
 
 class KsaLibraryError(RuntimeError):
@@ -84,6 +86,7 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_block_summaries.argtypes = [PP, P, P, I32, I32, P]
         lib.ksa_select_topk.argtypes = [PP, P, P, I32, P, P, P, SZ, P]
         lib.ksa_sparse_decode.argtypes = [PP, P, P, P, ctypes.POINTER(Selection), P, P, P, SZ, P]
+        lib.ksa_block_topk_decode.argtypes = [PP, P, P, P, P, I32, I32, P, P, P, P]
         lib.ksa_vote_select.argtypes = [PP, P, P, I32, I32, P, P, P, SZ, P]
         lib.ksa_dense_decode.argtypes = [PP, P, P, P, P, P, P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
@@ -93,7 +96,7 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
         for name in ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
-                     "ksa_vote_select", "ksa_dense_decode"):
+                     "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -247,6 +250,36 @@ def ksa_sparse_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len
                                  _dev(lse, "lse", torch.float32, (B, Hq)), pws, nws,
                                  _stream(stream)), "ksa_sparse_decode")
     return out, lse
+
+
+def ksa_block_topk_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          summaries: torch.Tensor, seq_len: int, block_size: int, top_k: int,
+                          refresh_last_block: bool = True, block_idx=None,
+                          want_block_idx: bool = False, out=None, lse=None, want_lse: bool = True,
+                          sm_scale: float = 0.0, stream=None):
+    """One whole decode step in one launch: refresh the newest block's summary
+    (in place, when asked), select the top-k blocks, attend them.
+    Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None,
+    block_idx [B,Hkv,min(k,NB)] int32 or None)."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len, block_size, sm_scale)
+    B, Hq, D = q.shape
+    Hkv, Tcap = k.shape[1], k.shape[2]
+    keff = min(top_k, nblocks(seq_len, block_size))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if block_idx is None and want_block_idx:
+        block_idx = torch.empty((B, Hkv, keff), dtype=torch.int32, device=q.device)
+    _check(lib.ksa_block_topk_decode(
+        ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"), _dev(v, "v", k.dtype, k.shape),
+        _dev(summaries, "summaries", k.dtype, (B, Hkv, nblocks(Tcap, block_size), D)),
+        int(top_k), 1 if refresh_last_block else 0,
+        _dev(block_idx, "block_idx", torch.int32, (B, Hkv, keff)),
+        _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
+        _stream(stream)), "ksa_block_topk_decode")
+    return out, lse, block_idx
 
 
 def ksa_vote_select(q: torch.Tensor, k: torch.Tensor, seq_len: int, token_budget: int,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libksa.so")
 OBJDIR = os.path.join(ROOT, "_build", "ksa")
-SOURCES = ["api.hip", "summaries.hip", "select.hip", "attention.hip", "vote.hip"]
+SOURCES = ["api.hip", "summaries.hip", "select.hip", "attention.hip", "vote.hip", "decode_step.hip"]
 ARCH = "gfx950"
 
 

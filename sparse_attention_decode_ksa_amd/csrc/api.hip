@@ -201,4 +201,23 @@ ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const voi
                                    (hipStream_t)stream));
 }
 
+ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, const void* k,
+                                 const void* v, void* summaries, int32_t top_k,
+                                 int32_t refresh_last_block, int32_t* block_idx, float* out,
+                                 float* lse, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !v || !summaries || !out || top_k < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(summaries) || !aligned4(out) ||
+      (lse && !aligned4(lse)) || (block_idx && !aligned4(block_idx)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  const int keff = top_k < d.NB ? top_k : d.NB;
+  if (d.NB > kStepMaxBlocks || keff > kIdxStage) return KSA_ERR_UNSUPPORTED;
+  if ((int64_t)keff * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
+  if (refresh_last_block && d.Bs > kStepMaxBs) return KSA_ERR_UNSUPPORTED;
+  return from_hip(launch_block_topk_decode(d, q, k, v, summaries, keff, refresh_last_block, block_idx,
+                                           out, lse, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,344 +1,16 @@
-// attention.hip -- decode attention of every query head over a token list of
-// its KV head: the selected blocks (Kinetics explainer, section 五), one token
-// set shared by every head of a sequence (LessIsMore explainer, section 五),
-// or the dense range [0, T) (Kinetics explainer, section 四).
-//
-// Work decomposition.  A (sequence b, KV head g) row's token list is a
-// sequence of "virtual positions" p = 0..L-1 (block list: p -> token
-// idx[p / Bs] * Bs + p % Bs; token list: p -> idx[p]; dense: p -> p).  It is
-// cut into chunks of CH positions.  `splits` workgroups share a row; each
-// covers a contiguous run of chunks and its waves take the run's chunks
-// round-robin.
-//
-// Inside a wave, a group of LPT lanes (a "slot") holds one token row: each
-// lane owns 16 bytes (8 bf16 or 4 fp32 channels) of K and V, so one 16-byte
-// load per lane reads 64/LPT consecutive-position rows and a Bs-aligned block
-// of 16 bf16 tokens is four fully used 1 KB loads.  All G query heads of the
-// group are handled by the same lanes, so each K/V byte is read once per
-// group (the GQA sharing the LessIsMore explainer's kernel relies on).
-//
-// Numerics.  q is pre-scaled by sm_scale*log2(e); logits accumulate in fp32
-// (bf16 x bf16 products are exact), the per-slot online softmax keeps
-// (m, l, acc) in the log2 domain with hardware exp2, and P stays fp32 for the
-// P.V accumulation.  States are merged slot -> wave -> workgroup -> split in
-// a fixed order, so results are bitwise repeatable.
-//
-// Pipelining.  The workgroup's slice of the index list is staged in LDS once;
-// while a wave computes one chunk, the K/V loads of its next
-// kPrefetchChunks chunks are in flight (a ring of register buffers).
-#include <float.h>
+// attention.hip -- the decode attention kernels and their launch plans.
+// The per-row bodies (numerics, lane layout, pipelining) are in
+// ksa_attention.h; this file holds the kernels that give each workgroup one
+// (row, split) pair, the fixed-order split merge, and plan_attention.
 #include <stdio.h>
 #include <stdlib.h>
 
 #include <type_traits>
 
-#include "ksa_device.h"
-#include "ksa_internal.h"
+#include "ksa_attention.h"
 
 namespace ksa {
 namespace {
-
-constexpr int kMaxWaves = 8;
-// chunks whose K/V loads are in flight while a wave computes another
-#ifndef KSA_ATTN_PREFETCH
-#define KSA_ATTN_PREFETCH 1
-#endif
-constexpr int kPrefetchChunks = KSA_ATTN_PREFETCH;
-// K/V rows are streamed once per call: nontemporal loads keep them from
-// displacing reusable lines in L2 and the Infinity Cache.
-#ifndef KSA_NT_LOADS
-#define KSA_NT_LOADS 1
-#endif
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-struct AttnArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const int32_t* idx;
-  int count;       // idx entries per row (block list) or per sequence (token list)
-  Dims d;
-  int ltot;        // virtual positions per row
-  int bs_shift;    // log2(Bs) when Bs is a power of two, else -1
-  int splits, cps;
-  float qscale;    // sm_scale * log2(e)
-  float* out;
-  float* lse;
-  float* part_acc; // [rows, splits, G, D]
-  float* part_ml;  // [rows, splits, G, 2]
-};
-
-// Token ids of the NI rows a lane loads for chunk c.  Indices of the
-// workgroup's range are staged in LDS (s_idx, entries from e0 on).
-template <int KIND, int CH, int SPW, int NI>
-__device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_idx, int e0, int slot,
-                                              int c, int* tok, bool* ok) {
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int p = c * CH + i * SPW + slot;
-    if constexpr (KIND == 2) {
-      ok[i] = p < a.d.T;
-      tok[i] = ok[i] ? p : 0;
-    } else if constexpr (KIND == 1) {
-      ok[i] = p < a.ltot;
-      const int at = min(max(p - e0, 0), kIdxStage - 1);  // in range whenever ok
-      tok[i] = ok[i] ? s_idx[at] : 0;
-    } else {
-      ok[i] = p < a.ltot;
-      int q, r;
-      if (a.bs_shift >= 0) {
-        q = p >> a.bs_shift;
-        r = p & ((1 << a.bs_shift) - 1);
-      } else {
-        q = p / a.d.Bs;
-        r = p - q * a.d.Bs;
-      }
-      const int at = min(max(q - e0, 0), kIdxStage - 1);  // in range whenever ok
-      const int blk = ok[i] ? s_idx[at] : 0;
-      const int t = blk * a.d.Bs + r;
-      ok[i] = ok[i] && t < a.d.T;
-      tok[i] = ok[i] ? t : 0;
-    }
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ uint4 ld_kv(const T* p) {
-#if KSA_NT_LOADS
-  return ld16_stream(p);
-#else
-  return ld16(p);
-#endif
-}
-
-template <typename T, int D, int KIND, int CH, int SPW, int NI>
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, const int* s_idx, int e0, int slot,
-                                           int c, const T* kbase, const T* vbase, uint4* kr,
-                                           uint4* vr, bool* okr) {
-  int tok[NI];
-  resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, e0, slot, c, tok, okr);
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    kr[i] = ld_kv(kbase + (int64_t)tok[i] * D);
-    vr[i] = ld_kv(vbase + (int64_t)tok[i] * D);
-  }
-}
-
-template <typename T, int D, int G, int NI, int LPT>
-__device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], const uint4* kc,
-                                              const uint4* vc, const bool* okc, float* m, float* l,
-                                              float (&acc)[G][KV<T>::EPL]) {
-  constexpr int EPL = KV<T>::EPL;
-  // logits of the NI tokens for every head of the group
-  float s[NI][G];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    float f[EPL];
-    KV<T>::widen(kc[i], f);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
-      s[i][h] = group_sum<LPT>(p);
-    }
-  }
-  // online softmax update, once per chunk
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = m[h];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      if (okc[i]) mx = fmaxf(mx, s[i][h]);
-    const float alpha = fast_exp2(m[h] - mx);
-    float ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const float p = okc[i] ? fast_exp2(s[i][h] - mx) : 0.f;
-      s[i][h] = p;
-      ps += p;
-    }
-    l[h] = fmaf(l[h], alpha, ps);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
-    m[h] = mx;
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    float f[EPL];
-    KV<T>::widen(vc[i], f);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[i][h], f[e], acc[h][e]);
-  }
-}
-
-// Merges the per-wave softmax states of a workgroup (staged in LDS) and
-// writes the row's output, or this split's partial state when the row is
-// split over several workgroups.  Fixed order: bitwise repeatable.
-template <int D, int G>
-__device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, int g, int split,
-                                            int nw, const float (*s_m)[G], const float (*s_l)[G],
-                                            const float (*s_acc)[G][D]) {
-  const Dims& d = a.d;
-  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
-    const int h = o / D, e = o - (o / D) * D;
-    float M = -FLT_MAX;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, A = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float sc = fast_exp2(s_m[w][h] - M);
-      L = fmaf(s_l[w][h], sc, L);
-      A = fmaf(s_acc[w][h][e], sc, A);
-    }
-    if (a.splits == 1) {
-      const int64_t oh = (int64_t)b * d.Hq + g * G + h;
-      a.out[oh * D + e] = A / L;
-      if (e == 0 && a.lse) a.lse[oh] = (M + log2f(L)) * kLn2;
-    } else {
-      const int64_t pi = ((int64_t)row * a.splits + split) * G + h;
-      a.part_acc[pi * D + e] = A;
-      if (e == 0) {
-        a.part_ml[pi * 2] = M;
-        a.part_ml[pi * 2 + 1] = L;
-      }
-    }
-  }
-}
-
-// Stages the index slice a workgroup (row, split) needs in LDS; returns the
-// first staged entry.  No barrier: the caller syncs before reading s_idx.
-template <int KIND, int CH>
-__device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int split, int* s_idx) {
-  if constexpr (KIND == 2) return 0;
-  const Dims& d = a.d;
-  const int nchunks = (a.ltot + CH - 1) / CH;
-  const int c_begin = split * a.cps;
-  const int c_end = min(c_begin + a.cps, nchunks);
-  int e0, e1;
-  const int32_t* src;
-  if constexpr (KIND == 0) {
-    e0 = (c_begin * CH) / d.Bs;
-    e1 = min(a.count, (c_end * CH + d.Bs - 1) / d.Bs);
-    src = a.idx + (int64_t)row * a.count;
-  } else {
-    const int b = row / d.Hkv;
-    e0 = c_begin * CH;
-    e1 = min(a.ltot, c_end * CH);
-    src = a.idx + (int64_t)b * a.count;
-  }
-  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
-  return e0;
-}
-
-// Attention of one row (or one split of it) on VALU; the row's index slice is
-// staged in s_idx (entries from e0 on).  `sync` waits for the staging.
-template <typename T, int D, int G, int KIND>
-__device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int split, const int* s_idx,
-                                              int e0, bool sync) {
-  constexpr int EPL = KV<T>::EPL;
-  constexpr int LPT = D / EPL;
-  constexpr int SPW = 64 / LPT;
-  constexpr int NI = kLoadsPerChunk;
-  constexpr int CH = SPW * NI;
-  constexpr int P = kPrefetchChunks;
-  __shared__ float s_m[kMaxWaves][G];
-  __shared__ float s_l[kMaxWaves][G];
-  __shared__ float s_acc[kMaxWaves][G][D];
-
-  const Dims& d = a.d;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int slot = lane / LPT, li = lane % LPT;
-  const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const int64_t kvrow = (int64_t)row * d.Tcap * D + li * EPL;
-  const T* kbase = (const T*)a.k + kvrow;
-  const T* vbase = (const T*)a.v + kvrow;
-
-  const int nchunks = (a.ltot + CH - 1) / CH;
-  const int c_begin = split * a.cps;
-  const int c_end = min(c_begin + a.cps, nchunks);
-
-  float qv[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    KV<T>::widen(ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL), qv[h]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
-  }
-
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -FLT_MAX;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-  if (sync) __syncthreads();
-
-  const int c0 = c_begin + wave;
-  const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
-  uint4 kb[P][NI], vb[P][NI];
-  bool okb[P][NI];
-#pragma unroll
-  for (int s = 0; s < P; ++s)
-    if (s < my_n)
-      load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, e0, slot, c0 + s * nw, kbase, vbase, kb[s],
-                                          vb[s], okb[s]);
-  for (int j0 = 0; j0 < my_n; j0 += P) {
-#pragma unroll
-    for (int s = 0; s < P; ++s) {
-      const int j = j0 + s;
-      if (j < my_n) {
-        uint4 kc[NI], vc[NI];
-        bool okc[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          kc[i] = kb[s][i];
-          vc[i] = vb[s][i];
-          okc[i] = okb[s][i];
-        }
-        if (j + P < my_n)
-          load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, e0, slot, c0 + (j + P) * nw, kbase, vbase,
-                                              kb[s], vb[s], okb[s]);
-        compute_chunk<T, D, G, NI, LPT>(qv, kc, vc, okc, m, l, acc);
-      }
-    }
-  }
-
-  // merge the wave's slots (lanes li, li+LPT, ... hold the same channels)
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float M = fmaxf(m[h], mo);
-      const float sa = fast_exp2(m[h] - M), sb = fast_exp2(mo - M);
-      l[h] = l[h] * sa + lo * sb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * sa + __shfl_xor(acc[h][e], off) * sb;
-      m[h] = M;
-    }
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (li == 0) {
-        s_m[wave][h] = m[h];
-        s_l[wave][h] = l[h];
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h][li * EPL + e] = acc[h][e];
-    }
-  }
-  __syncthreads();
-
-  merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
-}
 
 // For G <= 2 the register budget is held at 128 per lane, so that two
 // 512-thread workgroups (16 waves) fit on a CU.
@@ -350,180 +22,6 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_partial
   const int row = blockIdx.x / a.splits;
   const int e0 = stage_indices<KIND, CH>(a, row, split, s_idx);
   attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, e0, KIND != 2);
-}
-
-// ---------------------------------------------------------------------------
-// MFMA variant for bf16, D = 128 and G in {4, 8}.  Per chunk of 16 tokens:
-//  * QK^T on v_mfma_f32_16x16x32_bf16: A = 16 token rows x 32 dims of K (lane
-//    l holds token l%16, dims 8*(l/16).. of the slice, loaded straight from
-//    HBM into that layout), B = the same 32 dims of the group's G query heads
-//    (zero columns past G), four MFMAs cover D = 128.  The bf16 products are
-//    exact and accumulate in fp32; the fp32 logits are scaled afterwards.
-//    (Loading K coalesced and transposing it through LDS was measured slower
-//    here: the extra LDS round trip per chunk costs more than it saves at the
-//    8-12 waves per CU these kernels run with.)
-//  * Softmax in the MFMA output layout (lane l: head l%16, tokens 4*(l/16)..):
-//    one running max and sum per head for the whole wave, cross-lane steps by
-//    xor-16/32 shuffles.
-//  * The weights P (fp32) and the rescale factors go through a wave-private
-//    LDS tile to the V layout (16 lanes per token row, as in the VALU kernel),
-//    where P.V accumulates on VALU in fp32.
-// Softmax state is per wave rather than per slot, so the slots of a wave are
-// merged by plain sums.
-// Attention of one row (or one split of it) with MFMA QK^T (bf16, D = 128,
-// G in {4, 8}); indices staged as for attn_row_valu.
-template <int G, int KIND>
-__device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int split, const int* s_idx,
-                                              int e0, bool sync) {
-  constexpr int D = 128;
-  constexpr int EPL = 8;
-  constexpr int LPT = 16;
-  constexpr int SPW = 4;
-  constexpr int NI = 4;
-  constexpr int CH = 16;
-  static_assert(CH == SPW * NI, "chunk of the VALU kernel");
-  __shared__ float s_m[kMaxWaves][G];
-  __shared__ float s_l[kMaxWaves][G];
-  __shared__ float s_acc[kMaxWaves][G][D];
-  __shared__ float s_p[kMaxWaves][CH + 1][8];  // rows 0..15: P[token][head]; row 16: rescale
-
-  const Dims& d = a.d;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  const int r = lane & 15, kg = lane >> 4;  // MFMA: row/column and k-group / row quad
-  const int slot = kg, li = r;             // V layout: token slot and 16-byte piece
-  const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const int64_t kvrow = (int64_t)row * d.Tcap * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + kvrow + 8 * kg;
-  const uint16_t* vbase = (const uint16_t*)a.v + kvrow + li * EPL;
-
-  const int nchunks = (a.ltot + CH - 1) / CH;
-  const int c_begin = split * a.cps;
-  const int c_end = min(c_begin + a.cps, nchunks);
-
-  // B operand: the group's queries, column n = head r (zero past G)
-  bf16x8_t qop[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (r < G) u = ld16((const uint16_t*)a.q + ((int64_t)b * d.Hq + g * G + r) * D + 32 * i + 8 * kg);
-    qop[i] = as_bf16x8(u);
-  }
-  float m = -FLT_MAX, lsum = 0.f;  // softmax state of head r (MFMA layout)
-  float acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  if (sync) __syncthreads();
-
-  const int c0 = c_begin + wave;
-  const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
-  float(*pt)[8] = s_p[wave];
-
-  // loads of one chunk: K in the MFMA A layout, V in the row layout
-  auto load = [&](int c, uint4* kr, uint4* vr, bool& okk) {
-    int tk[1];
-    bool ok1[1];
-    resolve_chunk<KIND, CH, 1, 1>(a, s_idx, e0, r, c, tk, ok1);  // position c*16 + r
-    okk = ok1[0];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = ld_kv(kbase + (int64_t)tk[0] * D + 32 * i);
-    int tv[NI];
-    bool okv[NI];
-    resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, e0, slot, c, tv, okv);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = ld_kv(vbase + (int64_t)tv[i] * D);
-  };
-
-  uint4 kb[NI], vb[NI];
-  bool okb = false;
-  if (my_n > 0) load(c0, kb, vb, okb);
-  for (int j = 0; j < my_n; ++j) {
-    uint4 kc[NI], vc[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kc[i] = kb[i];
-      vc[i] = vb[i];
-    }
-    const bool okc = okb;
-    if (j + 1 < my_n) load(c0 + (j + 1) * nw, kb, vb, okb);
-
-    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NI; ++i) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[i]), qop[i], S, 0, 0, 0);
-    const uint64_t vm = __ballot(okc);  // bit t (t < 16): chunk token t is attended
-    float sv[4];
-    bool val[4];
-    float mloc = -FLT_MAX;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      sv[jj] = S[jj] * a.qscale;
-      val[jj] = (vm >> (4 * kg + jj)) & 1ull;
-      if (val[jj]) mloc = fmaxf(mloc, sv[jj]);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float mnew = fmaxf(m, mloc);
-    const float alpha = fast_exp2(m - mnew);
-    float ps = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      sv[jj] = val[jj] ? fast_exp2(sv[jj] - mnew) : 0.f;
-      ps += sv[jj];
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    lsum = fmaf(lsum, alpha, ps);
-    m = mnew;
-    if (r < G) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) pt[4 * kg + jj][r] = sv[jj];
-      if (kg == 0) pt[CH][r] = alpha;
-    }
-    wave_lds_fence();
-    float al[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) al[h] = pt[CH][h];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float pv[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pv[h] = pt[4 * i + slot][h];
-      float f[EPL];
-      KV<uint16_t>::widen(vc[i], f);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], f[e], acc[h][e]);
-    }
-    wave_lds_fence();
-  }
-
-  // slots share the wave's softmax state: their accumulators simply add up
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      acc[h][e] += __shfl_xor(acc[h][e], 16);
-      acc[h][e] += __shfl_xor(acc[h][e], 32);
-    }
-  if (lane < G) {
-    s_m[wave][lane] = m;
-    s_l[wave][lane] = lsum;
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h][li * EPL + e] = acc[h][e];
-  }
-  __syncthreads();
-  merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
 }
 
 template <int G, int KIND>
@@ -646,28 +144,7 @@ size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p) {
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse, void* workspace,
                             const AttnPlan& plan, hipStream_t stream) {
-  AttnArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.idx = idx;
-  a.count = count;
-  a.d = d;
-  a.ltot = kind == 0 ? count * d.Bs : (kind == 1 ? count : d.T);
-  a.bs_shift = -1;
-  if (kind == 0 && (d.Bs & (d.Bs - 1)) == 0) {
-    int sh = 0;
-    while ((1 << sh) < d.Bs) ++sh;
-    a.bs_shift = sh;
-  }
-  a.splits = plan.splits;
-  a.cps = plan.cps;
-  a.qscale = d.scale * kLog2e;
-  a.out = out;
-  a.lse = lse;
-  const size_t rows = (size_t)d.B * d.Hkv;
-  a.part_acc = (float*)workspace;
-  a.part_ml = workspace ? a.part_acc + rows * plan.splits * d.G * d.D : nullptr;
+  const AttnArgs a = make_attn_args(d, kind, q, k, v, idx, count, out, lse, workspace, plan);
   if (d.dtype == KSA_BF16) {
     if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);
     return launch_g<uint16_t, 128>(a, kind, plan, stream);

@@ -1,6 +1,7 @@
 // ksa_device.h -- device-side helpers for the gfx950 kernels of libksa:
 // 16-byte KV loads and widening, 64-wide wavefront reductions through DPP,
-// order-preserving 32-bit keys for fp32 scores, and wave/block scans.
+// exactly rounded block means, order-preserving 32-bit keys for fp32 scores,
+// and wave/block scans.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -104,6 +105,56 @@ __device__ __forceinline__ int ktile_slot(int t, int c) { return t * 16 + (c ^ t
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------- block means
+// fp64 -> bf16 bit pattern, round to nearest, ties to even.  Normal range:
+// drop 45 of the 52 fraction bits with an RNE bias on the integer pattern
+// (a carry into the exponent is the correct result).  Below 2^-126 the bf16
+// grid is uniform with spacing 2^-133: scale (exactly) and round there.
+__device__ __forceinline__ uint16_t bf16_rne_from_f64(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long sign = u & 0x8000000000000000ull;
+  unsigned long long a = u ^ sign;
+  uint32_t bits;
+  if (a < 0x3810000000000000ull) {  // |x| < 2^-126 (also 0)
+    double r = rint(__longlong_as_double((long long)a) * 0x1p133);
+    bits = (uint32_t)r;  // 0..128; 128 is the smallest normal
+  } else {
+    const unsigned long long lsb = (a >> 45) & 1ull;
+    a += 0xFFFFFFFFFFFull + lsb;  // 2^44 - 1 + lsb
+    a >>= 45;                     // (exp64 << 7) | fraction7
+    const unsigned long long e = (a >> 7) - 896;  // rebias 1023 -> 127
+    bits = e >= 255 ? 0x7F80u : (uint32_t)((e << 7) | (a & 0x7Full));
+  }
+  return (uint16_t)((sign >> 48) | bits);
+}
+
+// The 16 bytes of a block mean one lane stores: acc holds the lane's fp64
+// channel sums (token order), n the block's token count; each channel is
+// divided once in fp64 (IEEE) and rounded once, to nearest-even, to the KV
+// dtype.
+template <typename T>
+__device__ __forceinline__ uint4 mean_bits(const double* acc, int n);
+
+template <>
+__device__ __forceinline__ uint4 mean_bits<uint16_t>(const double* acc, int n) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = bf16_rne_from_f64(acc[2 * i] / (double)n);
+    uint32_t hi = bf16_rne_from_f64(acc[2 * i + 1] / (double)n);
+    w[i] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <>
+__device__ __forceinline__ uint4 mean_bits<float>(const double* acc, int n) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = __float_as_uint((float)(acc[i] / (double)n));
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ---------------------------------------------------------------- keys

@@ -56,11 +56,18 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
 hipError_t launch_block_summaries(const Dims& d, const void* k, void* summaries, int first_block,
                                   int num_blocks, hipStream_t stream);
 
-constexpr int kSelectMaxBlocks = 15360;  // keys live in LDS (60 KB)
+constexpr int kSelectMaxBlocks = 15360;  // a row's keys fit the registers of one top-k workgroup
 size_t select_workspace_bytes(const Dims& d);
 hipError_t launch_select_topk(const Dims& d, const void* q, const void* summaries, int keff,
                               int32_t* block_idx, float* block_scores, void* workspace,
                               hipStream_t stream);
+
+// Whole decode step in one launch (refresh + select + attend per row).
+constexpr int kStepMaxBlocks = 4096;  // blocks per row whose keys the step keeps in LDS
+constexpr int kStepMaxBs = 64;        // largest block size the step refreshes
+hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k, const void* v,
+                                    void* summaries, int keff, int refresh, int32_t* block_idx,
+                                    float* out, float* lse, hipStream_t stream);
 
 // Vote-union selection.
 struct VotePlan {

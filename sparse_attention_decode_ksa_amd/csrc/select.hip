@@ -12,15 +12,16 @@
 //     DPP; each score is stored as an order-preserving uint32 key in the
 //     workspace [rows, NB].
 //  2. topk_rows_kernel.  One workgroup per row with the row's keys in
-//     registers: a bucket search over the row's key range (LDS histograms of
-//     at most 256 buckets, one wave scanning them) finds the k-th largest key
-//     `thr` and how many keys equal to it are taken; a per-thread count and
-//     one workgroup scan place every selected id in ascending order, the
-//     lowest ids winning among keys equal to thr.
+//     registers runs the bucket search of ksa_topk.h: LDS histograms of at
+//     most 256 buckets over the row's key range find the k-th largest key
+//     and how many keys equal to it are taken; a per-thread count and one
+//     workgroup scan place every selected id in ascending order, the lowest
+//     ids winning among equal keys.
 // Integer work after phase 1 is exact, so the selection is a fixed function
 // of the fp32 scores.
 #include "ksa_device.h"
 #include "ksa_internal.h"
+#include "ksa_topk.h"
 
 namespace ksa {
 namespace {
@@ -83,138 +84,20 @@ __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
   }
 }
 
-// Top-k of one row per workgroup of kTopkThreads threads.  Thread t holds
-// keys [t*KPT, (t+1)*KPT) in registers, so a per-thread count and one
-// workgroup scan give every selected id its place in ascending order.
-//
-// Bucket search on the row's key range: with all candidates in [lo, hi], a
-// key's bucket is (key - lo) >> shift, shift chosen so that the range maps
-// onto at most 256 buckets (a monotone map, so buckets are ordered like the
-// keys).  One LDS histogram and one wave scan find the bucket holding the
-// `remaining`-th largest candidate; the range shrinks to that bucket.  It
-// stops when that bucket holds exactly the keys still needed (all of them
-// are taken) or when it is a single key value (the lowest ids among equal
-// keys are taken).  Buckets follow the data's own range rather than fixed
-// bit fields, so fp32 scores spread over the histogram instead of piling
-// onto the few bins a fixed top byte gives them.
+// Top-k of one row per workgroup of kTopkThreads threads, keys in registers
+// (thread t holds positions [t*KPT, (t+1)*KPT)).
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
     const uint32_t* __restrict__ gkeys, int NB, int keff, int32_t* __restrict__ block_idx) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t red[2][kTopkThreads / 64];
-  __shared__ uint32_t sh_bucket[3];
-  __shared__ uint64_t scan_scratch[17];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ TopkShared sh;
   const int row = blockIdx.x;
   const uint32_t* rk = gkeys + (int64_t)row * NB;
-  const int j0 = tid * KPT;
+  const int j0 = threadIdx.x * KPT;
   uint32_t key[KPT];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const bool in = j0 + i < NB;
-    key[i] = in ? rk[j0 + i] : 0u;
-    if (in) {
-      kmin = min(kmin, key[i]);
-      kmax = max(kmax, key[i]);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
-  if (lane == 0) {
-    red[0][wave] = kmin;
-    red[1][wave] = kmax;
-  }
-  __syncthreads();
-  uint32_t lo = red[0][0], hi = red[1][0];
-#pragma unroll
-  for (int w = 1; w < kTopkThreads / 64; ++w) {
-    lo = min(lo, red[0][w]);
-    hi = max(hi, red[1][w]);
-  }
-
-  uint32_t remaining = (uint32_t)keff;
-  uint32_t quota, thr;
-#pragma unroll 1
-  for (;;) {
-    const uint32_t span = hi - lo;
-    if (span == 0) {  // one value left: ties, lowest ids first
-      thr = lo;
-      quota = remaining;
-      break;
-    }
-    const int bits = 32 - __clz(span);
-    const int shift = bits > 8 ? bits - 8 : 0;
-    hist[tid] = 0;  // kTopkThreads == 256 bins
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (j0 + i < NB && key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> shift], 1u);
-    __syncthreads();
-    if (wave == 0) {
-      // lane l holds buckets 255-4l .. 252-4l (highest in lane 0)
-      const int top = 255 - 4 * lane;
-      const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
-      const uint32_t s = c0 + c1 + c2 + c3;
-      const uint32_t incl = wave_incl_scan(s);
-      const uint32_t excl = incl - s;
-      if (excl < remaining && remaining <= incl) {
-        uint32_t c = excl, n;
-        int bk;
-        if (c + c0 >= remaining) {
-          bk = top; n = c0;
-        } else if ((c += c0) + c1 >= remaining) {
-          bk = top - 1; n = c1;
-        } else if ((c += c1) + c2 >= remaining) {
-          bk = top - 2; n = c2;
-        } else {
-          c += c2;
-          bk = top - 3; n = c3;
-        }
-        sh_bucket[0] = (uint32_t)bk;
-        sh_bucket[1] = c;
-        sh_bucket[2] = n;
-      }
-    }
-    __syncthreads();
-    const uint32_t bk = sh_bucket[0], above = sh_bucket[1], n = sh_bucket[2];
-    remaining -= above;
-    const uint64_t blo = (uint64_t)lo + ((uint64_t)bk << shift);
-    const uint64_t bhi = (uint64_t)lo + (((uint64_t)bk + 1) << shift) - 1;
-    lo = (uint32_t)blo;
-    hi = bhi < (uint64_t)hi ? (uint32_t)bhi : hi;
-    if (n == remaining) {  // the whole bucket is taken: everything >= lo
-      thr = lo;
-      quota = 0xFFFFFFFFu;
-      break;
-    }
-  }
-
-  // ascending compaction: keys > thr, then keys == thr up to the quota
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    n_gt += (j0 + i < NB) && key[i] > thr;
-    n_eq += (j0 + i < NB) && key[i] == thr;
-  }
-  uint64_t total;
-  const uint64_t before = block_excl_scan64(((uint64_t)n_gt << 32) | n_eq, scan_scratch, &total);
-  uint32_t gt_before = (uint32_t)(before >> 32), eq_before = (uint32_t)before;
+  for (int i = 0; i < KPT; ++i) key[i] = j0 + i < NB ? rk[j0 + i] : 0u;
   int32_t* out = block_idx + (int64_t)row * keff;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if (j0 + i >= NB) break;
-    if (key[i] > thr) {
-      out[gt_before + min(eq_before, quota)] = j0 + i;
-      ++gt_before;
-    } else if (key[i] == thr) {
-      if (eq_before < quota) out[gt_before + eq_before] = j0 + i;
-      ++eq_before;
-    }
-  }
+  row_topk<KPT>(key, KPT, j0, NB, keff, sh, [&](int rank, int j) { out[rank] = j; });
 }
 
 template <typename T, int D>

@@ -13,51 +13,6 @@
 namespace ksa {
 namespace {
 
-// fp64 -> bf16 bit pattern, round to nearest, ties to even.  Normal range:
-// drop 45 of the 52 fraction bits with an RNE bias on the integer pattern
-// (a carry into the exponent is the correct result).  Below 2^-126 the bf16
-// grid is uniform with spacing 2^-133: scale (exactly) and round there.
-__device__ __forceinline__ uint16_t bf16_rne_from_f64(double x) {
-  unsigned long long u = (unsigned long long)__double_as_longlong(x);
-  const unsigned long long sign = u & 0x8000000000000000ull;
-  unsigned long long a = u ^ sign;
-  uint32_t bits;
-  if (a < 0x3810000000000000ull) {  // |x| < 2^-126 (also 0)
-    double r = rint(__longlong_as_double((long long)a) * 0x1p133);
-    bits = (uint32_t)r;  // 0..128; 128 is the smallest normal
-  } else {
-    const unsigned long long lsb = (a >> 45) & 1ull;
-    a += 0xFFFFFFFFFFFull + lsb;  // 2^44 - 1 + lsb
-    a >>= 45;                     // (exp64 << 7) | fraction7
-    const unsigned long long e = (a >> 7) - 896;  // rebias 1023 -> 127
-    bits = e >= 255 ? 0x7F80u : (uint32_t)((e << 7) | (a & 0x7Full));
-  }
-  return (uint16_t)((sign >> 48) | bits);
-}
-
-template <typename T>
-__device__ __forceinline__ void store_mean(T* dst, const double* acc, int n);
-
-template <>
-__device__ __forceinline__ void store_mean<uint16_t>(uint16_t* dst, const double* acc, int n) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t lo = bf16_rne_from_f64(acc[2 * i] / (double)n);
-    uint32_t hi = bf16_rne_from_f64(acc[2 * i + 1] / (double)n);
-    w[i] = lo | (hi << 16);
-  }
-  st16(dst, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
-template <>
-__device__ __forceinline__ void store_mean<float>(float* dst, const double* acc, int n) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = __float_as_uint((float)(acc[i] / (double)n));
-  st16(dst, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
 constexpr int kBatch = 16;
 
 template <typename T, int D>
@@ -96,7 +51,7 @@ __global__ __launch_bounds__(256) void block_summaries_kernel(const T* __restric
       }
     }
   }
-  store_mean<T>(summ + (bg * d.NBcap + j) * D + li * EPL, acc, n);
+  st16(summ + (bg * d.NBcap + j) * D + li * EPL, mean_bits<T>(acc, n));
 }
 
 template <typename T, int D>

@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_five_operations():
     names = declared_functions()
     for n in ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode", "ksa_vote_select",
-              "ksa_dense_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version"):
+              "ksa_dense_decode", "ksa_block_topk_decode", "ksa_workspace_bytes",
+              "ksa_status_string", "ksa_version"):
         assert n in names
     assert set(names) == set(ksa.EXPORTED)
 
@@ -115,6 +116,33 @@ def test_invalid_arguments_are_rejected_before_launch():
     need = ksa.ksa_workspace_bytes(p4, ksa.KSA_OP_VOTE_SELECT, 10)
     assert lib.ksa_vote_select(ctypes.byref(p4), FAKE, FAKE, 10, 2, FAKE, null, FAKE, need - 1,
                                null) == W
+
+
+def test_fused_step_validation():
+    lib = ksa.load_library()
+    null = None
+    E = ksa.KSA_ERR_INVALID_ARGUMENT
+    U = ksa.KSA_ERR_UNSUPPORTED
+
+    def call(p, top_k=4, refresh=1, q=FAKE, summ=FAKE, out=FAKE, idx=null, lse=null):
+        return lib.ksa_block_topk_decode(ctypes.byref(p) if p is not None else None, q, FAKE, FAKE,
+                                         summ, top_k, refresh, idx, out, lse, null)
+
+    p = P()
+    assert call(None) == E
+    assert call(p, top_k=0) == E
+    assert call(p, q=null) == E
+    assert call(p, summ=null) == E
+    assert call(p, out=null) == E
+    assert call(p, summ=ctypes.c_void_p(0x10008)) == E   # summaries must be 16-byte aligned
+    assert call(p, idx=ctypes.c_void_p(0x10002)) == E    # block_idx must be 4-byte aligned
+    assert call(P(Bs=0)) == E
+    assert call(P(D=96)) == U
+    # more blocks than the step keeps in LDS (4096), or more selected ids than it stages (2048)
+    assert call(P(T=4097 * 16, Tcap=4097 * 16)) == U
+    assert call(P(T=4096 * 2, Tcap=4096 * 2, Bs=2), top_k=2049) == U
+    # the newest block is refreshed only for Bs <= 64; without refresh any Bs is fine
+    assert call(P(Bs=65), refresh=1) == U
 
 
 def test_binding_rejects_cpu_tensors():
