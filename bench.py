@@ -343,9 +343,13 @@ def main():
             for l, x in enumerate(L):
                 other_step(l)
             torch.cuda.synchronize()
+            # (block ids bitwise; outputs bitwise unless the separate attention is
+            # planned with another split, which reorders its fp32 merge)
             for l, x in enumerate(L):
-                assert torch.equal(x["idx2"], x["idx"]) and torch.equal(x["out2"], x["out"]) \
-                    and torch.equal(x["lse2"], x["lse"]), "fused step and separate calls differ"
+                assert torch.equal(x["idx2"], x["idx"]), "fused step and separate calls select differently"
+                assert float((x["out2"] - x["out"]).abs().max()) <= 1e-5 \
+                    and float((x["lse2"] - x["lse"]).abs().max()) <= 1e-5, \
+                    "fused step and separate calls differ"
             g_other = capture(lambda: [other_step(l) for l in range(layers)])
         g_step = [capture(lambda l=l: step(l)) for l in range(layers)]
         g_cycle = capture(lambda: [step(l) for l in range(layers)])

@@ -190,10 +190,11 @@ ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const voi
  *   3. out [B, Hq, D] fp32 and lse [B, Hq] fp32 (nullable) are the attention
  *      of ksa_sparse_decode over those blocks.
  * summaries and block_idx are bitwise those of the three separate calls; out
- * and lse are too whenever ksa_sparse_decode would run one split of 8 waves
- * per row for this shape, and otherwise differ only in the fp32 order of the
- * final merge.  All rows run in one grid of B*Hkv workgroups, so the call is
- * meant for batches with at least a few hundred (sequence, KV head) rows.
+ * and lse differ from ksa_sparse_decode's only in the fp32 order of the final
+ * merge (and not at all when both run one workgroup of 8 waves per row, e.g.
+ * B*Hkv = 512, Hq/Hkv = 2 on MI355X).  Results are bitwise repeatable.  One
+ * workgroup serves each (sequence, KV head) row, so the call is meant for
+ * batches with at least a few hundred such rows.
  * Limits (else KSA_ERR_UNSUPPORTED): NB <= 4096, k_eff <= 2048,
  * k_eff * Bs < 2^30, and Bs <= 64 when refresh_last_block is set.
  * Needs no workspace. */

@@ -3,16 +3,19 @@
 // mean key, every block's mean key is scored against the query, the K' most
 // relevant blocks are kept and attention runs over their tokens only).
 //
-// One workgroup of 512 threads owns one (sequence, KV head) row and runs the
-// four steps back to back:
-//  1. refresh (optional): the token rows of block (T-1)/Bs are loaded, one
-//     per LPT-lane group, parked in LDS, and summed by one group in fp64 in
-//     token order; the rounded mean is written to the summaries and scored
-//     from registers;
-//  2. scoring: the row's summaries stream through double-buffered batches of
-//     16-byte loads; each block's relevance (sum_h q_h) . S_j (fp32) becomes
-//     an order-preserving key in LDS;
-//  3. top-k: the bucket search of ksa_topk.h on the LDS keys writes the
+// One workgroup of 8 waves (4 when the rows outnumber the 8-wave workgroups
+// the chip holds at once) owns one (sequence, KV head) row and runs the four
+// steps back to back:
+//  1. scoring: the row's summaries stream through double-buffered runs of
+//     16-byte loads that the waves take from a shared counter; each block's
+//     relevance (sum_h q_h) . S_j (fp32) becomes an order-preserving key in
+//     LDS, and the keys' range is gathered with LDS atomics;
+//  2. refresh (optional): the token rows of block (T-1)/Bs, loaded at the
+//     start (one per LPT-lane group) and held in registers during scoring,
+//     go through LDS to one group that sums them in fp64 in token order; the
+//     rounded mean is written to the summaries and scored from registers;
+//  3. top-k: the bucket search of ksa_topk.h on the LDS keys (over the
+//     gathered range, so no separate min/max pass) writes the
 //     selected block ids, ascending, into the attention's LDS index stage
 //     (and to block_idx when asked);
 //  4. attention: the per-row body of ksa_attention.h (VALU, or MFMA for bf16
@@ -20,9 +23,9 @@
 // The keys never leave the chip and three kernel boundaries disappear.  Each
 // step repeats the arithmetic of the separate calls (block_summaries_kernel,
 // block_score_kernel, topk_rows_kernel, the attention bodies), so summaries
-// and selections are bitwise those of ksa_block_summaries + ksa_select_topk,
-// and the attention equals ksa_sparse_decode's whenever that call plans one
-// split of 8 waves per row.
+// and selections are bitwise those of ksa_block_summaries + ksa_select_topk;
+// the attention equals ksa_sparse_decode's up to the fp32 order of the wave
+// merge (bitwise when both run one 8-wave workgroup per row).
 #include <type_traits>
 
 #include "ksa_attention.h"
@@ -31,8 +34,11 @@
 namespace ksa {
 namespace {
 
-constexpr int kStepThreads = kMaxWaves * 64;
-constexpr int kStepKPT = kStepMaxBlocks / kStepThreads;  // keys per thread in the top-k
+// Waves per SIMD the register budget is held to for groups of at most two
+// heads (4 -> 128 VGPRs: sixteen waves per CU).  A tuning knob.
+#ifndef KSA_STEP_OCC
+#define KSA_STEP_OCC 4
+#endif
 #ifndef KSA_STEP_UNROLL
 #define KSA_STEP_UNROLL 8
 #endif
@@ -55,9 +61,12 @@ constexpr int ref_stage_slots() {
   return ref > idx ? ref : idx;
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kStepThreads, (G <= 2 ? 4 : 1)) void block_topk_decode_kernel(
+// NW waves per workgroup (4 or 8).
+template <typename T, int D, int G, int NW>
+__global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_topk_decode_kernel(
     StepArgs s) {
+  constexpr int kStepThreads = NW * 64;
+  constexpr int kStepKPT = (kStepMaxBlocks + kStepThreads - 1) / kStepThreads;  // keys per thread
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int NGRP = kStepThreads / LPT;
@@ -67,8 +76,10 @@ __global__ __launch_bounds__(kStepThreads, (G <= 2 ? 4 : 1)) void block_topk_dec
   __shared__ uint32_t s_keys[kStepMaxBlocks];
   __shared__ uint4 s_buf[ref_stage_slots<T, D>()];
   __shared__ TopkShared s_topk;
-  uint4* s_ref = s_buf;                              // steps 1
-  int* s_idx = reinterpret_cast<int*>(s_buf);        // steps 3-4
+  __shared__ int s_next;           // next free scoring unit
+  __shared__ uint32_t s_lo, s_hi;  // range of the row's keys
+  uint4* s_ref = s_buf;                        // step 2
+  int* s_idx = reinterpret_cast<int*>(s_buf);  // steps 3-4
 
   const AttnArgs& a = s.a;
   const Dims& d = a.d;
@@ -80,51 +91,102 @@ __global__ __launch_bounds__(kStepThreads, (G <= 2 ? 4 : 1)) void block_topk_dec
   const int jref = s.refresh ? (d.T - 1) / d.Bs : -1;
   const int nref = s.refresh ? d.T - jref * d.Bs : 0;
 
-  // 1a. refresh rows first, so their loads return ahead of the summaries
+  // The refresh block's rows are loaded up front (branch-free: without a
+  // refresh the row's first token stands in, unused) and consumed only
+  // after the scoring loop, so no wave waits on them before scoring.
   uint4 rr[RP];
-  if (s.refresh) {
-    const T* kp = (const T*)a.k + ((int64_t)row * d.Tcap + (int64_t)jref * d.Bs) * D + li * EPL;
+  {
+    const int t0 = s.refresh ? jref * d.Bs : 0;
+    const int last = s.refresh ? nref - 1 : 0;
+    const T* kp = (const T*)a.k + ((int64_t)row * d.Tcap + t0) * D + li * EPL;
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int t = grp + r * NGRP;
-      if (t < nref) rr[r] = ld16(kp + (int64_t)t * D);
-    }
+    for (int r = 0; r < RP; ++r) rr[r] = ld16(kp + (int64_t)min(grp + r * NGRP, last) * D);
   }
 
-  // group query: sum of the G heads, fp32 (as block_score_kernel)
+  // the group's query rows (kept for the attention) and their fp32 sum, the
+  // group query of block_score_kernel
+  uint4 qraw[G];
   float qs[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qs[e] = 0.f;
+#pragma unroll
   for (int h = 0; h < G; ++h) {
+    qraw[h] = ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL);
     float f[EPL];
-    KV<T>::widen(ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL), f);
+    KV<T>::widen(qraw[h], f);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qs[e] += f[e];
   }
 
-  constexpr int kBatch = NGRP * U;
-  auto load_batch = [&](int base, uint4* r) {
+  // Scoring units: wave-sized runs of WU consecutive blocks (group s of a
+  // wave takes blocks u*SPW + s of the run, so each load instruction reads
+  // SPW whole summaries back to back).  A wave's first unit is its own; it
+  // then takes the next free unit from an LDS counter, so waves that are
+  // served faster by the memory system score more units and the workgroup's
+  // scoring ends close to its average wave.  Keys do not depend on which
+  // wave computed them.
+  constexpr int SPW = 64 / LPT;
+  constexpr int WU = SPW * U;
+  const int lane = tid & 63, wave = tid >> 6, slot = lane / LPT;
+  const int nw = NW;
+  const int nu = (NB + WU - 1) / WU;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // range of the keys this lane stored
+  auto load_unit = [&](int k, uint4* r) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = ld16_stream(srow + (int64_t)min(base + u * NGRP + grp, NB - 1) * D);
+    for (int u = 0; u < U; ++u)
+      r[u] = ld16_stream(srow + (int64_t)min(k * WU + u * SPW + slot, NB - 1) * D);
   };
-  auto score_batch = [&](int base, const uint4* r) {
+  auto score_unit = [&](int k, const uint4* r) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = base + u * NGRP + grp;
+      const int j = k * WU + u * SPW + slot;
       float f[EPL];
       KV<T>::widen(r[u], f);
       float p = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) p = fmaf(qs[e], f[e], p);
       p = group_sum<LPT>(p);
-      if (li == 0 && j < NB && j != jref) s_keys[j] = order_key(p);
+      if (li == 0 && j < NB && j != jref) {
+        const uint32_t kk = order_key(p);
+        s_keys[j] = kk;
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+      }
     }
   };
+  auto grab = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
 
+  // 1. scoring, two units in flight per wave (the refresh block is scored
+  // below).  Loads are unconditional (past the last unit they re-read the
+  // last block), so each unit waits only for its own loads.
   uint4 bufA[U], bufB[U];
-  load_batch(0, bufA);
+  int ua = wave;
+  load_unit(ua, bufA);
+  if (tid == 0) {
+    s_next = nw;
+    s_lo = 0xFFFFFFFFu;
+    s_hi = 0u;
+  }
+  topk_clear(s_topk);
+  __syncthreads();
+  for (;;) {
+    const int ub = grab();
+    load_unit(ub, bufB);
+    if (ua >= nu) break;
+    score_unit(ua, bufA);
+    ua = grab();
+    load_unit(ua, bufA);
+    if (ub >= nu) break;
+    score_unit(ub, bufB);
+  }
 
-  // 1b. refresh: in-order fp64 sum by group 0 (as block_summaries_kernel)
+  // 2. refresh: the block's rows go through LDS to group 0, which sums them
+  // in fp64 in token order (as block_summaries_kernel), stores the rounded
+  // mean and scores it
   if (s.refresh) {
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
@@ -150,16 +212,17 @@ __global__ __launch_bounds__(kStepThreads, (G <= 2 ? 4 : 1)) void block_topk_dec
 #pragma unroll
       for (int e = 0; e < EPL; ++e) p = fmaf(qs[e], f[e], p);
       p = group_sum<LPT>(p);
-      if (li == 0) s_keys[jref] = order_key(p);
+      if (li == 0) {
+        const uint32_t kk = order_key(p);
+        s_keys[jref] = kk;
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+      }
     }
   }
-
-  // 2. scoring, two batches in flight
-  for (int base = 0; base < NB; base += 2 * kBatch) {
-    if (base + kBatch < NB) load_batch(base + kBatch, bufB);
-    score_batch(base, bufA);
-    if (base + 2 * kBatch < NB) load_batch(base + 2 * kBatch, bufA);
-    if (base + kBatch < NB) score_batch(base + kBatch, bufB);
+  if (li == 0) {
+    atomicMin(&s_lo, kmin);
+    atomicMax(&s_hi, kmax);
   }
   __syncthreads();
 
@@ -170,7 +233,7 @@ __global__ __launch_bounds__(kStepThreads, (G <= 2 ? 4 : 1)) void block_topk_dec
 #pragma unroll
   for (int i = 0; i < kStepKPT; ++i) key[i] = (i < kpt && j0 + i < NB) ? s_keys[j0 + i] : 0u;
   int32_t* gidx = s.block_idx ? s.block_idx + (int64_t)row * s.keff : nullptr;
-  row_topk<kStepKPT>(key, kpt, j0, NB, s.keff, s_topk, [&](int rank, int j) {
+  row_topk_range<kStepKPT>(key, kpt, j0, NB, s.keff, s_lo, s_hi, s_topk, [&](int rank, int j) {
     s_idx[rank] = j;
     if (gidx) gidx[rank] = j;
   });
@@ -180,19 +243,43 @@ __global__ __launch_bounds__(kStepThreads, (G <= 2 ? 4 : 1)) void block_topk_dec
   if constexpr (kMfma)
     attn_row_mfma<G, 0>(a, row, 0, s_idx, 0, false);
   else
-    attn_row_valu<T, D, G, 0>(a, row, 0, s_idx, 0, false);
+    attn_row_valu<T, D, G, 0>(a, row, 0, s_idx, 0, false, qraw);
+}
+
+template <typename T, int D, int G>
+hipError_t launch_g(const StepArgs& s, int rows, hipStream_t stream) {
+  // Eight waves per row unless the rows outnumber the workgroups of eight
+  // waves that fit on the chip at once: then four, so that more rows are in
+  // flight and one row's top-k is covered by the others' streaming.
+  // eight-wave workgroups per CU: a property of the kernel, found once
+  static const int resident8 = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_topk_decode_kernel<T, D, G, 8>, 512, 0) !=
+        hipSuccess)
+      n = 1;
+    return n > 0 ? n : 1;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const dim3 grid(rows);
+  if ((int64_t)rows > (int64_t)resident8 * cus)
+    hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 4>), grid, dim3(256), 0, stream, s);
+  else
+    hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 8>), grid, dim3(512), 0, stream, s);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const StepArgs& s, hipStream_t stream) {
-  const dim3 grid(s.a.d.B * s.a.d.Hkv), block(kStepThreads);
+  const int rows = s.a.d.B * s.a.d.Hkv;
   switch (s.a.d.G) {
-    case 1: hipLaunchKernelGGL((block_topk_decode_kernel<T, D, 1>), grid, block, 0, stream, s); break;
-    case 2: hipLaunchKernelGGL((block_topk_decode_kernel<T, D, 2>), grid, block, 0, stream, s); break;
-    case 4: hipLaunchKernelGGL((block_topk_decode_kernel<T, D, 4>), grid, block, 0, stream, s); break;
-    default: hipLaunchKernelGGL((block_topk_decode_kernel<T, D, 8>), grid, block, 0, stream, s); break;
+    case 1: return launch_g<T, D, 1>(s, rows, stream);
+    case 2: return launch_g<T, D, 2>(s, rows, stream);
+    case 4: return launch_g<T, D, 4>(s, rows, stream);
+    default: return launch_g<T, D, 8>(s, rows, stream);
   }
-  return hipGetLastError();
 }
 
 }  // namespace

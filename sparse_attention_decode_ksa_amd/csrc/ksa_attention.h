@@ -264,9 +264,11 @@ __device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int spl
 
 // Attention of one row (or one split of it) on VALU; the row's index slice is
 // staged in s_idx (entries from e0 on).  `sync` waits for the staging.
+// qraw, when given, holds the lane's 16 bytes of each of the group's G query
+// rows (already loaded by the caller in this lane layout).
 template <typename T, int D, int G, int KIND>
 __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int split, const int* s_idx,
-                                              int e0, bool sync) {
+                                              int e0, bool sync, const uint4* qraw = nullptr) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int SPW = 64 / LPT;
@@ -293,7 +295,8 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   float qv[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    KV<T>::widen(ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL), qv[h]);
+    KV<T>::widen(qraw ? qraw[h] : ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL),
+                 qv[h]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
   }

@@ -188,6 +188,65 @@ __device__ __forceinline__ uint64_t wave_incl_scan64(uint64_t x) {
   return x;
 }
 
+// DPP forms (no LDS traffic): row shifts build 16-lane prefixes, the row
+// broadcasts of lanes 15 and 31 carry them across the wave.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  // lanes whose source is outside the row, or whose row is masked off, read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
+  x += dpp_u32<kDppRowShr1>(x);
+  x += dpp_u32<kDppRowShr2>(x);
+  x += dpp_u32<kDppRowShr4>(x);
+  x += dpp_u32<kDppRowShr8>(x);
+  x += dpp_u32<kDppRowBcast15, 0xA>(x);  // rows 1 and 3 add the end of rows 0 and 2
+  x += dpp_u32<kDppRowBcast31, 0xC>(x);  // rows 2 and 3 add the end of row 1
+  return x;
+}
+
+// Minimum / maximum over the 64 lanes of a wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppXor1, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppXor2, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppHalfMirror, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppMirror, 0xF, 0xF, false));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), e = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, e));
+}
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppXor1, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppXor2, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppHalfMirror, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kDppMirror, 0xF, 0xF, false));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), e = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, e));
+}
+
+// Exclusive prefix sum of 32-bit values over the workgroup (blockDim.x a
+// multiple of 64, at most 1024 threads); `scratch` holds 16 uint32 in LDS.
+// One barrier; every thread of the workgroup must call it, and scratch must
+// not be written again before the caller's next barrier.
+__device__ __forceinline__ uint32_t block_excl_scan32(uint32_t x, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const uint32_t incl = wave_incl_scan_dpp(x);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  const uint32_t t = lane < nwaves ? scratch[lane] : 0u;
+  const uint32_t ti = wave_incl_scan_dpp(t);
+  const uint32_t wave_before = __builtin_amdgcn_readlane(ti - t, wave);
+  return wave_before + incl - x;
+}
+
 // Exclusive prefix sum over the workgroup (blockDim.x a multiple of 64,
 // at most 1024 threads).  `scratch` holds 17 uint64 in LDS.  Returns the
 // exclusive prefix and writes the workgroup total to *total.  Contains

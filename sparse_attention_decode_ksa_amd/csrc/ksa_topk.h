@@ -9,13 +9,14 @@
 // Bucket search on the row's key range: with all candidates in [lo, hi], a
 // key's bucket is (key - lo) >> shift, shift chosen so that the range maps
 // onto at most 256 buckets (a monotone map, so buckets are ordered like the
-// keys).  One LDS histogram and one wave scan find the bucket holding the
+// keys).  One LDS histogram and one DPP wave scan find the bucket holding the
 // `remaining`-th largest candidate; the range shrinks to that bucket.  It
 // stops when that bucket holds exactly the keys still needed (all of them
 // are taken) or when it is a single key value (the lowest positions among
 // equal keys are taken).  Buckets follow the data's own range rather than
 // fixed bit fields, so fp32 scores spread over the histogram instead of
-// piling onto the few bins a fixed top byte gives them.
+// piling onto the few bins a fixed top byte gives them.  Two histogram
+// buffers alternate between rounds, so a round costs two barriers.
 #pragma once
 
 #include "ksa_device.h"
@@ -23,49 +24,34 @@
 namespace ksa {
 
 struct TopkShared {
-  uint32_t hist[256];
+  uint32_t hist[2][256];  // both zero on entry to row_topk_range
   uint32_t red[2][16];
   uint32_t bucket[3];
-  uint64_t scan[17];
+  uint32_t scan[16];
 };
+
+// Zeroes both histogram buffers (every thread of the workgroup calls it; the
+// caller's next barrier publishes it).
+__device__ __forceinline__ void topk_clear(TopkShared& sh) {
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) (&sh.hist[0][0])[i] = 0u;
+}
 
 // Selects the keff largest keys of the row (ties: lowest position first) and
 // calls emit(rank, position) for each, rank 0..keff-1 in ascending position
 // order.  Thread t's keys are key[0..kpt) at positions j0 + i; positions >= n
-// are not candidates.  Requires 1 <= keff <= n, kpt <= KPT, a workgroup of
-// 256..1024 threads (a multiple of 64), and every thread of it calling.
+// are not candidates; every candidate key lies in [lo, hi].  Requires
+// 1 <= keff <= n, n <= 65535, kpt <= KPT, both histogram buffers zero and
+// visible, a workgroup of 256..1024 threads (a multiple of 64), and every
+// thread of it calling.
 template <int KPT, typename Emit>
-__device__ __forceinline__ void row_topk(const uint32_t (&key)[KPT], int kpt, int j0, int n,
-                                         int keff, TopkShared& sh, Emit emit) {
+__device__ __forceinline__ void row_topk_range(const uint32_t (&key)[KPT], int kpt, int j0, int n,
+                                               int keff, uint32_t lo, uint32_t hi, TopkShared& sh,
+                                               Emit emit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
   auto valid = [&](int i) { return i < kpt && j0 + i < n; };
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if (valid(i)) {
-      kmin = min(kmin, key[i]);
-      kmax = max(kmax, key[i]);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
-  if (lane == 0) {
-    sh.red[0][wave] = kmin;
-    sh.red[1][wave] = kmax;
-  }
-  __syncthreads();
-  uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
-  for (int w = 1; w < nwaves; ++w) {
-    lo = min(lo, sh.red[0][w]);
-    hi = max(hi, sh.red[1][w]);
-  }
-
   uint32_t remaining = (uint32_t)keff;
   uint32_t quota, thr;
+  int buf = 0;
 #pragma unroll 1
   for (;;) {
     const uint32_t span = hi - lo;
@@ -76,19 +62,19 @@ __device__ __forceinline__ void row_topk(const uint32_t (&key)[KPT], int kpt, in
     }
     const int bits = 32 - __clz(span);
     const int shift = bits > 8 ? bits - 8 : 0;
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();
+    uint32_t* hist = sh.hist[buf];
+    // the other buffer is cleared for the next round (nobody reads it now)
+    if (tid < 256) sh.hist[buf ^ 1][tid] = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (valid(i) && key[i] >= lo && key[i] <= hi) atomicAdd(&sh.hist[(key[i] - lo) >> shift], 1u);
+      if (valid(i) && key[i] >= lo && key[i] <= hi) atomicAdd(&hist[(key[i] - lo) >> shift], 1u);
     __syncthreads();
     if (wave == 0) {
       // lane l holds buckets 255-4l .. 252-4l (highest in lane 0)
       const int top = 255 - 4 * lane;
-      const uint32_t c0 = sh.hist[top], c1 = sh.hist[top - 1], c2 = sh.hist[top - 2],
-                     c3 = sh.hist[top - 3];
+      const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
       const uint32_t s = c0 + c1 + c2 + c3;
-      const uint32_t incl = wave_incl_scan(s);
+      const uint32_t incl = wave_incl_scan_dpp(s);
       const uint32_t excl = incl - s;
       if (excl < remaining && remaining <= incl) {
         uint32_t c = excl, cnt;
@@ -110,6 +96,7 @@ __device__ __forceinline__ void row_topk(const uint32_t (&key)[KPT], int kpt, in
     }
     __syncthreads();
     const uint32_t bk = sh.bucket[0], above = sh.bucket[1], cnt = sh.bucket[2];
+    buf ^= 1;
     remaining -= above;
     const uint64_t blo = (uint64_t)lo + ((uint64_t)bk << shift);
     const uint64_t bhi = (uint64_t)lo + (((uint64_t)bk + 1) << shift) - 1;
@@ -122,16 +109,16 @@ __device__ __forceinline__ void row_topk(const uint32_t (&key)[KPT], int kpt, in
     }
   }
 
-  // ascending compaction: keys > thr, then keys == thr up to the quota
+  // ascending compaction: keys > thr, then keys == thr up to the quota.
+  // Counts are packed (gt << 16 | eq); both totals stay below 2^16.
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     n_gt += valid(i) && key[i] > thr;
     n_eq += valid(i) && key[i] == thr;
   }
-  uint64_t total;
-  const uint64_t before = block_excl_scan64(((uint64_t)n_gt << 32) | n_eq, sh.scan, &total);
-  uint32_t gt_before = (uint32_t)(before >> 32), eq_before = (uint32_t)before;
+  const uint32_t before = block_excl_scan32((n_gt << 16) | n_eq, sh.scan);
+  uint32_t gt_before = before >> 16, eq_before = before & 0xFFFFu;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     if (!valid(i)) break;
@@ -143,6 +130,37 @@ __device__ __forceinline__ void row_topk(const uint32_t (&key)[KPT], int kpt, in
       ++eq_before;
     }
   }
+}
+
+// As row_topk_range, with the key range found here (one min/max reduction).
+// Requires both histogram buffers zero; they need not be visible yet (the
+// reduction's barrier publishes them).
+template <int KPT, typename Emit>
+__device__ __forceinline__ void row_topk(const uint32_t (&key)[KPT], int kpt, int j0, int n,
+                                         int keff, TopkShared& sh, Emit emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (i < kpt && j0 + i < n) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  }
+  kmin = wave_min_dpp(kmin);
+  kmax = wave_max_dpp(kmax);
+  if (lane == 0) {
+    sh.red[0][wave] = kmin;
+    sh.red[1][wave] = kmax;
+  }
+  __syncthreads();
+  uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
+  for (int w = 1; w < nwaves; ++w) {
+    lo = min(lo, sh.red[0][w]);
+    hi = max(hi, sh.red[1][w]);
+  }
+  row_topk_range<KPT>(key, kpt, j0, n, keff, lo, hi, sh, emit);
 }
 
 }  // namespace ksa

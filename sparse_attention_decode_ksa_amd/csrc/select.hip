@@ -97,6 +97,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = j0 + i < NB ? rk[j0 + i] : 0u;
   int32_t* out = block_idx + (int64_t)row * keff;
+  topk_clear(sh);
   row_topk<KPT>(key, KPT, j0, NB, keff, sh, [&](int rank, int j) { out[rank] = j; });
 }
 

@@ -145,13 +145,17 @@ def test_fused_step_optional_outputs():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-@pytest.mark.parametrize("name,seqs", [("c2", [0, 37, 63]), ("c3", [0, 31]), ("c5", [0, 255])])
-def test_fused_step_full_workloads(name, seqs):
-    """The full-size block top-k workloads: one split of 8 waves per row on
-    both paths, so the fused step equals the separate calls bit for bit."""
+@pytest.mark.parametrize("name,seqs,bitwise", [("c2", [0, 37, 63], True), ("c3", [0, 31], True),
+                                               ("c5", [0, 255], False)])
+def test_fused_step_full_workloads(name, seqs, bitwise):
+    """The full-size block top-k workloads.  c2 and c3 run one 8-wave
+    workgroup per row on both paths, so the fused step equals the separate
+    calls bit for bit; c5 has more rows than the chip holds 8-wave
+    workgroups, so the fused step uses 4-wave workgroups and agrees to fp32
+    merge-order rounding."""
     w = WORKLOADS[name]
     q, k, v = gpu_inputs(w)
-    s, idx, out, lse = fused_vs_separate(w, q, k, v, refresh=True, bitwise_out=True)
+    s, idx, out, lse = fused_vs_separate(w, q, k, v, refresh=True, bitwise_out=bitwise)
     check_against_oracle(w, q, k, v, s, idx, out, lse, seqs)
     del q, k, v
     torch.cuda.empty_cache()
