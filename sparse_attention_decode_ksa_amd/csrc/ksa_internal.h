@@ -73,6 +73,7 @@ hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k,
 struct VotePlan {
   int hist;        // C = T - W history tokens (candidates)
   int words;       // 32-token words per head bitmask
+  int kstride;     // uint32 keys per head row (hist rounded up to a multiple of 4)
   int kv;          // N - W picks per head
   size_t keys_off, bits_off, votes_off, vhist_off, total;
 };

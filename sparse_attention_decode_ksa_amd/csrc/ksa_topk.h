@@ -24,7 +24,7 @@
 namespace ksa {
 
 struct TopkShared {
-  uint32_t hist[2][256];  // both zero on entry to row_topk_range
+  uint32_t hist[2][256];  // both zero on entry to topk_cut
   uint32_t red[2][16];
   uint32_t bucket[3];
   uint32_t scan[16];
@@ -36,30 +36,28 @@ __device__ __forceinline__ void topk_clear(TopkShared& sh) {
   for (int i = threadIdx.x; i < 512; i += blockDim.x) (&sh.hist[0][0])[i] = 0u;
 }
 
-// Selects the keff largest keys of the row (ties: lowest position first) and
-// calls emit(rank, position) for each, rank 0..keff-1 in ascending position
-// order.  Thread t's keys are key[0..kpt) at positions j0 + i; positions >= n
-// are not candidates; every candidate key lies in [lo, hi].  Requires
-// 1 <= keff <= n, n <= 65535, kpt <= KPT, both histogram buffers zero and
-// visible, a workgroup of 256..1024 threads (a multiple of 64), and every
-// thread of it calling.
-template <int KPT, typename Emit>
-__device__ __forceinline__ void row_topk_range(const uint32_t (&key)[KPT], int kpt, int j0, int n,
-                                               int keff, uint32_t lo, uint32_t hi, TopkShared& sh,
-                                               Emit emit) {
+// Where the keff largest keys of a row end: every key > thr is taken, and
+// of the keys == thr the `quota` at the lowest positions (quota 0xFFFFFFFF:
+// all of them, which is exactly what is still needed).
+struct TopkCut {
+  uint32_t thr, quota;
+};
+
+// The bucket search.  Thread t's candidates are key[i] with valid(i); every
+// candidate lies in [lo, hi].  Requires 1 <= keff <= the number of
+// candidates, both histogram buffers zero and visible, a workgroup of
+// 256..1024 threads (a multiple of 64), and every thread of it calling.
+// Leaves one histogram buffer dirty (row_topk_range does not reuse them).
+template <int KPT, typename Valid>
+__device__ __forceinline__ TopkCut topk_cut(const uint32_t (&key)[KPT], Valid valid, int keff,
+                                            uint32_t lo, uint32_t hi, TopkShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto valid = [&](int i) { return i < kpt && j0 + i < n; };
   uint32_t remaining = (uint32_t)keff;
-  uint32_t quota, thr;
   int buf = 0;
 #pragma unroll 1
   for (;;) {
     const uint32_t span = hi - lo;
-    if (span == 0) {  // one value left: ties, lowest positions first
-      thr = lo;
-      quota = remaining;
-      break;
-    }
+    if (span == 0) return TopkCut{lo, remaining};  // one value left: ties, lowest positions first
     const int bits = 32 - __clz(span);
     const int shift = bits > 8 ? bits - 8 : 0;
     uint32_t* hist = sh.hist[buf];
@@ -102,12 +100,107 @@ __device__ __forceinline__ void row_topk_range(const uint32_t (&key)[KPT], int k
     const uint64_t bhi = (uint64_t)lo + (((uint64_t)bk + 1) << shift) - 1;
     lo = (uint32_t)blo;
     hi = bhi < (uint64_t)hi ? (uint32_t)bhi : hi;
-    if (cnt == remaining) {  // the whole bucket is taken: everything >= lo
-      thr = lo;
-      quota = 0xFFFFFFFFu;
-      break;
+    if (cnt == remaining) return TopkCut{lo, 0xFFFFFFFFu};  // the whole bucket: everything >= lo
+  }
+}
+
+// The fp32 score a key encodes (the inverse of order_key).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// topk_cut for keys of fp32 scores, with a first round on the scores' own
+// scale: bucket = floor((x - x_lo) * 256 / (x_hi - x_lo)) is monotone in x
+// (each fp32 step rounds monotonically), and it spreads scores over the
+// histogram where their bit patterns, whose leading bits are mostly the
+// exponent, pile onto a few buckets (which serialises the LDS atomics).  The
+// bucket holding the cut narrows the key range for topk_cut.  Same
+// requirements as topk_cut.
+template <int KPT, typename Valid>
+__device__ __forceinline__ TopkCut topk_cut_fp32(const uint32_t (&key)[KPT], Valid valid, int keff,
+                                                 uint32_t lo, uint32_t hi, TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const float xlo = key_value(lo);
+  const float scale = 256.0f / (key_value(hi) - xlo);
+  // a range too wide for fp32 arithmetic, or too narrow to scale, skips the round
+  if (!(hi > lo) || !(scale > 0.f && scale < 1.0e30f))
+    return topk_cut<KPT>(key, valid, keff, lo, hi, sh);
+  auto bucket = [&](uint32_t k) { return min(255, (int)((key_value(k) - xlo) * scale)); };
+  uint32_t* hist = sh.hist[0];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (valid(i)) atomicAdd(&hist[bucket(key[i])], 1u);
+  __syncthreads();
+  if (wave == 0) {
+    const int top = 255 - 4 * lane;
+    const uint32_t c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
+    const uint32_t s = c0 + c1 + c2 + c3;
+    const uint32_t incl = wave_incl_scan_dpp(s);
+    const uint32_t excl = incl - s;
+    const uint32_t need = (uint32_t)keff;
+    if (excl < need && need <= incl) {
+      uint32_t c = excl, cnt;
+      int bk;
+      if (c + c0 >= need) {
+        bk = top; cnt = c0;
+      } else if ((c += c0) + c1 >= need) {
+        bk = top - 1; cnt = c1;
+      } else if ((c += c1) + c2 >= need) {
+        bk = top - 2; cnt = c2;
+      } else {
+        c += c2;
+        bk = top - 3; cnt = c3;
+      }
+      sh.bucket[0] = (uint32_t)bk;
+      sh.bucket[1] = c;
+      sh.bucket[2] = cnt;
     }
   }
+  __syncthreads();
+  const int bk = (int)sh.bucket[0];
+  const uint32_t rem = (uint32_t)keff - sh.bucket[1], cnt = sh.bucket[2];
+  // the bucket's key range (keys between two of its keys are in it too)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (valid(i) && bucket(key[i]) == bk) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  }
+  kmin = wave_min_dpp(kmin);
+  kmax = wave_max_dpp(kmax);
+  if (tid < 256) hist[tid] = 0u;  // read by wave 0 before the last barrier
+  if (lane == 0) {
+    sh.red[0][wave] = kmin;
+    sh.red[1][wave] = kmax;
+  }
+  __syncthreads();
+  lo = sh.red[0][0];
+  hi = sh.red[1][0];
+  for (int w = 1; w < nwaves; ++w) {
+    lo = min(lo, sh.red[0][w]);
+    hi = max(hi, sh.red[1][w]);
+  }
+  if (cnt == rem) return TopkCut{lo, 0xFFFFFFFFu};  // the whole bucket is taken
+  return topk_cut<KPT>(key, valid, (int)rem, lo, hi, sh);
+}
+
+// Selects the keff largest keys of the row (ties: lowest position first) and
+// calls emit(rank, position) for each, rank 0..keff-1 in ascending position
+// order.  Thread t's keys are key[0..kpt) at positions j0 + i; positions >= n
+// are not candidates; every candidate key lies in [lo, hi].  Requires
+// 1 <= keff <= n, n <= 65535, kpt <= KPT, both histogram buffers zero and
+// visible, a workgroup of 256..1024 threads (a multiple of 64), and every
+// thread of it calling.
+template <int KPT, typename Emit>
+__device__ __forceinline__ void row_topk_range(const uint32_t (&key)[KPT], int kpt, int j0, int n,
+                                               int keff, uint32_t lo, uint32_t hi, TopkShared& sh,
+                                               Emit emit) {
+  auto valid = [&](int i) { return i < kpt && j0 + i < n; };
+  const TopkCut cut = topk_cut_fp32<KPT>(key, valid, keff, lo, hi, sh);
+  const uint32_t thr = cut.thr, quota = cut.quota;
 
   // ascending compaction: keys > thr, then keys == thr up to the quota.
   // Counts are packed (gt << 16 | eq); both totals stay below 2^16.

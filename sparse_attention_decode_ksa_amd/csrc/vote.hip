@@ -8,12 +8,13 @@
 //  1. vote_scores: every (b, KV head g) row streams its history keys once;
 //     the G query heads of the group score every token in fp32 (MFMA for
 //     bf16 D=128 groups of 4 and 8, VALU otherwise) and store
-//     order-preserving uint32 keys [B, Hq, C] in the workspace.
-//  2. vote_head_select: one workgroup per (b, h), the head's keys held in LDS
-//     when they fit, finds the Kv-th largest key and how many keys equal to
-//     it are taken (lowest token ids first) by a bucket search over the
-//     head's key range, and writes the head's picks as a bitmask
-//     [B, Hq, ceil(C/32)].
+//     order-preserving uint32 keys [B, Hq, C (padded to 4)] in the
+//     workspace.
+//  2. vote_head_topk: one workgroup per (b, h), the head's keys held in
+//     registers (in LDS or re-read for very long histories), finds the
+//     Kv-th largest key and how many keys equal to it are taken (lowest
+//     token ids first) by a bucket search over the head's key range, and
+//     writes the head's picks as a bitmask [B, Hq, ceil(C/32)].
 //  3. vote_count: one lane per history token sums its bit over the Hq heads
 //     (its vote total), stores it, and adds it to a per-sequence histogram of
 //     vote totals.
@@ -27,21 +28,44 @@
 
 #include "ksa_device.h"
 #include "ksa_internal.h"
+#include "ksa_topk.h"
 
 namespace ksa {
 namespace {
 
 constexpr int kScoreWaves = 4;
-constexpr int kScoreChunksPerWave = 8;
-constexpr int kHeadThreads = 1024;
+constexpr int kScoreChunksPerWave = 8;  // VALU scoring
+// MFMA scoring: chunks of 16 tokens per wave, and how many are in flight
+#ifndef KSA_VOTE_CHUNKS
+#define KSA_VOTE_CHUNKS 8
+#endif
+#ifndef KSA_VOTE_PREFETCH
+#define KSA_VOTE_PREFETCH 2
+#endif
+constexpr int kVoteChunks = KSA_VOTE_CHUNKS;
+constexpr int kVotePrefetch = KSA_VOTE_PREFETCH;
+static_assert(kVoteChunks % kVotePrefetch == 0, "whole prefetch rounds per wave");
+constexpr int kHeadThreads = 1024;  // selection with the keys in LDS or re-read
+// selection with the keys in registers: threads per workgroup and the most
+// history tokens per thread
+#ifndef KSA_HEAD_NT
+#define KSA_HEAD_NT 512
+#endif
+constexpr int kHeadNT = KSA_HEAD_NT;
+constexpr int kHeadMaxKPT = 64;
 constexpr int kHeadLdsKeys = 36864;  // keys a head-select workgroup keeps in LDS (144 KB)
 constexpr int kCountThreads = 256;
 constexpr int kSetThreads = 1024;
+constexpr int kSetStage = 8192;  // picks per sequence the vote set stages in LDS
+#ifndef KSA_SET_STEPS
+#define KSA_SET_STEPS 2
+#endif
+constexpr int kSetSteps = KSA_SET_STEPS;  // steps of four tokens per thread per piece of the vote set
 
 // ------------------------------------------------------------------ 1 (VALU)
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, Dims d, int hist,
+    const T* __restrict__ q, const T* __restrict__ k, Dims d, int hist, int kstride,
     uint32_t* __restrict__ keys) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
@@ -64,7 +88,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
   const int c0 = (blockIdx.x * kScoreWaves + wave) * kScoreChunksPerWave;
   const int c1 = min(c0 + kScoreChunksPerWave, nchunks);
   // head written by this lane (lanes li < G of each slot write)
-  uint32_t* kout = keys + ((int64_t)b * d.Hq + g * G + (li < G ? li : 0)) * hist;
+  uint32_t* kout = keys + ((int64_t)b * d.Hq + g * G + (li < G ? li : 0)) * kstride;
   if (c0 >= c1) return;
 
   uint4 kr[NI];
@@ -104,13 +128,18 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
 // coalesced row-layout loads, re-read in the MFMA A layout from a
 // wave-private swizzled LDS tile, and S = K Q^T runs on four
 // v_mfma_f32_16x16x32_bf16; lane l then holds head l%16's logits of tokens
-// 4*(l/16).. and writes their keys.
+// 4*(l/16) .. +3 and stores their four keys with one 16-byte store.  Each
+// wave owns kVoteChunks consecutive chunks and keeps kVotePrefetch of them
+// in flight; loads past its range re-read its last token (in cache), so
+// every load is unconditional.
 template <int G>
 __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Dims d, int hist,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Dims d, int hist, int kstride,
     uint32_t* __restrict__ keys) {
   constexpr int D = 128;
   constexpr int CH = 16;
+  constexpr int P = kVotePrefetch;
+  constexpr int Q = kVoteChunks;
   __shared__ uint4 s_k[kScoreWaves][CH * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, kg = lane >> 4;  // MFMA row / k-group; also row layout piece / slot
@@ -118,10 +147,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const uint16_t* kb = k + (int64_t)row * d.Tcap * D + 8 * r;
 
-  const int nchunks = (hist + CH - 1) / CH;
-  const int c0 = (blockIdx.x * kScoreWaves + wave) * kScoreChunksPerWave;
-  const int c1 = min(c0 + kScoreChunksPerWave, nchunks);
-  if (c0 >= c1) return;
+  const int c0 = (blockIdx.x * kScoreWaves + wave) * Q;
+  if (c0 * CH >= hist) return;
+  const int tend = min((c0 + Q) * CH, hist) - 1;  // last token of this wave's range
   bf16x8_t qop[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -129,52 +157,171 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
     if (r < G) u = ld16(q + ((int64_t)b * d.Hq + g * G + r) * D + 32 * i + 8 * kg);
     qop[i] = as_bf16x8(u);
   }
-  uint32_t* kout = keys + ((int64_t)b * d.Hq + g * G + (r < G ? r : 0)) * hist;
+  uint32_t* kout = keys + ((int64_t)b * d.Hq + g * G + (r < G ? r : 0)) * kstride;
   uint4* kt = s_k[wave];
+  auto put = [&](int t, const uint4& o) {
+    if (t + 3 < hist) {
+      st16(kout + t, o);  // kstride and t are multiples of 4
+    } else {
+      kout[t] = o.x;
+      if (t + 1 < hist) kout[t + 1] = o.y;
+      if (t + 2 < hist) kout[t + 2] = o.z;
+    }
+  };
 
   // row layout: load i, lane (slot kg, piece r) reads token 4i + kg of the chunk
-  uint4 kr[4];
+  uint4 kr[P][4];
+  auto load = [&](int c, uint4(&dst)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kr[i] = ld16_stream(kb + (int64_t)min(c0 * CH + 4 * i + kg, hist - 1) * D);
-  for (int c = c0; c < c1; ++c) {
-    uint4 kc[4];
+    for (int i = 0; i < 4; ++i) dst[i] = ld16_stream(kb + (int64_t)min(c * CH + 4 * i + kg, tend) * D);
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kc[i] = kr[i];
-    if (c + 1 < c1) {
+  for (int s = 0; s < P; ++s) load(c0 + s, kr[s]);
+#pragma unroll 1
+  for (int j0 = 0; j0 < Q; j0 += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      const int c = c0 + j0 + s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kt[ktile_slot(4 * i + kg, r)] = kr[s][i];
+      load(c + P, kr[s]);
+      wave_lds_fence();
+      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        kr[i] = ld16_stream(kb + (int64_t)min((c + 1) * CH + 4 * i + kg, hist - 1) * D);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kt[ktile_slot(4 * i + kg, r)] = kc[i];
-    wave_lds_fence();
-    f32x4_t S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kt[ktile_slot(r, 4 * i + kg)]), qop[i], S,
-                                                  0, 0, 0);
-    wave_lds_fence();
-    if (r < G) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = c * CH + 4 * kg + j;
-        if (t < hist) kout[t] = order_key(S[j]);
-      }
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kt[ktile_slot(r, 4 * i + kg)]), qop[i],
+                                                    S, 0, 0, 0);
+      wave_lds_fence();
+      const uint4 o = make_uint4(order_key(S[0]), order_key(S[1]), order_key(S[2]), order_key(S[3]));
+      const int t = c * CH + 4 * kg;
+      if (r < G && t < hist) put(t, o);
     }
   }
 }
 
 // ------------------------------------------------------------------ 2
-// Per (b, h): the Kv largest keys among the head's `hist` keys, as a bitmask.
-// Bucket search on the key range (as in select.hip): buckets
-// (key - lo) >> shift over the current range [lo, hi], one LDS histogram per
-// pass, until the threshold bucket holds exactly the keys still needed (all
-// taken) or a single key value (lowest token ids first).  The first
+// Per (b, h), history of at most NT * KPT tokens: the head's keys sit in
+// registers, token t = i * NT + tid in key[i] (coalesced loads).  A first
+// histogram on the keys' 12 leading bits picks the bucket where the Kv
+// largest end, the bucket search of ksa_topk.h resolves it, and each wave's
+// ballot of "taken" is two words of the bitmask as it stands.  Ties at the
+// threshold (equal fp32 logits) take the lowest token ids: the equal keys
+// are ranked in token order by a per-(slot, wave) count.  The first
 // workgroup of each sequence also clears that sequence's vote histogram,
 // which vote_count fills after this kernel.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void vote_head_topk_kernel(
+    const uint32_t* __restrict__ keys, int hist, int kstride, int kv, int words, int Hq,
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist) {
+  constexpr int NWV = NT / 64;
+  static_assert(4096 % NT == 0, "radix buckets per thread");
+  __shared__ TopkShared sh;
+  __shared__ uint32_t s_rh[4097];  // first-round histogram (4096: tokens past the history)
+  __shared__ uint32_t s_eq[KPT][NWV];  // equal keys per (slot, wave), then their prefix
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t hr = blockIdx.x;  // b * Hq + h
+  if (hr % Hq == 0)
+    for (int i = tid; i < 256; i += NT) vhist[(hr / Hq) * 256 + i] = 0u;
+  uint32_t* br = bits + hr * words;
+  if (kv == 0) {  // the whole budget is the recency window: no picks
+    for (int w = tid; w < words; w += NT) br[w] = 0u;
+    return;
+  }
+  const uint32_t* kr = keys + hr * kstride;
+  auto valid = [&](int i) { return i * NT + tid < hist; };
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = kr[min(i * NT + tid, hist - 1)];  // unconditional loads
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = valid(i) ? key[i] : 0u;
+  for (int j = tid; j < 4097; j += NT) s_rh[j] = 0u;
+  topk_clear(sh);
+  __syncthreads();
+  // First round on the keys' 12 leading bits (sign, exponent and three
+  // mantissa bits of the score): fp32 scores spread over these buckets
+  // without a pass for their range, and each key costs one shift.
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) atomicAdd(&s_rh[valid(i) ? key[i] >> 20 : 4096u], 1u);
+  __syncthreads();
+  {
+    // thread t owns buckets 4095 - BPT*t down to 4096 - BPT*(t+1)
+    constexpr int BPT = 4096 / NT;
+    uint32_t c[BPT], sum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = s_rh[4095 - BPT * tid - j];
+      sum += c[j];
+    }
+    const uint32_t excl = block_excl_scan32(sum, sh.scan);
+    const uint32_t need = (uint32_t)kv;
+    if (excl < need && need <= excl + sum) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        if (acc + c[j] >= need) {
+          sh.bucket[0] = (uint32_t)(4095 - BPT * tid - j);
+          sh.bucket[1] = acc;
+          sh.bucket[2] = c[j];
+          break;
+        }
+        acc += c[j];
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t lo = sh.bucket[0] << 20, rem = (uint32_t)kv - sh.bucket[1];
+  const TopkCut cut = sh.bucket[2] == rem
+                          ? TopkCut{lo, 0xFFFFFFFFu}  // the whole bucket is taken
+                          : topk_cut<KPT>(key, valid, (int)rem, lo, lo | 0xFFFFFu, sh);
+  const bool ties = cut.quota != 0xFFFFFFFFu;  // uniform
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (ties) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const uint64_t m = __ballot(valid(i) && key[i] == cut.thr);
+      if (lane == 0) s_eq[i][wave] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    if (tid == 0) {  // exclusive prefix in token order (slot-major, then wave)
+      uint32_t run = 0;
+      for (int i = 0; i < KPT; ++i)
+        for (int w = 0; w < NWV; ++w) {
+          const uint32_t c = s_eq[i][w];
+          s_eq[i][w] = run;
+          run += c;
+        }
+    }
+    __syncthreads();
+  }
+  // the ballot of slot i goes to lane i (two words), stored after the loop
+  uint32_t mlo = 0u, mhi = 0u;
+  auto keep = [&](int i, uint64_t bal) {
+    mlo = lane == i ? (uint32_t)bal : mlo;
+    mhi = lane == i ? (uint32_t)(bal >> 32) : mhi;
+  };
+  if (ties) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool eq = valid(i) && key[i] == cut.thr;
+      const uint64_t m = __ballot(eq);
+      const bool take = (valid(i) && key[i] > cut.thr) ||
+                        (eq && s_eq[i][wave] + (uint32_t)__popcll(m & below) < cut.quota);
+      keep(i, __ballot(take));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) keep(i, __ballot(valid(i) && key[i] >= cut.thr));
+  }
+  const int w0 = (lane * NT + wave * 64) >> 5;
+  if (lane < KPT && w0 < words) br[w0] = mlo;
+  if (lane < KPT && w0 + 1 < words) br[w0 + 1] = mhi;
+}
+
+// Per (b, h), any history length: the same selection with the keys in LDS
+// (kLdsKeys) or re-read from the workspace each pass.
 template <bool kLdsKeys>
 __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
-    const uint32_t* __restrict__ keys, int hist, int kv, int words, int Hq,
+    const uint32_t* __restrict__ keys, int hist, int kstride, int kv, int words, int Hq,
     uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist) {
   extern __shared__ uint32_t lkeys[];  // the head's keys (kLdsKeys)
   __shared__ uint32_t hbin[256];
@@ -190,7 +337,7 @@ __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
     for (int w = tid; w < words; w += kHeadThreads) br[w] = 0u;
     return;
   }
-  const uint32_t* kr = keys + hr * hist;
+  const uint32_t* kr = keys + hr * kstride;
 
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int t = tid; t < hist; t += kHeadThreads) {
@@ -310,7 +457,7 @@ __global__ __launch_bounds__(kCountThreads) void vote_count_kernel(
     uint32_t cnt = 0;
 #pragma unroll 8
     for (int h = 0; h < Hq; ++h) cnt += (bb[(int64_t)h * words] >> bit) & 1u;
-    votes8[(int64_t)b * hist + t] = (uint8_t)cnt;
+    votes8[(int64_t)b * words * 32 + t] = (uint8_t)cnt;
     if (votes) votes[(int64_t)b * T + t] = (uint8_t)cnt;
     atomicAdd(&lh[cnt], 1u);
   }
@@ -322,8 +469,10 @@ __global__ __launch_bounds__(kCountThreads) void vote_count_kernel(
 __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
     const uint8_t* __restrict__ votes8, const uint32_t* __restrict__ vhist, int T, int hist, int kv,
     int N, int W, int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
-  __shared__ uint64_t scan_scratch[17];
   __shared__ uint32_t sh_v, sh_above;
+  __shared__ int32_t s_pick[kSetStage];
+  __shared__ uint32_t s_cnt[2][kSetSteps * (kSetThreads / 64)];  // per (step, wave): above, on
+  __shared__ uint32_t s_tot[2];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   int32_t* out = token_idx + (int64_t)b * N;
@@ -338,7 +487,7 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
     const uint32_t* vh = vhist + b * 256;
     const uint32_t c0 = vh[top], c1 = vh[top - 1], c2 = vh[top - 2], c3 = vh[top - 3];
     const uint32_t s = c0 + c1 + c2 + c3;
-    const uint32_t incl = wave_incl_scan(s);
+    const uint32_t incl = wave_incl_scan_dpp(s);
     const uint32_t excl = incl - s;
     const uint32_t need = (uint32_t)kv;
     if (excl < need && need <= incl) {
@@ -362,28 +511,106 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
   const uint32_t vthr = sh_v;
   const uint32_t take_eq = (uint32_t)kv - sh_above;
 
-  // ascending compaction over contiguous runs of tokens
-  const uint8_t* vb = votes8 + (int64_t)b * hist;
-  const int per = (hist + kSetThreads - 1) / kSetThreads;
-  const int ta = min(tid * per, hist), tb = min(ta + per, hist);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int t = ta; t < tb; ++t) {
-    const uint32_t v = vb[t];
-    n_gt += v > vthr;
-    n_eq += v == vthr;
-  }
-  uint64_t total;
-  const uint64_t before = block_excl_scan64(((uint64_t)n_gt << 32) | n_eq, scan_scratch, &total);
-  uint32_t gt_before = (uint32_t)(before >> 32), eq_before = (uint32_t)before;
-  for (int t = ta; t < tb; ++t) {
-    const uint32_t v = vb[t];
-    if (v > vthr) {
-      out[gt_before + min(eq_before, take_eq)] = t;
-      ++gt_before;
-    } else if (v == vthr) {
-      if (eq_before < take_eq) out[gt_before + eq_before] = t;
-      ++eq_before;
+  // Ascending compaction, four tokens per thread per step: thread tid of
+  // step i holds the vote bytes of tokens 4u .. 4u+3, u = base + i *
+  // kSetThreads + tid (one 32-bit load).  Pass 1 counts, per (step, wave),
+  // the tokens above the threshold and those on it (ballots per byte); one
+  // wave turns the counts into exclusive prefixes in token order; pass 2
+  // places every pick from its prefix and its rank inside the wave.
+  // Histories longer than kSetSteps steps run in pieces with a carry.  The
+  // picks are staged in LDS when they fit, so the output is written
+  // coalesced.
+  constexpr int NWV = kSetThreads / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint32_t* vb = reinterpret_cast<const uint32_t*>(votes8 + (int64_t)b * ((hist + 31) / 32) * 32);
+  const int nq = (hist + 3) / 4;  // vote words of four tokens
+  const bool stage = kv <= kSetStage;  // uniform
+  uint32_t carry_gt = 0, carry_eq = 0;
+  for (int base = 0; base < nq; base += kSetSteps * kSetThreads) {
+    uint32_t vv[kSetSteps];
+#pragma unroll
+    for (int i = 0; i < kSetSteps; ++i) vv[i] = vb[min(base + i * kSetThreads + tid, nq - 1)];
+    // ballots of step i: g[k] / e[k] = lanes whose token 4u+k is above / on the threshold
+    auto ballots = [&](int i, uint64_t(&g)[4], uint64_t(&e)[4]) {
+      const int t0 = 4 * (base + i * kSetThreads + tid);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t v = (vv[i] >> (8 * k)) & 0xFFu;
+        const bool in = t0 + k < hist;
+        g[k] = __ballot(in && v > vthr);
+        e[k] = __ballot(in && v == vthr);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kSetSteps; ++i) {
+      uint64_t g[4], e[4];
+      ballots(i, g, e);
+      if (lane == 0) {
+        s_cnt[0][i * NWV + wave] = (uint32_t)(__popcll(g[0]) + __popcll(g[1]) + __popcll(g[2]) + __popcll(g[3]));
+        s_cnt[1][i * NWV + wave] = (uint32_t)(__popcll(e[0]) + __popcll(e[1]) + __popcll(e[2]) + __popcll(e[3]));
+      }
     }
+    __syncthreads();
+    if (wave == 0) {  // lane l: the entries of step l, in wave order
+      uint32_t sg = 0, se = 0;
+      if (lane < kSetSteps) {
+#pragma unroll
+        for (int j = 0; j < NWV; ++j) {
+          const uint32_t gc = s_cnt[0][lane * NWV + j], ec = s_cnt[1][lane * NWV + j];
+          s_cnt[0][lane * NWV + j] = sg;
+          s_cnt[1][lane * NWV + j] = se;
+          sg += gc;
+          se += ec;
+        }
+      }
+      const uint32_t ig = wave_incl_scan_dpp(sg), ie = wave_incl_scan_dpp(se);
+      if (lane < kSetSteps) {
+#pragma unroll
+        for (int j = 0; j < NWV; ++j) {
+          s_cnt[0][lane * NWV + j] += ig - sg + carry_gt;
+          s_cnt[1][lane * NWV + j] += ie - se + carry_eq;
+        }
+      }
+      if (lane == 63) {
+        s_tot[0] = ig;
+        s_tot[1] = ie;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSetSteps; ++i) {
+      uint64_t g[4], e[4];
+      ballots(i, g, e);
+      uint32_t rg = s_cnt[0][i * NWV + wave], re = s_cnt[1][i * NWV + wave];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        rg += (uint32_t)__popcll(g[k] & below);
+        re += (uint32_t)__popcll(e[k] & below);
+      }
+      const int t0 = 4 * (base + i * kSetThreads + tid);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // the thread's own tokens, in order
+        const bool gt = (g[k] >> lane) & 1ull, eq = (e[k] >> lane) & 1ull;
+        int pos = -1;
+        if (gt) pos = (int)(rg + min(re, take_eq));
+        if (eq && re < take_eq) pos = (int)(rg + re);
+        if (pos >= 0) {
+          if (stage)
+            s_pick[pos] = t0 + k;
+          else
+            out[pos] = t0 + k;
+        }
+        rg += gt;
+        re += eq;
+      }
+    }
+    carry_gt += s_tot[0];
+    carry_eq += s_tot[1];
+    __syncthreads();  // s_cnt and s_tot are rewritten by the next piece
+  }
+  if (stage) {
+    for (int i = tid; i < kv; i += kSetThreads) out[i] = s_pick[i];
   }
 }
 
@@ -401,32 +628,72 @@ __global__ void vote_all_kernel(int T, int32_t* __restrict__ token_idx, uint8_t*
 #endif
 
 template <typename T, int D, int G>
-hipError_t launch_scores(const Dims& d, const void* q, const void* k, int hist, uint32_t* keys,
-                         hipStream_t s) {
-  const int ch = chunk_tokens(d);
-  const int nchunks = (hist + ch - 1) / ch;
-  const int per_wg = kScoreWaves * kScoreChunksPerWave;
-  const dim3 grid((nchunks + per_wg - 1) / per_wg, d.B * d.Hkv);
+hipError_t launch_scores(const Dims& d, const void* q, const void* k, int hist, int kstride,
+                         uint32_t* keys, hipStream_t s) {
   constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
   if constexpr (mfma) {
+    const int nchunks = (hist + 15) / 16;
+    const int per_wg = kScoreWaves * kVoteChunks;
+    const dim3 grid((nchunks + per_wg - 1) / per_wg, d.B * d.Hkv);
     hipLaunchKernelGGL((vote_scores_mfma_kernel<G>), grid, dim3(kScoreWaves * 64), 0, s,
-                       (const uint16_t*)q, (const uint16_t*)k, d, hist, keys);
+                       (const uint16_t*)q, (const uint16_t*)k, d, hist, kstride, keys);
   } else {
+    const int nchunks = (hist + chunk_tokens(d) - 1) / chunk_tokens(d);
+    const int per_wg = kScoreWaves * kScoreChunksPerWave;
+    const dim3 grid((nchunks + per_wg - 1) / per_wg, d.B * d.Hkv);
     hipLaunchKernelGGL((vote_scores_kernel<T, D, G>), grid, dim3(kScoreWaves * 64), 0, s,
-                       (const T*)q, (const T*)k, d, hist, keys);
+                       (const T*)q, (const T*)k, d, hist, kstride, keys);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_scores_g(const Dims& d, const void* q, const void* k, int hist, uint32_t* keys,
-                           hipStream_t s) {
+hipError_t launch_scores_g(const Dims& d, const void* q, const void* k, int hist, int kstride,
+                           uint32_t* keys, hipStream_t s) {
   switch (d.G) {
-    case 1: return launch_scores<T, D, 1>(d, q, k, hist, keys, s);
-    case 2: return launch_scores<T, D, 2>(d, q, k, hist, keys, s);
-    case 4: return launch_scores<T, D, 4>(d, q, k, hist, keys, s);
-    default: return launch_scores<T, D, 8>(d, q, k, hist, keys, s);
+    case 1: return launch_scores<T, D, 1>(d, q, k, hist, kstride, keys, s);
+    case 2: return launch_scores<T, D, 2>(d, q, k, hist, kstride, keys, s);
+    case 4: return launch_scores<T, D, 4>(d, q, k, hist, kstride, keys, s);
+    default: return launch_scores<T, D, 8>(d, q, k, hist, kstride, keys, s);
   }
+}
+
+hipError_t launch_head_select(const Dims& d, const VotePlan& p, const uint32_t* keys, uint32_t* bits,
+                              uint32_t* vhist, hipStream_t stream) {
+  const dim3 grid(d.B * d.Hq), block(kHeadThreads);
+  const int kpt = (p.hist + kHeadNT - 1) / kHeadNT;
+#define KSA_HEAD_TOPK(K)                                                                      \
+  hipLaunchKernelGGL((vote_head_topk_kernel<kHeadNT, K>), grid, dim3(kHeadNT), 0, stream, keys, \
+                     p.hist, p.kstride, p.kv, p.words, d.Hq, bits, vhist)
+  if (kpt <= 8) {
+    KSA_HEAD_TOPK(8);
+  } else if (kpt <= 16) {
+    KSA_HEAD_TOPK(16);
+  } else if (kpt <= 24) {
+    KSA_HEAD_TOPK(24);
+  } else if (kpt <= 32) {
+    KSA_HEAD_TOPK(32);
+  } else if (kpt <= 40) {
+    KSA_HEAD_TOPK(40);
+  } else if (kpt <= 48) {
+    KSA_HEAD_TOPK(48);
+  } else if (kpt <= kHeadMaxKPT) {
+    KSA_HEAD_TOPK(kHeadMaxKPT);
+  } else if (p.hist <= kHeadLdsKeys) {
+#undef KSA_HEAD_TOPK
+    const size_t lds = (size_t)p.hist * sizeof(uint32_t);
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute((const void*)vote_head_select_kernel<true>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(vote_head_select_kernel<true>, grid, block, lds, stream, keys, p.hist,
+                       p.kstride, p.kv, p.words, d.Hq, bits, vhist);
+  } else {
+    hipLaunchKernelGGL(vote_head_select_kernel<false>, grid, block, 0, stream, keys, p.hist,
+                       p.kstride, p.kv, p.words, d.Hq, bits, vhist);
+  }
+  return hipGetLastError();
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -437,12 +704,13 @@ VotePlan plan_vote(const Dims& d, int N, int W) {
   VotePlan p;
   p.hist = d.T - W;
   p.words = (p.hist + 31) / 32;
+  p.kstride = (p.hist + 3) & ~3;  // key rows start 16-byte aligned
   p.kv = N - W;
   const size_t rows = (size_t)d.B * d.Hq;
   p.keys_off = 0;
-  p.bits_off = align256(rows * (size_t)p.hist * sizeof(uint32_t));
+  p.bits_off = align256(rows * (size_t)p.kstride * sizeof(uint32_t));
   p.votes_off = align256(p.bits_off + rows * (size_t)p.words * sizeof(uint32_t));
-  p.vhist_off = align256(p.votes_off + (size_t)d.B * p.hist);
+  p.vhist_off = align256(p.votes_off + (size_t)d.B * p.words * 32);
   p.total = p.vhist_off + (size_t)d.B * 256 * sizeof(uint32_t);
   if (d.T <= N) p.total = 0;
   return p;
@@ -463,26 +731,13 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
   uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
   hipError_t e;
   if (d.dtype == KSA_BF16)
-    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, keys, stream)
-                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, keys, stream);
+    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
+                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
   else
-    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, keys, stream)
-                  : launch_scores_g<float, 128>(d, q, k, plan.hist, keys, stream);
+    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
+                  : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
   if (e != hipSuccess) return e;
-  if (plan.hist <= kHeadLdsKeys) {
-    const size_t lds = (size_t)plan.hist * sizeof(uint32_t);
-    if (lds > 65536) {
-      e = hipFuncSetAttribute((const void*)vote_head_select_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(vote_head_select_kernel<true>, dim3(d.B * d.Hq), dim3(kHeadThreads), lds,
-                       stream, keys, plan.hist, plan.kv, plan.words, d.Hq, bits, vhist);
-  } else {
-    hipLaunchKernelGGL(vote_head_select_kernel<false>, dim3(d.B * d.Hq), dim3(kHeadThreads), 0,
-                       stream, keys, plan.hist, plan.kv, plan.words, d.Hq, bits, vhist);
-  }
-  e = hipGetLastError();
+  e = launch_head_select(d, plan, keys, bits, vhist, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(vote_count_kernel, dim3((plan.hist + kCountThreads - 1) / kCountThreads, d.B),
                      dim3(kCountThreads), 0, stream, bits, d.Hq, plan.hist, plan.words, d.T, votes8,

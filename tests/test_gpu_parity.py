@@ -395,6 +395,34 @@ def test_select_topk_large_block_counts(T, Bs, k):
     check_block_selection(idx.cpu().numpy().reshape(4, -1), raw.reshape(4, -1), w.top_k)
 
 
+@pytest.mark.parametrize("T,W,Hq,Hkv,D,integer", [
+    (4003, 128, 32, 8, 128, False),   # MFMA scoring, history not a multiple of 4 (ragged key tail)
+    (12000, 500, 8, 2, 128, False),   # 16 keys per thread in registers, MFMA G = 4
+    (24000, 600, 16, 2, 128, False),  # 24 keys per thread, MFMA G = 8
+    (30000, 100, 4, 2, 64, True),     # 32 keys per thread, integer logits: exact ties everywhere
+    (35000, 1000, 4, 2, 64, False),   # 34000 history tokens: keys in LDS, vote set over 2 words a thread
+])
+def test_vote_select_selection_paths(T, W, Hq, Hkv, D, integer):
+    """Each way the per-head selection can run (keys in registers at 8..32
+    per thread, in LDS, or streamed) and both vote-set layouts agree with
+    the oracle's rule on the GPU's own logits (integer inputs: bit for bit)."""
+    w = small_workload(B=1, Hq=Hq, Hkv=Hkv, D=D, T=T, dtype="bf16", seed=T + W)
+    if integer:
+        q, k, v = gpu_inputs(w, integer=True, lo=-1, hi=1)
+    else:
+        q, k, v = gpu_inputs(w)
+    N = 2048
+    idx, votes = ksa.ksa_vote_select(q, k, w.T, N, W, want_votes=True)
+    torch.cuda.synchronize()
+    if integer:
+        sel, ref_votes = oracle.vote_select(np_bits(q), np_bits(k), w.T, N, W)
+        np.testing.assert_array_equal(votes.cpu().numpy().astype(np.int32), ref_votes)
+        np.testing.assert_array_equal(idx.cpu().numpy(), sel)
+    else:
+        lg = oracle.head_logits(np_bits(q), np_bits(k), w.T)
+        check_votes(votes.cpu().numpy(), idx.cpu().numpy(), lg, N, W)
+
+
 def test_vote_select_history_longer_than_lds():
     """More than 36864 history tokens: the per-head selection streams its keys
     from the workspace instead of holding them in LDS."""
