@@ -15,12 +15,14 @@
 //     Kv-th largest key and how many keys equal to it are taken (lowest
 //     token ids first) by a bucket search over the head's key range, and
 //     writes the head's picks as a bitmask [B, Hq, ceil(C/32)].
-//  3. vote_count: one lane per history token sums its bit over the Hq heads
-//     (its vote total), stores it, and adds it to a per-sequence histogram of
-//     vote totals.
-//  4. vote_set: one workgroup per b reads the histogram, finds the vote
-//     threshold, and compacts the first Kv tokens by (votes desc, t asc) in
-//     ascending order with one workgroup scan; the W recent tokens follow.
+//  3. vote_tally_set (histories up to 32768 tokens): one workgroup per b
+//     adds the heads' bitmasks into bit-sliced vote totals, finds the vote
+//     threshold by a binary search on popcounts, and compacts the first Kv
+//     tokens by (votes desc, t asc) in ascending order with one workgroup
+//     scan; the W recent tokens follow.  Longer histories take two kernels:
+//     vote_count (one lane per token sums its bit over the heads, stores the
+//     total and fills a per-sequence histogram of totals) and vote_set (the
+//     threshold from the histogram, then the same compaction).
 // Everything after the fp32 scores is exact integer work.
 #include <float.h>
 
@@ -614,6 +616,141 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
   }
 }
 
+// ------------------------------------------------------------------ 3+4 in one
+// Histories of at most kSetThreads * 32 tokens: one workgroup per sequence
+// tallies the votes and builds the set.  Thread w owns the 32 tokens of
+// bitmask word w: it adds the Hq heads' words into NP bit planes (a
+// bit-sliced counter, so plane k holds bit k of every token's vote total).
+// The vote threshold v* (the largest v with at least Kv tokens voted >= v)
+// comes from a binary search whose counts are popcounts of bit-sliced
+// comparisons; the picks are the tokens above v* and the first ones on it,
+// placed in token order by one workgroup scan and staged in LDS.
+template <int NP>
+__device__ __forceinline__ uint32_t votes_at_least(const uint32_t (&c)[NP], int v) {
+  // tokens of the word whose vote total is >= v (0 <= v < 2^NP), MSB first
+  uint32_t gt = 0u, eq = 0xFFFFFFFFu;
+#pragma unroll
+  for (int k = NP - 1; k >= 0; --k) {
+    if ((v >> k) & 1) {
+      eq &= c[k];
+    } else {
+      gt |= eq & c[k];
+      eq &= ~c[k];
+    }
+  }
+  return gt | eq;
+}
+
+template <int NP>
+__global__ __launch_bounds__(kSetThreads) void vote_tally_set_kernel(
+    const uint32_t* __restrict__ bits, int Hq, int T, int hist, int words, int kv, int N, int W,
+    int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
+  constexpr int NWV = kSetThreads / 64;
+  __shared__ uint32_t s_red[2][NWV];
+  __shared__ uint32_t s_scan[16];
+  __shared__ int32_t s_pick[kSetStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  int32_t* out = token_idx + (int64_t)b * N;
+  for (int i = tid; i < W; i += kSetThreads) {
+    out[kv + i] = hist + i;
+    if (votes) votes[(int64_t)b * T + hist + i] = 0;
+  }
+
+  // bit-sliced vote totals of the thread's word
+  const int w = tid;
+  const uint32_t valid = w >= words ? 0u
+                         : (w == words - 1 && (hist & 31)) ? (1u << (hist & 31)) - 1u
+                                                            : 0xFFFFFFFFu;
+  uint32_t c[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) c[k] = 0u;
+  const uint32_t* bw = bits + (int64_t)b * Hq * words + min(w, words - 1);
+  for (int h0 = 0; h0 < Hq; h0 += 8) {
+    uint32_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = bw[(int64_t)min(h0 + j, Hq - 1) * words];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t carry = h0 + j < Hq ? x[j] & valid : 0u;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const uint32_t t = c[k] & carry;
+        c[k] ^= carry;
+        carry = t;
+      }
+    }
+  }
+  if (votes && w < words) {
+    for (int j = 0; j < 32 && w * 32 + j < hist; ++j) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < NP; ++k) v |= ((c[k] >> j) & 1u) << k;
+      votes[(int64_t)b * T + w * 32 + j] = (uint8_t)v;
+    }
+  }
+  if (kv == 0) return;  // uniform: the whole workgroup leaves
+
+  // v*: count(votes >= lo) >= Kv > count(votes >= hi), hi - lo shrinking to 1
+  auto count_at_least = [&](int v, int parity) {
+    uint32_t n = (uint32_t)__popc(votes_at_least<NP>(c, v) & valid);
+    n = wave_incl_scan_dpp(n);
+    if (lane == 63) s_red[parity][wave] = n;
+    __syncthreads();
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) tot += s_red[parity][i];
+    return tot;
+  };
+  int lo = 0, hi = Hq + 1, parity = 0;
+  uint32_t above = 0;  // count(votes >= hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    const uint32_t n = count_at_least(mid, parity);
+    parity ^= 1;
+    if (n >= (uint32_t)kv) {
+      lo = mid;
+    } else {
+      hi = mid;
+      above = n;
+    }
+  }
+  const uint32_t take_eq = (uint32_t)kv - above;
+  const uint32_t ge = votes_at_least<NP>(c, lo) & valid;
+  const uint32_t gtm = hi <= Hq ? votes_at_least<NP>(c, hi) & valid : 0u;
+  const uint32_t eqm = ge & ~gtm;
+
+  // ascending compaction over the words, one scan
+  const uint32_t n_gt = (uint32_t)__popc(gtm), n_eq = (uint32_t)__popc(eqm);
+  const uint32_t before = block_excl_scan32((n_gt << 16) | n_eq, s_scan);
+  uint32_t gt_before = before >> 16, eq_before = before & 0xFFFFu;
+  const bool stage = kv <= kSetStage;  // uniform
+  uint32_t m = gtm | eqm;
+  while (m) {
+    const int j = __ffs(m) - 1;
+    m &= m - 1u;
+    const int t = w * 32 + j;
+    int pos = -1;
+    if ((gtm >> j) & 1u) {
+      pos = (int)(gt_before + min(eq_before, take_eq));
+      ++gt_before;
+    } else {
+      if (eq_before < take_eq) pos = (int)(gt_before + eq_before);
+      ++eq_before;
+    }
+    if (pos >= 0) {
+      if (stage)
+        s_pick[pos] = t;
+      else
+        out[pos] = t;
+    }
+  }
+  if (stage) {
+    __syncthreads();
+    for (int i = tid; i < kv; i += kSetThreads) out[i] = s_pick[i];
+  }
+}
+
 // T <= N: the whole context, no vote.
 __global__ void vote_all_kernel(int T, int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
   const int b = blockIdx.y;
@@ -739,6 +876,15 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
   if (e != hipSuccess) return e;
   e = launch_head_select(d, plan, keys, bits, vhist, stream);
   if (e != hipSuccess) return e;
+  if (plan.words <= kSetThreads) {
+    if (d.Hq < 64)
+      hipLaunchKernelGGL(vote_tally_set_kernel<6>, dim3(d.B), dim3(kSetThreads), 0, stream, bits,
+                         d.Hq, d.T, plan.hist, plan.words, plan.kv, N, W, token_idx, votes);
+    else
+      hipLaunchKernelGGL(vote_tally_set_kernel<8>, dim3(d.B), dim3(kSetThreads), 0, stream, bits,
+                         d.Hq, d.T, plan.hist, plan.words, plan.kv, N, W, token_idx, votes);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(vote_count_kernel, dim3((plan.hist + kCountThreads - 1) / kCountThreads, d.B),
                      dim3(kCountThreads), 0, stream, bits, d.Hq, plan.hist, plan.words, d.T, votes8,
                      votes, vhist);
