@@ -203,13 +203,67 @@ ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, cons
                                  int32_t refresh_last_block, int32_t* block_idx, float* out,
                                  float* lse, void* stream);
 
+/* ---------------------------------------------------------------------
+ * Paged KV cache with one length per sequence (Kinetics explainer, section
+ * 五: block top-k attention works with a paged cache, the attention blocks
+ * being its pages).
+ * K and V live in pools of pages; a page holds block_size consecutive tokens
+ * of one sequence for every KV head:
+ *   k_pool, v_pool  [num_pages, Hkv, Bs, D]   KV dtype
+ * Logical block j of sequence b (tokens [j*Bs, (j+1)*Bs)) is page
+ * block_table[b * max_blocks + j]; sequence b holds T_b = seq_lens[b]
+ * tokens, NB_b = ceil(T_b / Bs) blocks.  Summaries stay per sequence:
+ *   summaries  [B, Hkv, max_blocks, D]
+ * In the problem struct, seq_len is the longest T_b (it sizes launches and
+ * workspaces) and max_seq_len must equal max_blocks * Bs.  The table and the
+ * lengths are device data and are not validated: a page id >= num_pages for
+ * a block < NB_b is undefined behaviour; lengths are clamped into
+ * [1, max_blocks * Bs].  num_pages * Hkv * Bs must stay below 2^31. */
+typedef struct {
+  const int32_t* block_table; /* device [B, max_blocks] int32 */
+  const int32_t* seq_lens;    /* device [B] int32 */
+  int32_t max_blocks;         /* >= 1: row stride of block_table */
+  int32_t num_pages;          /* >= 1: pages in each pool */
+} ksa_paged_kv;
+
+/* ksa_paged_block_summaries -- ksa_block_summaries on a paged cache: for
+ * every (sequence, KV head), the blocks j in [first_block, first_block +
+ * num_blocks) with j < NB_b get their mean key (same arithmetic, n_j counted
+ * against T_b).  first_block = -1 with num_blocks = 1 selects each
+ * sequence's own newest block (T_b - 1) / Bs (the decode-step refresh).
+ * Requires num_blocks >= 1 and first_block + num_blocks <= max_blocks (or the
+ * -1 form).  Needs no workspace. */
+ksa_status ksa_paged_block_summaries(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                     const void* k_pool, void* summaries, int32_t first_block,
+                                     int32_t num_blocks, void* stream);
+
+/* ksa_paged_block_topk_decode -- ksa_block_topk_decode on a paged cache with
+ * per-sequence lengths: each row uses its own T_b, NB_b and
+ * k_eff_b = min(top_k, NB_b).  block_idx (nullable) is [B, Hkv, top_k]
+ * int32: the k_eff_b ids ascending, then -1.  When every T_b equals T,
+ * summaries, ids, out and lse are bitwise those of ksa_block_topk_decode on
+ * the same tokens stored contiguously.  Same limits as
+ * ksa_block_topk_decode, with NB = max_blocks.  Needs no workspace. */
+ksa_status ksa_paged_block_topk_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       void* summaries, int32_t top_k, int32_t refresh_last_block,
+                                       int32_t* block_idx, float* out, float* lse, void* stream);
+
+/* ksa_paged_dense_decode -- ksa_dense_decode on a paged cache: every query
+ * head of sequence b attends its T_b tokens.
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_PAGED_DENSE, 0) bytes. */
+ksa_status ksa_paged_dense_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                  const void* q, const void* k_pool, const void* v_pool, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Operations for ksa_workspace_bytes. */
 enum {
   KSA_OP_SELECT_TOPK = 0,    /* param: top_k */
   KSA_OP_SPARSE_BLOCKS = 1,  /* param: selection count (blocks per row) */
   KSA_OP_SPARSE_TOKENS = 2,  /* param: selection count (tokens per sequence) */
   KSA_OP_VOTE_SELECT = 3,    /* param: token_budget */
-  KSA_OP_DENSE = 4           /* param: unused */
+  KSA_OP_DENSE = 4,          /* param: unused */
+  KSA_OP_PAGED_DENSE = 5     /* param: unused */
 };
 
 /* Workspace bytes a call needs for this problem; a pure host function of its

@@ -133,6 +133,19 @@ def block_summaries(k: np.ndarray, T: int, Bs: int, first_block: int = 0, num_bl
     return (out, m64) if want_f64 else out
 
 
+def gather_pages(pool: np.ndarray, block_table: np.ndarray, b: int, T: int, Bs: int) -> np.ndarray:
+    """Tokens [0, T) of sequence b of a paged cache, as a contiguous
+    [1, Hkv, T, D] array (Kinetics explainer, section 五: the method works
+    with a paged KV cache, its blocks being the pages).  Page
+    block_table[b, j] of the pool [num_pages, Hkv, Bs, D] holds tokens
+    [j*Bs, (j+1)*Bs) of the sequence for every KV head; the paged result is
+    the contiguous definition applied to these tokens."""
+    nb = nblocks(T, Bs)
+    pages = pool[np.asarray(block_table)[b, :nb]]              # [nb, Hkv, Bs, D]
+    seq = pages.transpose(1, 0, 2, 3).reshape(pool.shape[1], nb * Bs, pool.shape[3])
+    return np.ascontiguousarray(seq[None, :, :T])
+
+
 def group_scores(q: np.ndarray, summaries: np.ndarray, T: int, Bs: int, sm_scale: float = 0.0,
                  Tcap: int | None = None):
     """(raw, scaled) block relevance [B,Hkv,NB] from the stored summaries

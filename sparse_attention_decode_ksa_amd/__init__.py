@@ -9,8 +9,9 @@ unloadable library raises :class:`KsaLibraryError` on first use.
 
 Function names match the C entry points: ``ksa_block_summaries``,
 ``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode``,
-``ksa_vote_select``, ``ksa_dense_decode``, ``ksa_workspace_bytes``,
-``ksa_status_string``.
+``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
+``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
+``ksa_paged_dense_decode``, ``ksa_workspace_bytes``, ``ksa_status_string``.
 """
 from __future__ import annotations
 
@@ -29,11 +30,12 @@ KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMA
 KSA_F32, KSA_BF16 = 0, 1
 KSA_SEL_BLOCKS, KSA_SEL_TOKENS = 0, 1
 (KSA_OP_SELECT_TOPK, KSA_OP_SPARSE_BLOCKS, KSA_OP_SPARSE_TOKENS, KSA_OP_VOTE_SELECT,
- KSA_OP_DENSE) = range(5)
+ KSA_OP_DENSE, KSA_OP_PAGED_DENSE) = range(6)
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode",
+            "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
             "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
 
 
@@ -63,6 +65,12 @@ class Selection(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("idx", ctypes.c_void_p), ("count", ctypes.c_int32)]
 
 
+class PagedKv(ctypes.Structure):
+    """Mirror of ``ksa_paged_kv``."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("max_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -89,14 +97,17 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_block_topk_decode.argtypes = [PP, P, P, P, P, I32, I32, P, P, P, P]
         lib.ksa_vote_select.argtypes = [PP, P, P, I32, I32, P, P, P, SZ, P]
         lib.ksa_dense_decode.argtypes = [PP, P, P, P, P, P, P, SZ, P]
+        PG = ctypes.POINTER(PagedKv)
+        lib.ksa_paged_block_summaries.argtypes = [PP, PG, P, P, I32, I32, P]
+        lib.ksa_paged_block_topk_decode.argtypes = [PP, PG, P, P, P, P, I32, I32, P, P, P, P]
+        lib.ksa_paged_dense_decode.argtypes = [PP, PG, P, P, P, P, P, P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
-                     "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode"):
+        for name in EXPORTED[:9]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -321,4 +332,101 @@ def ksa_dense_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len:
                                 _dev(out, "out", torch.float32, (B, Hq, D)),
                                 _dev(lse, "lse", torch.float32, (B, Hq)), pws, nws,
                                 _stream(stream)), "ksa_dense_decode")
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- paged cache
+def _paged_args(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                seq_lens: torch.Tensor, max_len: Optional[int], sm_scale: float):
+    """Problem and ksa_paged_kv for q [B,Hq,D], pools [num_pages,Hkv,Bs,D],
+    block_table [B,max_blocks] int32 and seq_lens [B] int32.  max_len is the
+    longest sequence (read from seq_lens, a device sync, when not given)."""
+    if k_pool.dim() != 4 or block_table.dim() != 2 or seq_lens.dim() != 1:
+        raise ValueError("pools must be [num_pages,Hkv,Bs,D], block_table [B,max_blocks], "
+                         "seq_lens [B]")
+    num_pages, Hkv, Bs, D = k_pool.shape
+    B = block_table.shape[0]
+    max_blocks = block_table.shape[1]
+    if max_len is None:
+        max_len = int(seq_lens.max().item())
+    Hq = q.shape[1] if q is not None else Hkv
+    prob = Problem(B, Hq, Hkv, D, int(max_len), max_blocks * Bs, Bs, _dtype_code(k_pool),
+                   float(sm_scale))
+    pg = PagedKv(_dev(block_table, "block_table", torch.int32, (B, max_blocks)),
+                 _dev(seq_lens, "seq_lens", torch.int32, (B,)), max_blocks, num_pages)
+    return prob, pg
+
+
+def ksa_paged_block_summaries(k_pool: torch.Tensor, summaries: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor,
+                              max_len: Optional[int] = None, first_block: int = 0,
+                              num_blocks: Optional[int] = None, newest_only: bool = False,
+                              stream=None) -> torch.Tensor:
+    """Mean key of blocks [first_block, first_block + num_blocks) of every
+    sequence (those below its own block count), or of each sequence's newest
+    block, into summaries [B,Hkv,max_blocks,D]."""
+    lib = load_library()
+    prob, pg = _paged_args(None, k_pool, block_table, seq_lens, max_len, 0.0)
+    B, max_blocks = block_table.shape
+    if newest_only:
+        first_block, num_blocks = -1, 1
+    elif num_blocks is None:
+        num_blocks = max_blocks - first_block
+    _check(lib.ksa_paged_block_summaries(
+        ctypes.byref(prob), ctypes.byref(pg), _dev(k_pool, "k_pool"),
+        _dev(summaries, "summaries", k_pool.dtype, (B, k_pool.shape[1], max_blocks, k_pool.shape[3])),
+        int(first_block), int(num_blocks), _stream(stream)), "ksa_paged_block_summaries")
+    return summaries
+
+
+def ksa_paged_block_topk_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                summaries: torch.Tensor, block_table: torch.Tensor,
+                                seq_lens: torch.Tensor, top_k: int,
+                                max_len: Optional[int] = None, refresh_last_block: bool = True,
+                                block_idx=None, want_block_idx: bool = False, out=None, lse=None,
+                                want_lse: bool = True, sm_scale: float = 0.0, stream=None):
+    """The one-launch decode step on a paged cache with per-sequence lengths.
+    Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None, block_idx
+    [B,Hkv,top_k] int32 (-1 past each row's k_eff) or None)."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, sm_scale)
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if block_idx is None and want_block_idx:
+        block_idx = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=q.device)
+    _check(lib.ksa_paged_block_topk_decode(
+        ctypes.byref(prob), ctypes.byref(pg), _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool", k_pool.dtype, k_pool.shape),
+        _dev(summaries, "summaries", k_pool.dtype, (B, Hkv, block_table.shape[1], D)),
+        int(top_k), 1 if refresh_last_block else 0,
+        _dev(block_idx, "block_idx", torch.int32, (B, Hkv, top_k)),
+        _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
+        _stream(stream)), "ksa_paged_block_topk_decode")
+    return out, lse, block_idx
+
+
+def ksa_paged_dense_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_table: torch.Tensor, seq_lens: torch.Tensor,
+                           max_len: Optional[int] = None, out=None, lse=None,
+                           want_lse: bool = True, sm_scale: float = 0.0, workspace=None,
+                           stream=None):
+    """Exact attention of every query head over its sequence's T_b tokens of
+    a paged cache.  Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None)."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, sm_scale)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_PAGED_DENSE, 0, q.device, workspace)
+    _check(lib.ksa_paged_dense_decode(
+        ctypes.byref(prob), ctypes.byref(pg), _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool", k_pool.dtype, k_pool.shape),
+        _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
+        pws, nws, _stream(stream)), "ksa_paged_dense_decode")
     return out, lse

@@ -75,9 +75,28 @@ size_t workspace_for(const ksa_problem& p, int32_t op, int32_t param) {
       return plan_vote(d, param, 0).total;
     case KSA_OP_DENSE:
       return attention_workspace_bytes(d, plan_attention(d, 2, d.T));
+    case KSA_OP_PAGED_DENSE:
+      return attention_workspace_bytes(d, plan_attention(d, 3, (int64_t)d.NB * d.Bs));
     default:
       return SIZE_MAX;
   }
+}
+
+// The paged-cache description: pointers, strides and the pool's row count
+// (page ids are int32 row offsets: num_pages * Hkv * Bs < 2^31).
+ksa_status check_paged(const ksa_problem& p, const ksa_paged_kv* pg, PagedKv* out) {
+  if (!pg || !pg->block_table || !pg->seq_lens || !aligned4(pg->block_table) ||
+      !aligned4(pg->seq_lens))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (pg->max_blocks < 1 || pg->num_pages < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)pg->max_blocks * p.block_size != p.max_seq_len) return KSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)pg->num_pages * p.num_kv_heads * p.block_size >= ((int64_t)1 << 31))
+    return KSA_ERR_UNSUPPORTED;
+  out->table = pg->block_table;
+  out->seq_lens = pg->seq_lens;
+  out->max_blocks = pg->max_blocks;
+  out->num_pages = pg->num_pages;
+  return KSA_OK;
 }
 
 }  // namespace
@@ -101,10 +120,11 @@ const char* ksa_status_string(ksa_status status) {
 }
 
 size_t ksa_workspace_bytes(const ksa_problem* problem, int32_t op, int32_t param) {
-  const bool blocks = op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS;
+  const bool blocks =
+      op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS || op == KSA_OP_PAGED_DENSE;
   if (check_problem(problem, blocks) != KSA_OK) return SIZE_MAX;
-  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_DENSE) return SIZE_MAX;
-  if (op != KSA_OP_DENSE && param < 1) return SIZE_MAX;
+  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_PAGED_DENSE) return SIZE_MAX;
+  if (op != KSA_OP_DENSE && op != KSA_OP_PAGED_DENSE && param < 1) return SIZE_MAX;
   return workspace_for(*problem, op, param);
 }
 
@@ -218,6 +238,70 @@ ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, cons
   if (refresh_last_block && d.Bs > kStepMaxBs) return KSA_ERR_UNSUPPORTED;
   return from_hip(launch_block_topk_decode(d, q, k, v, summaries, keff, refresh_last_block, block_idx,
                                            out, lse, (hipStream_t)stream));
+}
+
+ksa_status ksa_paged_block_summaries(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                     const void* k_pool, void* summaries, int32_t first_block,
+                                     int32_t num_blocks, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!k_pool || !summaries || !aligned16(k_pool) || !aligned16(summaries))
+    return KSA_ERR_INVALID_ARGUMENT;
+  const bool newest = first_block == -1 && num_blocks == 1;
+  if (!newest &&
+      (first_block < 0 || num_blocks < 1 || (int64_t)first_block + num_blocks > pk.max_blocks))
+    return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_paged_block_summaries(d, pk, k_pool, summaries, first_block, num_blocks,
+                                               (hipStream_t)stream));
+}
+
+ksa_status ksa_paged_block_topk_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       void* summaries, int32_t top_k, int32_t refresh_last_block,
+                                       int32_t* block_idx, float* out, float* lse, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k_pool || !v_pool || !summaries || !out || top_k < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(summaries) ||
+      !aligned4(out) || (lse && !aligned4(lse)) || (block_idx && !aligned4(block_idx)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  const int keff_max = top_k < pk.max_blocks ? top_k : pk.max_blocks;
+  if (pk.max_blocks > kStepMaxBlocks || keff_max > kIdxStage) return KSA_ERR_UNSUPPORTED;
+  if ((int64_t)keff_max * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
+  if (refresh_last_block && d.Bs > kStepMaxBs) return KSA_ERR_UNSUPPORTED;
+  return from_hip(launch_block_topk_decode(d, q, k_pool, v_pool, summaries, top_k,
+                                           refresh_last_block, block_idx, out, lse,
+                                           (hipStream_t)stream, &pk));
+}
+
+ksa_status ksa_paged_dense_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                  const void* q, const void* k_pool, const void* v_pool, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k_pool || !v_pool || !out) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned4(out) ||
+      (lse && !aligned4(lse)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  const AttnPlan plan = plan_attention(d, 3, (int64_t)d.NB * d.Bs);
+  const size_t need = attention_workspace_bytes(d, plan);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_attention(d, 3, q, k_pool, v_pool, nullptr, 0, out, lse, workspace, plan,
+                                   (hipStream_t)stream, &pk));
 }
 
 }  // extern "C"

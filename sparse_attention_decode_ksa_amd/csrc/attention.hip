@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_partial
   const int split = blockIdx.x % a.splits;
   const int row = blockIdx.x / a.splits;
   const int e0 = stage_indices<KIND, CH>(a, row, split, s_idx);
-  attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, e0, KIND != 2);
+  attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, nullptr, e0, KIND != 2);
 }
 
 template <int G, int KIND>
@@ -30,7 +30,48 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   const int split = blockIdx.x % a.splits;
   const int row = blockIdx.x / a.splits;
   const int e0 = stage_indices<KIND, 16>(a, row, split, s_idx);
-  attn_row_mfma<G, KIND>(a, row, split, s_idx, e0, KIND != 2);
+  attn_row_mfma<G, KIND>(a, row, split, s_idx, nullptr, e0, KIND != 2);
+}
+
+#ifndef KSA_MFMA
+#define KSA_MFMA 1
+#endif
+
+// Dense attention over a paged cache: the row's length comes from seq_lens,
+// and the logical ids and pages of the blocks in this split's range are
+// staged in LDS (splits past a short row's end write an empty partial
+// state, which the merge weighs by zero).
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_dense_kernel(
+    AttnArgs a0) {
+  constexpr bool kMfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
+  constexpr int CH = kMfma ? 16 : (64 / (D / KV<T>::EPL)) * kLoadsPerChunk;
+  __shared__ int s_idx[kIdxStage];
+  __shared__ int s_pg[kIdxStage];
+  const int split = blockIdx.x % a0.splits;
+  const int row = blockIdx.x / a0.splits;
+  const int b = row / a0.d.Hkv;
+  const int Bs = a0.d.Bs;
+  AttnArgs a = a0;
+  const int Tb = min(max(a0.seq_lens[b], 1), a0.tstride * Bs);
+  const int nb = (Tb + Bs - 1) / Bs;
+  a.d.T = Tb;
+  a.ltot = nb * Bs;
+  a.count = nb;
+  const int nchunks = (a.ltot + CH - 1) / CH;
+  const int c_begin = split * a.cps;
+  const int c_end = min(c_begin + a.cps, nchunks);
+  const int e0 = (c_begin * CH) / Bs;
+  const int e1 = min(nb, (c_end * CH + Bs - 1) / Bs);
+  const int32_t* tb = a.table + (int64_t)b * a.tstride;
+  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) {
+    s_idx[i] = e0 + i;
+    s_pg[i] = tb[e0 + i];
+  }
+  if constexpr (kMfma)
+    attn_row_mfma<G, 3>(a, row, split, s_idx, s_pg, e0, true);
+  else
+    attn_row_valu<T, D, G, 3>(a, row, split, s_idx, s_pg, e0, true);
 }
 
 // Fixed-order merge of the split partial states of each row.
@@ -59,16 +100,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   }
 }
 
-#ifndef KSA_MFMA
-#define KSA_MFMA 1
-#endif
-
 template <typename T, int D, int G>
 hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStream_t s) {
   const int rows = a.d.B * a.d.Hkv;
   const dim3 grid(rows * p.splits), block(p.nw * 64);
   constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
-  if constexpr (mfma) {
+  if (kind == 3) {
+    hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G>), grid, block, 0, s, a);
+  } else if constexpr (mfma) {
     switch (kind) {
       case 0: hipLaunchKernelGGL((attn_mfma_kernel<G, 0>), grid, block, 0, s, a); break;
       case 1: hipLaunchKernelGGL((attn_mfma_kernel<G, 1>), grid, block, 0, s, a); break;
@@ -127,7 +166,7 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   // a workgroup's index slice must fit the LDS stage
   int64_t cap = INT64_MAX;
   if (kind == 1) cap = kIdxStage / ch;
-  if (kind == 0) cap = ((int64_t)(kIdxStage - 2) * d.Bs) / ch;
+  if (kind == 0 || kind == 3) cap = ((int64_t)(kIdxStage - 2) * d.Bs) / ch;
   if (cps > cap) cps = cap;
   if (cps < 1) cps = 1;
   splits = (chunks + cps - 1) / cps;
@@ -143,8 +182,13 @@ size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p) {
 
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse, void* workspace,
-                            const AttnPlan& plan, hipStream_t stream) {
-  const AttnArgs a = make_attn_args(d, kind, q, k, v, idx, count, out, lse, workspace, plan);
+                            const AttnPlan& plan, hipStream_t stream, const PagedKv* paged) {
+  AttnArgs a = make_attn_args(d, kind, q, k, v, idx, count, out, lse, workspace, plan);
+  if (paged) {
+    a.table = paged->table;
+    a.seq_lens = paged->seq_lens;
+    a.tstride = paged->max_blocks;
+  }
   if (d.dtype == KSA_BF16) {
     if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);
     return launch_g<uint16_t, 128>(a, kind, plan, stream);

@@ -48,7 +48,7 @@ struct StepArgs {
   AttnArgs a;          // attention over the selected blocks (ids come from LDS)
   void* summ;          // [B, Hkv, NBcap, D]; block (T-1)/Bs is rewritten on refresh
   int refresh;
-  int keff;
+  int keff;            // k_eff; paged: top_k (each row's k_eff is at most this)
   int32_t* block_idx;  // [B, Hkv, keff] or null
 };
 
@@ -61,8 +61,9 @@ constexpr int ref_stage_slots() {
   return ref > idx ? ref : idx;
 }
 
-// NW waves per workgroup (4 or 8).
-template <typename T, int D, int G, int NW>
+// NW waves per workgroup (4 or 8).  PAGED: K and V are page pools (the
+// attention's kind 3) and every row has its own length from seq_lens.
+template <typename T, int D, int G, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_topk_decode_kernel(
     StepArgs s) {
   constexpr int kStepThreads = NW * 64;
@@ -78,18 +79,32 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   __shared__ TopkShared s_topk;
   __shared__ int s_next;           // next free scoring unit
   __shared__ uint32_t s_lo, s_hi;  // range of the row's keys
+  __shared__ int s_pgbuf[PAGED ? kIdxStage : 1];  // pages of the selected blocks
   uint4* s_ref = s_buf;                        // step 2
   int* s_idx = reinterpret_cast<int*>(s_buf);  // steps 3-4
+  int* s_pg = PAGED ? s_pgbuf : nullptr;
 
-  const AttnArgs& a = s.a;
-  const Dims& d = a.d;
+  const Dims& d = s.a.d;
   const int row = blockIdx.x;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const int tid = threadIdx.x, li = tid % LPT, grp = tid / LPT;
-  const int NB = d.NB;
+  // the row's length, blocks and k_eff; for a paged cache the attention
+  // sees this row's length
+  AttnArgs a = s.a;
+  int keff = s.keff;
+  const int32_t* ptab = nullptr;
+  if constexpr (PAGED) {
+    a.d.T = min(max(a.seq_lens[b], 1), a.tstride * d.Bs);
+    a.d.NB = (a.d.T + d.Bs - 1) / d.Bs;
+    keff = min(s.keff, a.d.NB);
+    a.ltot = keff * d.Bs;
+    ptab = a.table + (int64_t)b * a.tstride;
+  }
+  const int Trow = a.d.T;
+  const int NB = a.d.NB;
   T* srow = (T*)s.summ + (int64_t)row * d.NBcap * D + li * EPL;
-  const int jref = s.refresh ? (d.T - 1) / d.Bs : -1;
-  const int nref = s.refresh ? d.T - jref * d.Bs : 0;
+  const int jref = s.refresh ? (Trow - 1) / d.Bs : -1;
+  const int nref = s.refresh ? Trow - jref * d.Bs : 0;
 
   // The refresh block's rows are loaded up front (branch-free: without a
   // refresh the row's first token stands in, unused) and consumed only
@@ -98,7 +113,11 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   {
     const int t0 = s.refresh ? jref * d.Bs : 0;
     const int last = s.refresh ? nref - 1 : 0;
-    const T* kp = (const T*)a.k + ((int64_t)row * d.Tcap + t0) * D + li * EPL;
+    const T* kp;
+    if constexpr (PAGED)  // the block's page; its rows start the page's KV-head slab
+      kp = (const T*)a.k + ((int64_t)ptab[max(jref, 0)] * d.Hkv + g) * d.Bs * D + li * EPL;
+    else
+      kp = (const T*)a.k + ((int64_t)row * d.Tcap + t0) * D + li * EPL;
 #pragma unroll
     for (int r = 0; r < RP; ++r) rr[r] = ld16(kp + (int64_t)min(grp + r * NGRP, last) * D);
   }
@@ -233,20 +252,26 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
 #pragma unroll
   for (int i = 0; i < kStepKPT; ++i) key[i] = (i < kpt && j0 + i < NB) ? s_keys[j0 + i] : 0u;
   int32_t* gidx = s.block_idx ? s.block_idx + (int64_t)row * s.keff : nullptr;
-  row_topk_range<kStepKPT>(key, kpt, j0, NB, s.keff, s_lo, s_hi, s_topk, [&](int rank, int j) {
+  row_topk_range<kStepKPT>(key, kpt, j0, NB, keff, s_lo, s_hi, s_topk, [&](int rank, int j) {
     s_idx[rank] = j;
+    if constexpr (PAGED) s_pg[rank] = ptab[j];
     if (gidx) gidx[rank] = j;
   });
+  if constexpr (PAGED) {  // ids past this row's k_eff
+    if (gidx)
+      for (int i = keff + tid; i < s.keff; i += kStepThreads) gidx[i] = -1;
+  }
   __syncthreads();
 
   // 4. attention over the selected blocks
+  constexpr int KIND = PAGED ? 3 : 0;
   if constexpr (kMfma)
-    attn_row_mfma<G, 0>(a, row, 0, s_idx, 0, false);
+    attn_row_mfma<G, KIND>(a, row, 0, s_idx, s_pg, 0, false);
   else
-    attn_row_valu<T, D, G, 0>(a, row, 0, s_idx, 0, false, qraw);
+    attn_row_valu<T, D, G, KIND>(a, row, 0, s_idx, s_pg, 0, false, qraw);
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool PAGED>
 hipError_t launch_g(const StepArgs& s, int rows, hipStream_t stream) {
   // Eight waves per row unless the rows outnumber the workgroups of eight
   // waves that fit on the chip at once: then four, so that more rows are in
@@ -254,8 +279,8 @@ hipError_t launch_g(const StepArgs& s, int rows, hipStream_t stream) {
   // eight-wave workgroups per CU: a property of the kernel, found once
   static const int resident8 = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_topk_decode_kernel<T, D, G, 8>, 512, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_topk_decode_kernel<T, D, G, 8, PAGED>,
+                                                     512, 0) != hipSuccess)
       n = 1;
     return n > 0 ? n : 1;
   }();
@@ -265,43 +290,58 @@ hipError_t launch_g(const StepArgs& s, int rows, hipStream_t stream) {
     cus = 256;
   const dim3 grid(rows);
   if ((int64_t)rows > (int64_t)resident8 * cus)
-    hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 4>), grid, dim3(256), 0, stream, s);
+    hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 4, PAGED>), grid, dim3(256), 0, stream, s);
   else
-    hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 8>), grid, dim3(512), 0, stream, s);
+    hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 8, PAGED>), grid, dim3(512), 0, stream, s);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 hipError_t launch_typed(const StepArgs& s, hipStream_t stream) {
   const int rows = s.a.d.B * s.a.d.Hkv;
   switch (s.a.d.G) {
-    case 1: return launch_g<T, D, 1>(s, rows, stream);
-    case 2: return launch_g<T, D, 2>(s, rows, stream);
-    case 4: return launch_g<T, D, 4>(s, rows, stream);
-    default: return launch_g<T, D, 8>(s, rows, stream);
+    case 1: return launch_g<T, D, 1, PAGED>(s, rows, stream);
+    case 2: return launch_g<T, D, 2, PAGED>(s, rows, stream);
+    case 4: return launch_g<T, D, 4, PAGED>(s, rows, stream);
+    default: return launch_g<T, D, 8, PAGED>(s, rows, stream);
   }
+}
+
+template <bool PAGED>
+hipError_t launch_dtype(const StepArgs& s, hipStream_t stream) {
+  const Dims& d = s.a.d;
+  if (d.dtype == KSA_BF16) {
+    if (d.D == 64) return launch_typed<uint16_t, 64, PAGED>(s, stream);
+    return launch_typed<uint16_t, 128, PAGED>(s, stream);
+  }
+  if (d.D == 64) return launch_typed<float, 64, PAGED>(s, stream);
+  return launch_typed<float, 128, PAGED>(s, stream);
 }
 
 }  // namespace
 
 hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k, const void* v,
                                     void* summaries, int keff, int refresh, int32_t* block_idx,
-                                    float* out, float* lse, hipStream_t stream) {
+                                    float* out, float* lse, hipStream_t stream,
+                                    const PagedKv* paged) {
+  // keff is the id stride; a paged call's rows select at most max_blocks
+  const int kplan = keff < d.NBcap ? keff : d.NBcap;
   const int ch = chunk_tokens(d);
-  const int nchunks = ceil_div((int64_t)keff * d.Bs, ch);
+  const int nchunks = ceil_div((int64_t)kplan * d.Bs, ch);
   const AttnPlan plan{kMaxWaves, 1, nchunks, ch};
   StepArgs s;
-  s.a = make_attn_args(d, 0, q, k, v, nullptr, keff, out, lse, nullptr, plan);
+  s.a = make_attn_args(d, 0, q, k, v, nullptr, kplan, out, lse, nullptr, plan);
   s.summ = summaries;
   s.refresh = refresh ? 1 : 0;
   s.keff = keff;
   s.block_idx = block_idx;
-  if (d.dtype == KSA_BF16) {
-    if (d.D == 64) return launch_typed<uint16_t, 64>(s, stream);
-    return launch_typed<uint16_t, 128>(s, stream);
+  if (paged) {
+    s.a.table = paged->table;
+    s.a.seq_lens = paged->seq_lens;
+    s.a.tstride = paged->max_blocks;
+    return launch_dtype<true>(s, stream);
   }
-  if (d.D == 64) return launch_typed<float, 64>(s, stream);
-  return launch_typed<float, 128>(s, stream);
+  return launch_dtype<false>(s, stream);
 }
 
 }  // namespace ksa

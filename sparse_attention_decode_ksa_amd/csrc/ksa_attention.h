@@ -66,10 +66,17 @@ struct AttnArgs {
   float* lse;
   float* part_acc; // [rows, splits, G, D]
   float* part_ml;  // [rows, splits, G, 2]
+  // paged cache (kind 3): pages of each sequence's logical blocks, lengths
+  const int32_t* table;    // [B, tstride]
+  const int32_t* seq_lens; // [B]
+  int tstride;             // max_blocks
+  int page_rows;           // Hkv * Bs: token rows per page
 };
 
 // Kernel arguments of one attention call (host side).  kind: 0 = selected
-// blocks, 1 = shared token list, 2 = dense range [0, T).
+// blocks, 1 = shared token list, 2 = dense range [0, T), 3 = blocks of a
+// paged cache (logical ids and their pages staged in LDS; the per-row
+// length is set by the kernel).
 inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const void* k, const void* v,
                                const int32_t* idx, int count, float* out, float* lse,
                                void* workspace, const AttnPlan& plan) {
@@ -80,9 +87,9 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.idx = idx;
   a.count = count;
   a.d = d;
-  a.ltot = kind == 0 ? count * d.Bs : (kind == 1 ? count : d.T);
+  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs : (kind == 1 ? count : d.T);
   a.bs_shift = -1;
-  if (kind == 0 && (d.Bs & (d.Bs - 1)) == 0) {
+  if ((kind == 0 || kind == 3) && (d.Bs & (d.Bs - 1)) == 0) {
     int sh = 0;
     while ((1 << sh) < d.Bs) ++sh;
     a.bs_shift = sh;
@@ -95,14 +102,20 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   const size_t rows = (size_t)d.B * d.Hkv;
   a.part_acc = (float*)workspace;
   a.part_ml = workspace ? a.part_acc + rows * plan.splits * d.G * d.D : nullptr;
+  a.table = nullptr;
+  a.seq_lens = nullptr;
+  a.tstride = 0;
+  a.page_rows = d.Hkv * d.Bs;
   return a;
 }
 
-// Token ids of the NI rows a lane loads for chunk c.  Indices of the
-// workgroup's range are staged in LDS (s_idx, entries from e0 on).
+// Token rows of the NI rows a lane loads for chunk c (token ids; for a paged
+// cache, rows page * page_rows + r of the pool seen from the KV head's first
+// row).  Indices of the workgroup's range are staged in LDS (s_idx, entries
+// from e0 on; pages in s_pg for kind 3).
 template <int KIND, int CH, int SPW, int NI>
-__device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_idx, int e0, int slot,
-                                              int c, int* tok, bool* ok) {
+__device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_idx, const int* s_pg,
+                                              int e0, int slot, int c, int* tok, bool* ok) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int p = c * CH + i * SPW + slot;
@@ -127,7 +140,10 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_id
       const int blk = ok[i] ? s_idx[at] : 0;
       const int t = blk * a.d.Bs + r;
       ok[i] = ok[i] && t < a.d.T;
-      tok[i] = ok[i] ? t : 0;
+      if constexpr (KIND == 3)
+        tok[i] = ok[i] ? s_pg[at] * a.page_rows + r : 0;
+      else
+        tok[i] = ok[i] ? t : 0;
     }
   }
 }
@@ -142,11 +158,11 @@ __device__ __forceinline__ uint4 ld_kv(const T* p) {
 }
 
 template <typename T, int D, int KIND, int CH, int SPW, int NI>
-__device__ __forceinline__ void load_chunk(const AttnArgs& a, const int* s_idx, int e0, int slot,
-                                           int c, const T* kbase, const T* vbase, uint4* kr,
-                                           uint4* vr, bool* okr) {
+__device__ __forceinline__ void load_chunk(const AttnArgs& a, const int* s_idx, const int* s_pg,
+                                           int e0, int slot, int c, const T* kbase,
+                                           const T* vbase, uint4* kr, uint4* vr, bool* okr) {
   int tok[NI];
-  resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, e0, slot, c, tok, okr);
+  resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, s_pg, e0, slot, c, tok, okr);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     kr[i] = ld_kv(kbase + (int64_t)tok[i] * D);
@@ -268,7 +284,8 @@ __device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int spl
 // rows (already loaded by the caller in this lane layout).
 template <typename T, int D, int G, int KIND>
 __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int split, const int* s_idx,
-                                              int e0, bool sync, const uint4* qraw = nullptr) {
+                                              const int* s_pg, int e0, bool sync,
+                                              const uint4* qraw = nullptr) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int SPW = 64 / LPT;
@@ -284,7 +301,8 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   const int nw = blockDim.x >> 6;
   const int slot = lane / LPT, li = lane % LPT;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const int64_t kvrow = (int64_t)row * d.Tcap * D + li * EPL;
+  const int64_t kvrow =
+      (KIND == 3 ? (int64_t)g * d.Bs * D : (int64_t)row * d.Tcap * D) + li * EPL;
   const T* kbase = (const T*)a.k + kvrow;
   const T* vbase = (const T*)a.v + kvrow;
 
@@ -318,8 +336,8 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
 #pragma unroll
   for (int s = 0; s < P; ++s)
     if (s < my_n)
-      load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, e0, slot, c0 + s * nw, kbase, vbase, kb[s],
-                                          vb[s], okb[s]);
+      load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, s_pg, e0, slot, c0 + s * nw, kbase, vbase,
+                                          kb[s], vb[s], okb[s]);
   for (int j0 = 0; j0 < my_n; j0 += P) {
 #pragma unroll
     for (int s = 0; s < P; ++s) {
@@ -334,8 +352,8 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
           okc[i] = okb[s][i];
         }
         if (j + P < my_n)
-          load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, e0, slot, c0 + (j + P) * nw, kbase, vbase,
-                                              kb[s], vb[s], okb[s]);
+          load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, s_pg, e0, slot, c0 + (j + P) * nw, kbase,
+                                              vbase, kb[s], vb[s], okb[s]);
         compute_chunk<T, D, G, NI, LPT>(qv, kc, vc, okc, m, l, acc);
       }
     }
@@ -394,7 +412,7 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
 // G in {4, 8}); indices staged as for attn_row_valu.
 template <int G, int KIND>
 __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int split, const int* s_idx,
-                                              int e0, bool sync) {
+                                              const int* s_pg, int e0, bool sync) {
   constexpr int D = 128;
   constexpr int EPL = 8;
   constexpr int LPT = 16;
@@ -413,7 +431,7 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
   const int r = lane & 15, kg = lane >> 4;  // MFMA: row/column and k-group / row quad
   const int slot = kg, li = r;             // V layout: token slot and 16-byte piece
   const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const int64_t kvrow = (int64_t)row * d.Tcap * D;
+  const int64_t kvrow = KIND == 3 ? (int64_t)g * d.Bs * D : (int64_t)row * d.Tcap * D;
   const uint16_t* kbase = (const uint16_t*)a.k + kvrow + 8 * kg;
   const uint16_t* vbase = (const uint16_t*)a.v + kvrow + li * EPL;
 
@@ -445,13 +463,13 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
   auto load = [&](int c, uint4* kr, uint4* vr, bool& okk) {
     int tk[1];
     bool ok1[1];
-    resolve_chunk<KIND, CH, 1, 1>(a, s_idx, e0, r, c, tk, ok1);  // position c*16 + r
+    resolve_chunk<KIND, CH, 1, 1>(a, s_idx, s_pg, e0, r, c, tk, ok1);  // position c*16 + r
     okk = ok1[0];
 #pragma unroll
     for (int i = 0; i < NI; ++i) kr[i] = ld_kv(kbase + (int64_t)tk[0] * D + 32 * i);
     int tv[NI];
     bool okv[NI];
-    resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, e0, slot, c, tv, okv);
+    resolve_chunk<KIND, CH, SPW, NI>(a, s_idx, s_pg, e0, slot, c, tv, okv);
 #pragma unroll
     for (int i = 0; i < NI; ++i) vr[i] = ld_kv(vbase + (int64_t)tv[i] * D);
   };

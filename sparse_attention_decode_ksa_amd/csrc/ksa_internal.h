@@ -47,14 +47,29 @@ struct AttnPlan {
 AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row);
 size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p);
 
+// A paged cache (device table and lengths, see ksa_paged_kv).
+struct PagedKv {
+  const int32_t* table;
+  const int32_t* seq_lens;
+  int max_blocks;
+  int num_pages;
+};
+
 // Attention over a row-wise token list.  kind: 0 = selected blocks,
-// 1 = shared token list, 2 = dense range [0, T).
+// 1 = shared token list, 2 = dense range [0, T), 3 = dense over a paged
+// cache (`paged` given; d.T is the longest sequence).
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse,
-                            void* workspace, const AttnPlan& plan, hipStream_t stream);
+                            void* workspace, const AttnPlan& plan, hipStream_t stream,
+                            const PagedKv* paged = nullptr);
 
 hipError_t launch_block_summaries(const Dims& d, const void* k, void* summaries, int first_block,
                                   int num_blocks, hipStream_t stream);
+// Paged: blocks [first, first + num) below each sequence's NB_b, or each
+// sequence's newest block when first_block < 0.
+hipError_t launch_paged_block_summaries(const Dims& d, const PagedKv& p, const void* k_pool,
+                                        void* summaries, int first_block, int num_blocks,
+                                        hipStream_t stream);
 
 constexpr int kSelectMaxBlocks = 15360;  // a row's keys fit the registers of one top-k workgroup
 size_t select_workspace_bytes(const Dims& d);
@@ -67,7 +82,8 @@ constexpr int kStepMaxBlocks = 4096;  // blocks per row whose keys the step keep
 constexpr int kStepMaxBs = 64;        // largest block size the step refreshes
 hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k, const void* v,
                                     void* summaries, int keff, int refresh, int32_t* block_idx,
-                                    float* out, float* lse, hipStream_t stream);
+                                    float* out, float* lse, hipStream_t stream,
+                                    const PagedKv* paged = nullptr);
 
 // Vote-union selection.
 struct VotePlan {

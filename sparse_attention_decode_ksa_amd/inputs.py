@@ -190,6 +190,32 @@ def integer_inputs(w: Workload, lo: int = -2, hi: int = 2, device="cpu", seed: O
     return {"q": q, "k": k, "v": v}
 
 
+def to_paged(k: torch.Tensor, v: torch.Tensor, block_size: int, seed: int = 0,
+             spare_pages: int = 0):
+    """Store contiguous caches k, v [B, Hkv, cap, D] as page pools
+    [num_pages, Hkv, Bs, D] (cap a multiple of Bs) with a seeded random page
+    order: block j of sequence b goes to page block_table[b, j].  Returns
+    (k_pool, v_pool, block_table [B, cap/Bs] int32); the pool has
+    `spare_pages` extra pages of noise that no sequence uses.  Only moves
+    bytes: the paged cache holds exactly the contiguous cache's tokens."""
+    B, Hkv, cap, D = k.shape
+    if cap % block_size:
+        raise ValueError("cap must be a multiple of the block size")
+    nbc = cap // block_size
+    num_pages = B * nbc + spare_pages
+    gen = torch.Generator(device=k.device)
+    gen.manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=gen, device=k.device)
+    table = perm[: B * nbc].view(B, nbc).to(torch.int32).contiguous()
+    pools = []
+    for x in (k, v):
+        pool = _normal(gen, (num_pages, Hkv, block_size, D), k.device).to(x.dtype)
+        blocks = x.view(B, Hkv, nbc, block_size, D).permute(0, 2, 1, 3, 4)  # [B, nbc, Hkv, Bs, D]
+        pool[table.view(-1).long()] = blocks.reshape(B * nbc, Hkv, block_size, D)
+        pools.append(pool)
+    return pools[0], pools[1], table
+
+
 def as_numpy_bits(t: torch.Tensor):
     """CPU numpy view of a tensor's exact bytes: float32 stays float32, bf16
     becomes its uint16 bit patterns (the form the oracle takes)."""

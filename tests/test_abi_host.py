@@ -151,3 +151,50 @@ def test_binding_rejects_cpu_tensors():
     k = torch.zeros(1, 1, 16, 64)
     with pytest.raises(ValueError):
         ksa.ksa_dense_decode(q, k, k, 16)
+
+
+def test_paged_validation():
+    """The paged calls check the cache description on the host: table and
+    lengths present and aligned, max_seq_len == max_blocks * Bs, a pool whose
+    rows fit int32 offsets; the step keeps the fused step's limits."""
+    lib = ksa.load_library()
+    null = None
+    E = ksa.KSA_ERR_INVALID_ARGUMENT
+    U = ksa.KSA_ERR_UNSUPPORTED
+    FA = ctypes.c_void_p(0x10000)
+
+    def pg(max_blocks=64, num_pages=200, table=FA, lens=FA):
+        return ksa.PagedKv(table, lens, max_blocks, num_pages)
+
+    def step(p, g, top_k=4, refresh=1):
+        return lib.ksa_paged_block_topk_decode(ctypes.byref(p), ctypes.byref(g) if g else None,
+                                               FAKE, FAKE, FAKE, FAKE, top_k, refresh, null,
+                                               FAKE, null, null)
+
+    def summ(p, g, first=0, num=1):
+        return lib.ksa_paged_block_summaries(ctypes.byref(p), ctypes.byref(g), FAKE, FAKE, first,
+                                             num, null)
+
+    def dense(p, g, nws=0):
+        return lib.ksa_paged_dense_decode(ctypes.byref(p), ctypes.byref(g), FAKE, FAKE, FAKE, FAKE,
+                                          null, null, nws, null)
+
+    p = P()  # Tcap 1024 = 64 blocks of 16
+    assert step(p, None) == E
+    assert step(p, pg(table=null)) == E
+    assert step(p, pg(lens=ctypes.c_void_p(0x10002))) == E
+    assert step(p, pg(max_blocks=63)) == E              # max_seq_len must be max_blocks * Bs
+    assert step(p, pg(num_pages=0)) == E
+    assert step(p, pg(), top_k=0) == E
+    assert step(P(Bs=65, T=65 * 64, Tcap=65 * 64), pg()) == U          # refresh needs Bs <= 64
+    assert step(P(T=4097 * 16, Tcap=4097 * 16), pg(max_blocks=4097)) == U
+    assert step(P(Hkv=2), pg(num_pages=1 << 26)) == U   # pool rows beyond int32
+    assert summ(p, pg(), first=-1, num=2) == E           # -1 selects the newest block only
+    assert summ(p, pg(), first=60, num=5) == E
+    assert summ(p, pg(), first=-2) == E
+    # paged dense needs a workspace when it splits rows
+    need = ksa.ksa_workspace_bytes(P(B=1, Hkv=1, Hq=1, T=1 << 15, Tcap=1 << 15),
+                                   ksa.KSA_OP_PAGED_DENSE, 0)
+    assert need > 0
+    assert dense(P(B=1, Hkv=1, Hq=1, T=1 << 15, Tcap=1 << 15), pg(max_blocks=2048)) == \
+        ksa.KSA_ERR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,169 @@
+"""GPU parity of the paged-cache calls: ksa_paged_block_summaries,
+ksa_paged_block_topk_decode and ksa_paged_dense_decode.
+
+Pools come from the seeded contiguous inputs through to_paged (a random page
+order plus spare pages of noise); every sequence has its own length.  Each
+sequence is checked against the oracle on its own tokens, gathered from the
+pool by oracle.gather_pages, under the acceptance rules of tests/parity.py.
+With one length for the whole batch the paged calls must reproduce the
+contiguous calls bit for bit (the same arithmetic on the same tokens).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_decode_ksa_amd as ksa
+from sparse_attention_decode_ksa_amd.inputs import small_workload, to_paged
+from parity import check_attention, check_block_selection
+from test_gpu_parity import DEV, gpu_inputs, np_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def paged_inputs(lens, Bs, seed, **kw):
+    nbmax = max(ksa.nblocks(t, Bs) for t in lens) + 1
+    w = small_workload(B=len(lens), T=max(lens), Tcap=nbmax * Bs, Bs=Bs, seed=seed, **kw)
+    q, k, v = gpu_inputs(w)
+    kp, vp, table = to_paged(k, v, Bs, seed=seed + 1, spare_pages=3)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return w, q, k, v, kp, vp, table, seq
+
+
+def gathered(pool, table, b, T, Bs):
+    return oracle.gather_pages(np_bits(pool), table.cpu().numpy(), b, T, Bs)
+
+
+PAGED_CASES = [
+    dict(lens=[1000, 17, 1, 512], Bs=16, Hq=4, Hkv=2, D=64, dtype="bf16", top_k=8),
+    dict(lens=[3000, 2048, 777], Bs=16, Hq=8, Hkv=1, D=128, dtype="bf16", top_k=64),   # MFMA G = 8
+    dict(lens=[4099, 64, 2000], Bs=32, Hq=16, Hkv=4, D=128, dtype="bf16", top_k=20),   # MFMA G = 4
+    dict(lens=[517, 200, 7], Bs=7, Hq=2, Hkv=2, D=64, dtype="bf16", top_k=30),         # Bs not 2^n
+    dict(lens=[1025, 1024, 33], Bs=16, Hq=4, Hkv=2, D=128, dtype="f32", top_k=12),     # T-1 opens a block
+    dict(lens=[200, 150], Bs=1, Hq=4, Hkv=4, D=128, dtype="f32", top_k=17),            # one-token pages
+]
+
+
+def case_id(c):
+    return "%s-G%d-D%d-Bs%d-k%d-%s" % (c["dtype"], c["Hq"] // c["Hkv"], c["D"], c["Bs"], c["top_k"],
+                                       "_".join(map(str, c["lens"])))
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=case_id)
+def test_paged_summaries_match_oracle_per_sequence(case):
+    c = dict(case)
+    lens, Bs = c.pop("lens"), c.pop("Bs")
+    c.pop("top_k")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=lens[0], **c)
+    s = torch.full((w.B, w.Hkv, table.shape[1], w.D), 7, dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    got = np_bits(s)
+    for b, T in enumerate(lens):
+        nb = ksa.nblocks(T, Bs)
+        ref = oracle.block_summaries(gathered(kp, table, b, T, Bs), T, Bs)
+        np.testing.assert_array_equal(got[b:b + 1, :, :nb], ref[:, :, :nb])
+        assert np.all(s[b, :, nb:].float().cpu().numpy() == 7)  # past the sequence: untouched
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=case_id)
+def test_paged_step_matches_oracle_per_sequence(case):
+    c = dict(case)
+    lens, Bs, top_k = c.pop("lens"), c.pop("Bs"), c.pop("top_k")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=lens[-1] + 11, **c)
+    s = torch.empty((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    # the newest block of every sequence holds stale values until the refresh
+    for b, T in enumerate(lens):
+        s[b, :, (T - 1) // Bs] = (torch.randn(s[b, :, 0].shape, device=DEV) * 3).to(s.dtype)
+    out, lse, idx = ksa.ksa_paged_block_topk_decode(q, kp, vp, s, table, seq, top_k,
+                                                    want_block_idx=True)
+    torch.cuda.synchronize()
+    got_s, ids = np_bits(s), idx.cpu().numpy()
+    for b, T in enumerate(lens):
+        nb = ksa.nblocks(T, Bs)
+        keff = min(top_k, nb)
+        kb, vb = gathered(kp, table, b, T, Bs), gathered(vp, table, b, T, Bs)
+        qb = np_bits(q[b:b + 1])
+        sb = oracle.block_summaries(kb, T, Bs)
+        np.testing.assert_array_equal(got_s[b:b + 1, :, :nb], sb[:, :, :nb])
+        assert np.all(ids[b, :, keff:] == -1)
+        raw, _ = oracle.group_scores(qb, sb, T, Bs)
+        ib = ids[b:b + 1, :, :keff]
+        check_block_selection(ib.reshape(w.Hkv, -1), raw.reshape(w.Hkv, -1), top_k)
+        ro, rl = oracle.attend_blocks(qb, kb, vb, T, Bs, ib)
+        check_attention(out[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("case", PAGED_CASES[:3] + PAGED_CASES[4:5], ids=case_id)
+def test_paged_dense_matches_oracle_per_sequence(case):
+    c = dict(case)
+    lens, Bs = c.pop("lens"), c.pop("Bs")
+    c.pop("top_k")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=lens[1] + 5, **c)
+    out, lse = ksa.ksa_paged_dense_decode(q, kp, vp, table, seq)
+    torch.cuda.synchronize()
+    for b, T in enumerate(lens):
+        ro, rl = oracle.attend_dense(np_bits(q[b:b + 1]), gathered(kp, table, b, T, Bs),
+                                     gathered(vp, table, b, T, Bs), T)
+        check_attention(out[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("G,D,dtype,Bs,T", [(2, 128, "bf16", 16, 5000), (4, 128, "bf16", 32, 4097),
+                                             (8, 128, "bf16", 16, 3001), (1, 64, "f32", 16, 999)])
+def test_paged_step_equals_contiguous_step_bitwise(G, D, dtype, Bs, T):
+    """One length for the whole batch: summaries, ids, out and lse of the paged
+    step are bitwise those of the contiguous step on the same tokens, and the
+    paged dense call agrees with the contiguous one to fp32 merge order."""
+    w, q, k, v, kp, vp, table, seq = paged_inputs([T] * 6, Bs, seed=T, Hq=2 * G, Hkv=2, D=D,
+                                                  dtype=dtype)
+    nbc = table.shape[1]
+    s_c = torch.empty((w.B, w.Hkv, nbc, w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_block_summaries(k, s_c, T - 1, Bs) if T > 1 else None
+    s_c[:, :, (T - 1) // Bs] = 0
+    s_p = s_c.clone()
+    oc, lc, ic = ksa.ksa_block_topk_decode(q, k, v, s_c, T, Bs, 24, want_block_idx=True)
+    op, lp, ip = ksa.ksa_paged_block_topk_decode(q, kp, vp, s_p, table, seq, 24, max_len=T,
+                                                 want_block_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s_c, s_p)
+    assert torch.equal(ic, ip[:, :, :ic.shape[2]])
+    assert torch.equal(oc, op) and torch.equal(lc, lp)
+    dc, dlc = ksa.ksa_dense_decode(q, k, v, T)
+    dp, dlp = ksa.ksa_paged_dense_decode(q, kp, vp, table, seq, max_len=T)
+    torch.cuda.synchronize()
+    assert float((dc - dp).abs().max()) <= 1e-5 and float((dlc - dlp).abs().max()) <= 1e-5
+
+
+def test_paged_step_without_refresh_keeps_summaries():
+    w, q, k, v, kp, vp, table, seq = paged_inputs([700, 300, 90], 16, seed=70, Hq=4, Hkv=2, D=64,
+                                                  dtype="bf16")
+    s = torch.empty((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    before = s.clone()
+    out, lse, idx = ksa.ksa_paged_block_topk_decode(q, kp, vp, s, table, seq, 10,
+                                                    refresh_last_block=False, want_block_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s, before)
+    for b, T in enumerate([700, 300, 90]):
+        kb = gathered(kp, table, b, T, 16)
+        sb = oracle.block_summaries(kb, T, 16)
+        raw, _ = oracle.group_scores(np_bits(q[b:b + 1]), sb, T, 16)
+        keff = min(10, ksa.nblocks(T, 16))
+        ib = idx[b].cpu().numpy()
+        assert np.all(ib[:, keff:] == -1)
+        check_block_selection(ib[:, :keff], raw.reshape(w.Hkv, -1), 10)
+
+
+def test_paged_newest_block_refresh_only():
+    """first_block = -1 rewrites each sequence's own newest block and nothing else."""
+    lens = [100, 33, 64]
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, 16, seed=9, Hq=4, Hkv=2, D=128, dtype="bf16")
+    s = torch.full((w.B, w.Hkv, table.shape[1], w.D), 3, dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq, newest_only=True)
+    got = np_bits(s)
+    for b, T in enumerate(lens):
+        j = (T - 1) // 16
+        ref = oracle.block_summaries(gathered(kp, table, b, T, 16), T, 16)
+        np.testing.assert_array_equal(got[b, :, j], ref[0, :, j])
+        others = [i for i in range(table.shape[1]) if i != j]
+        assert np.all(s[b, :, others].float().cpu().numpy() == 3)

@@ -411,3 +411,21 @@ def test_kv_byte_accounting_matches_the_pages_sizes():
     per_gpu = ts["batch"] * ts["context_tokens"] * per_tok / ts["gpus_per_node"]
     assert abs(per_gpu / 1e9 - 34.36) < 0.01
     assert ts["batch"] // ts["gpus_per_node"] == 256
+
+
+def test_gather_pages_reads_each_token_from_its_page():
+    """Every element of the pool encodes (page, head, slot, channel); the
+    gathered sequence must hold, at token t, slot t % Bs of page
+    table[b, t // Bs], and stop at T."""
+    rng = np.random.default_rng(0)
+    num_pages, Hkv, Bs, D = 11, 2, 4, 3
+    pool = np.fromfunction(lambda p, h, s, c: p * 1000 + h * 100 + s * 10 + c,
+                           (num_pages, Hkv, Bs, D)).astype(np.float32)
+    table = rng.permutation(num_pages)[:8].reshape(2, 4).astype(np.int32)
+    T = 13
+    seq = oracle.gather_pages(pool, table, 1, T, Bs)
+    assert seq.shape == (1, Hkv, T, D)
+    for h in range(Hkv):
+        for t in range(T):
+            for c in range(D):
+                assert seq[0, h, t, c] == table[1, t // Bs] * 1000 + h * 100 + (t % Bs) * 10 + c
