@@ -32,6 +32,7 @@ more per step than plain launches on MI355X, so region 1 is the headline.
 Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--path fused|calls]
+    python bench.py --paged uniform|ragged [--workload c2|c3|c5]  # the step on a paged cache
     python bench.py --copy-probe      # a plain 1 GiB copy, to calibrate HBM counters
 """
 from __future__ import annotations
@@ -64,6 +65,9 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    ap.add_argument("--paged", default="none", choices=["none", "uniform", "ragged"],
+                    help="block top-k step on a paged cache (random page order): every "
+                         "sequence at T, or lengths drawn in [T/2, T]")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of 1 GiB (counter calibration)")
     ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -201,6 +205,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.paged != "none":
+        paged_main(args)
         return
     if args.counter_summary:
         counter_summary(args)
@@ -479,6 +486,133 @@ def main():
     if vote:
         line["sparse_layer_step"] = {"ms": round(ms_attn, 5), "value": round(B / (ms_attn * 1e-3), 1),
                                      "speedup_vs_dense": round(ms_dense / ms_attn, 3)}
+    print(json.dumps(line), flush=True)
+
+
+def paged_main(args):
+    """The block top-k decode step on a paged cache: every layer's K and V are
+    stored as page pools in a seeded random page order (to_paged), each
+    sequence has its own length (all T, or drawn in [T/2, T]), and the step
+    is one ksa_paged_block_topk_decode launch; dense is ksa_paged_dense_decode."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_decode_ksa_amd as ksa
+    from sparse_attention_decode_ksa_amd.inputs import WORKLOADS, make_inputs, to_paged
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = ksa.load_library()
+    R = Runner(lib, ksa)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    assert w.plant == "blocks", "--paged runs the block top-k workloads"
+    B, Hq, Hkv, D, T, Bs, K = w.B, w.Hq, w.Hkv, w.D, w.T, w.Bs, w.top_k
+    elt = 2 if w.dtype == "bf16" else 4
+    rows = B * Hkv
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed * 7 + 1)
+    if args.paged == "ragged":
+        lens = torch.randint(T // 2, T + 1, (B,), generator=gen).tolist()
+    else:
+        lens = [T] * B
+    nbc = (T + Bs - 1) // Bs
+    touched = rows * (nbc + 2 * K * Bs) * D * elt
+    layers = args.layers or max(4, min(8, math.ceil(1.0e9 / touched)))
+    t0 = time.time()
+    L = []
+    for l in range(layers):
+        x = make_inputs(w, device=dev, seed=w.seed * 1000 + l)
+        kp, vp, table = to_paged(x["k"], x["v"], Bs, seed=w.seed * 1000 + l + 1)
+        del x["k"], x["v"]
+        x.update(kp=kp, vp=vp, table=table,
+                 seq=torch.tensor(lens, dtype=torch.int32, device=dev),
+                 s=torch.empty((B, Hkv, table.shape[1], D), dtype=kp.dtype, device=dev),
+                 out=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
+                 lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
+                 idx=torch.empty((B, Hkv, K), dtype=torch.int32, device=dev),
+                 dout=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
+                 dlse=torch.empty((B, Hq), dtype=torch.float32, device=dev))
+        ksa.ksa_paged_block_summaries(x["kp"], x["s"], x["table"], x["seq"], max_len=T)
+        L.append(x)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    prob = ksa.Problem(B, Hq, Hkv, D, T, L[0]["table"].shape[1] * Bs, Bs,
+                       ksa.KSA_BF16 if elt == 2 else ksa.KSA_F32, 0.0)
+    pp = ctypes.byref(prob)
+    stream = torch.cuda.Stream(device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = lambda t: ctypes.c_void_p(t.data_ptr())
+    wsd = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_PAGED_DENSE, 0), dev)
+    for x in L:
+        x["pg"] = ksa.PagedKv(V(x["table"]).value, V(x["seq"]).value, x["table"].shape[1],
+                              x["kp"].shape[0])
+        pg = ctypes.byref(x["pg"])
+        x["step"] = (lib.ksa_paged_block_topk_decode,
+                     (pp, pg, V(x["q"]), V(x["kp"]), V(x["vp"]), V(x["s"]), K, 1, V(x["idx"]),
+                      V(x["out"]), V(x["lse"]), sp))
+        x["dense"] = (lib.ksa_paged_dense_decode,
+                      (pp, pg, V(x["q"]), V(x["kp"]), V(x["vp"]), V(x["dout"]), V(x["dlse"]),
+                       V(wsd), wsd.numel(), sp))
+
+    def step(i):
+        R.run(L[i % layers]["step"])
+
+    def dense_only(i):
+        R.run(L[i % layers]["dense"])
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        ms_step = timed(torch, stream, args.steps, step)
+        dense_only(0)
+        ms_dense = timed(torch, stream, args.dense_steps, dense_only)
+
+    # algorithmic bytes of one step, from each row's length and its selected blocks
+    x = L[0]
+    ids = x["idx"].cpu().numpy().reshape(B, Hkv, K)
+    tl = np.array(lens)
+    nb = (tl + Bs - 1) // Bs
+    sel_tok = 0
+    for b in range(B):
+        for g in range(Hkv):
+            j = ids[b, g][ids[b, g] >= 0]
+            sel_tok += int(np.minimum(Bs, tl[b] - j * Bs).sum())
+    last_tok = int((tl - (nb - 1) * Bs).sum()) * Hkv
+    q_bytes = B * Hq * D * elt
+    out_bytes = B * Hq * (D + 1) * 4
+    step_bytes = (int(nb.sum()) * Hkv * D * elt            # summaries scored
+                  + last_tok * D * elt + rows * D * elt      # newest block refreshed
+                  + sel_tok * D * elt * 2                    # selected K and V
+                  + 2 * q_bytes + out_bytes + int(np.minimum(K, nb).sum()) * Hkv * 8 + B * 4)
+    dense_bytes = int(tl.sum()) * Hkv * D * elt * 2 + q_bytes + out_bytes
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    cfg = {"workload": "%s: %s" % (w.name, w.description), "batch": B, "q_heads": Hq,
+           "kv_heads": Hkv, "head_dim": D, "context": T, "layers_cycled": layers,
+           "block_size": Bs, "top_k_blocks": K, "paged": args.paged,
+           "seq_len_mean": round(float(tl.mean()), 1), "seq_len_min": int(tl.min()),
+           "pages_per_layer": int(L[0]["kp"].shape[0])}
+    line = {
+        "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
+        "value": round(B / (ms_step * 1e-3), 1), "unit": "seqs*steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if elt == 2 else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q with planted structure), paged in a random page order",
+        "config": cfg, "step_bytes": step_bytes,
+        "dense": {"ms_per_step": round(ms_dense, 5), "value": round(B / (ms_dense * 1e-3), 1),
+                  "gbps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)},
+        "speedup_vs_dense": round(ms_dense / ms_step, 3),
+        "roofline": {"kernel": "ksa_paged_block_topk_decode (refresh + score + top-k + attention, "
+                               "one launch)", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "avg_launch_ms": round(ms_step, 5),
+                     "bytes_per_launch": step_bytes},
+        "cpu_baseline": None,
+        "input_gen_s": round(gen_s, 2),
+    }
     print(json.dumps(line), flush=True)
 
 

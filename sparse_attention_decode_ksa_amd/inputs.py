@@ -207,11 +207,14 @@ def to_paged(k: torch.Tensor, v: torch.Tensor, block_size: int, seed: int = 0,
     gen.manual_seed(seed)
     perm = torch.randperm(num_pages, generator=gen, device=k.device)
     table = perm[: B * nbc].view(B, nbc).to(torch.int32).contiguous()
+    spare = perm[B * nbc:].long()
     pools = []
     for x in (k, v):
-        pool = _normal(gen, (num_pages, Hkv, block_size, D), k.device).to(x.dtype)
+        pool = torch.empty((num_pages, Hkv, block_size, D), dtype=x.dtype, device=k.device)
         blocks = x.view(B, Hkv, nbc, block_size, D).permute(0, 2, 1, 3, 4)  # [B, nbc, Hkv, Bs, D]
         pool[table.view(-1).long()] = blocks.reshape(B * nbc, Hkv, block_size, D)
+        if spare_pages:
+            pool[spare] = _normal(gen, (spare_pages, Hkv, block_size, D), k.device).to(x.dtype)
         pools.append(pool)
     return pools[0], pools[1], table
 
