@@ -256,6 +256,51 @@ ksa_status ksa_paged_dense_decode(const ksa_problem* problem, const ksa_paged_kv
                                   const void* q, const void* k_pool, const void* v_pool, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * Selection variants (the ablations the pages report) and a quality signal.
+ *
+ * ksa_select_topk_ex -- ksa_select_topk with options:
+ *   aggregate KSA_AGG_SUM ranks a block by the group's summed relevance (the
+ *     method, as ksa_select_topk); KSA_AGG_MAX by its largest single-head
+ *     relevance max_h q_h . summaries[b,g,j,:] (block_scores then holds
+ *     sm_scale * that maximum);
+ *   force_last_block != 0 always keeps block (T-1)/Bs (the local block,
+ *     Kinetics explainer, section 五, local attention) and ranks the others
+ *     for the remaining k_eff - 1 places.
+ * Same outputs, limits and workspace as ksa_select_topk. */
+typedef enum { KSA_AGG_SUM = 0, KSA_AGG_MAX = 1 } ksa_group_agg;
+typedef struct {
+  int32_t top_k;             /* >= 1 */
+  ksa_group_agg aggregate;
+  int32_t force_last_block;
+} ksa_select_options;
+ksa_status ksa_select_topk_ex(const ksa_problem* problem, const void* q, const void* summaries,
+                              const ksa_select_options* options, int32_t* block_idx,
+                              float* block_scores, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ksa_vote_select_heads -- ksa_vote_select where only the listed query heads
+ * vote (voting_heads: host array of num_voting distinct heads < Hq, read
+ * during the call).  One head is the random-head ablation of the LessIsMore
+ * explainer, section 五 (one head's picks serve every head); all Hq heads is
+ * ksa_vote_select.  votes then counts the listed heads' picks only.
+ * Same outputs, limits and workspace as ksa_vote_select. */
+ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, const void* k,
+                                 int32_t token_budget, int32_t recent_window,
+                                 const int32_t* voting_heads, int32_t num_voting,
+                                 int32_t* token_idx, uint8_t* votes, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ksa_attention_recall -- the share of each query head's dense softmax mass
+ * that a selection covers (the attention recall the LessIsMore explainer,
+ * sections 四 and 五, judges selections by): with lse_selected from
+ * ksa_sparse_decode (or a decode step) and lse_dense from ksa_dense_decode on
+ * the same queries and scale, recall[i] = exp(lse_selected[i] - lse_dense[i])
+ * = sum over the selected tokens of the dense softmax weights.  count >= 1
+ * fp32 entries each ([B, Hq] arrays).  Needs no workspace. */
+ksa_status ksa_attention_recall(const float* lse_selected, const float* lse_dense, float* recall,
+                                int32_t count, void* stream);
+
 /* Operations for ksa_workspace_bytes. */
 enum {
   KSA_OP_SELECT_TOPK = 0,    /* param: top_k */

@@ -76,6 +76,7 @@ def _load():
             S = ctypes.POINTER(Shape)
             lib.orc_block_summaries.argtypes = [S, P, I, I, P, P]
             lib.orc_group_scores.argtypes = [S, P, P, P, P]
+            lib.orc_group_scores_max.argtypes = [S, P, P, P, P]
             lib.orc_topk.argtypes = [I, I, P, I, P]
             lib.orc_topk.restype = I
             lib.orc_attend_blocks.argtypes = [S, P, P, P, P, I, P, P]
@@ -147,10 +148,12 @@ def gather_pages(pool: np.ndarray, block_table: np.ndarray, b: int, T: int, Bs: 
 
 
 def group_scores(q: np.ndarray, summaries: np.ndarray, T: int, Bs: int, sm_scale: float = 0.0,
-                 Tcap: int | None = None):
+                 Tcap: int | None = None, aggregate: str = "sum"):
     """(raw, scaled) block relevance [B,Hkv,NB] from the stored summaries
     (Kinetics explainer, section 五).  raw = sum over the group's heads of
-    q_h . summary (ranking key); scaled = sm_scale * raw / G."""
+    q_h . summary (ranking key); scaled = sm_scale * raw / G.  aggregate="max"
+    is the selection variant that ranks a block by its most interested head:
+    raw = max over the group's heads of q_h . summary, scaled = sm_scale * raw."""
     lib = _load()
     B, Hq, D = q.shape
     Bs_, Hkv, nbcap, Ds = summaries.shape
@@ -161,8 +164,19 @@ def group_scores(q: np.ndarray, summaries: np.ndarray, T: int, Bs: int, sm_scale
     nb = nblocks(T, Bs)
     raw = np.zeros((B, Hkv, nb), np.float64)
     scaled = np.zeros((B, Hkv, nb), np.float64)
-    lib.orc_group_scores(ctypes.byref(s), _ptr(q), _ptr(summaries), _ptr(raw), _ptr(scaled))
+    fn = lib.orc_group_scores_max if aggregate == "max" else lib.orc_group_scores
+    fn(ctypes.byref(s), _ptr(q), _ptr(summaries), _ptr(raw), _ptr(scaled))
     return raw, scaled
+
+
+def topk_with_block(scores: np.ndarray, k: int, forced: int) -> np.ndarray:
+    """The forced-local-block selection variant: block `forced` (the one
+    holding the newest token) is always kept, and the other min(k, n) - 1
+    are the first ones of the remaining blocks by (score desc, index asc).
+    Returned ascending, like topk."""
+    rest = np.array(scores, dtype=np.float64, copy=True)
+    rest[..., forced] = np.inf
+    return topk(rest, k)
 
 
 def topk(scores: np.ndarray, k: int) -> np.ndarray:
@@ -218,6 +232,24 @@ def attend_dense(q, k, v, T: int, sm_scale: float = 0.0):
     return out, lse
 
 
+def attention_recall(q, k, T: int, tokens_per_head, sm_scale: float = 0.0):
+    """Attention recall (LessIsMore explainer, sections 四 and 五): for every
+    query head, the sum of its dense softmax weights over the tokens a
+    selection keeps.  tokens_per_head(b, h) -> iterable of token ids.
+    Returns [B, Hq] fp64."""
+    B, Hq, D = q.shape
+    scale = sm_scale if sm_scale > 0 else 1.0 / np.sqrt(D)
+    lg = head_logits(q, k, T) * scale                       # [B, Hq, T]
+    m = lg.max(axis=-1, keepdims=True)
+    p = np.exp(lg - m)
+    p /= p.sum(axis=-1, keepdims=True)
+    out = np.zeros((B, Hq), np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h] = p[b, h, sorted(set(int(t) for t in tokens_per_head(b, h)))].sum()
+    return out
+
+
 def head_logits(q, k, T: int):
     """Full score matrix q_h . k_t for every head and every t < T
     (LessIsMore explainer, section 五).  [B,Hq,T] fp64, unscaled."""
@@ -228,10 +260,15 @@ def head_logits(q, k, T: int):
     return out
 
 
-def votes(logits: np.ndarray, N: int, W: int) -> np.ndarray:
+def votes(logits: np.ndarray, N: int, W: int, heads=None) -> np.ndarray:
     """Per-token vote counts [B,T] int32 (LessIsMore explainer, section 二):
-    every head picks its first N-W history tokens by (logit desc, t asc)."""
+    every head picks its first N-W history tokens by (logit desc, t asc).
+    `heads` (a list of head indices) restricts the vote to those heads: one
+    head is the LessIsMore explainer's random-head ablation (section 五),
+    where a single head's picks serve every head."""
     lib = _load()
+    if heads is not None:
+        logits = logits[:, list(heads)]
     logits = np.ascontiguousarray(logits, dtype=np.float64)
     B, Hq, T = logits.shape
     out = np.zeros((B, T), np.int32)
@@ -251,11 +288,12 @@ def set_from_votes(vote_counts: np.ndarray, N: int, W: int) -> np.ndarray:
     return out
 
 
-def vote_select(q, k, T: int, N: int, W: int):
-    """Whole vote-union selection: returns (token_idx [B,min(N,T)], votes [B,T])."""
+def vote_select(q, k, T: int, N: int, W: int, heads=None):
+    """Whole vote-union selection: returns (token_idx [B,min(N,T)], votes [B,T]);
+    `heads` as in votes."""
     if T > N:
         lg = head_logits(q, k, T)
     else:
         lg = np.zeros((q.shape[0], q.shape[1], T), np.float64)
-    vc = votes(lg, N, W)
+    vc = votes(lg, N, W, heads)
     return set_from_votes(vc, N, W), vc

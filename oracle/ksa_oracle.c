@@ -151,6 +151,34 @@ void orc_group_scores(const orc_shape* s, const void* q, const void* summ,
       }
 }
 
+/* The MAX group aggregation of the selection variants: raw[b,g,j] = the   */
+/* largest over the group's heads h of q_h . summary_j (the block counts as  */
+/* relevant as its most interested head finds it); scaled = sm_scale * raw. */
+void orc_group_scores_max(const orc_shape* s, const void* q, const void* summ,
+                          double* raw, double* scaled) {
+  const int64_t NB = orc_nblocks(s->T, s->Bs);
+  const int64_t NBcap = orc_nblocks(s->Tcap, s->Bs);
+  const int64_t G = s->Hq / s->Hkv;
+  const double sc = orc_scale(s);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < s->B; ++b)
+    for (int64_t g = 0; g < s->Hkv; ++g)
+      for (int64_t j = 0; j < NB; ++j) {
+        double best = 0.0;
+        for (int64_t hh = 0; hh < G; ++hh) {
+          int64_t h = g * G + hh;
+          double acc = 0.0;
+          for (int64_t d = 0; d < s->D; ++d)
+            acc += orc_get(q, s->dtype, (b * s->Hq + h) * s->D + d) *
+                   orc_get(summ, s->dtype, ((b * s->Hkv + g) * NBcap + j) * s->D + d);
+          if (hh == 0 || acc > best) best = acc;
+        }
+        int64_t o = (b * s->Hkv + g) * NB + j;
+        if (raw) raw[o] = best;
+        if (scaled) scaled[o] = sc * best;
+      }
+}
+
 /* (value, index) pair ordered by value descending, then index ascending. */
 typedef struct {
   double val;

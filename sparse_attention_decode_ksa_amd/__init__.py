@@ -11,7 +11,9 @@ Function names match the C entry points: ``ksa_block_summaries``,
 ``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode``,
 ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
-``ksa_paged_dense_decode``, ``ksa_workspace_bytes``, ``ksa_status_string``.
+``ksa_paged_dense_decode``, the selection variants ``ksa_select_topk_ex`` and
+``ksa_vote_select_heads``, the diagnostic ``ksa_attention_recall``,
+``ksa_workspace_bytes``, ``ksa_status_string``.
 """
 from __future__ import annotations
 
@@ -36,7 +38,9 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode",
             "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
+            "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
             "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
 class KsaLibraryError(RuntimeError):
@@ -63,6 +67,12 @@ class Problem(ctypes.Structure):
 class Selection(ctypes.Structure):
     """Mirror of ``ksa_selection``."""
     _fields_ = [("kind", ctypes.c_int32), ("idx", ctypes.c_void_p), ("count", ctypes.c_int32)]
+
+
+class SelectOptions(ctypes.Structure):
+    """Mirror of ``ksa_select_options``."""
+    _fields_ = [("top_k", ctypes.c_int32), ("aggregate", ctypes.c_int32),
+                ("force_last_block", ctypes.c_int32)]
 
 
 class PagedKv(ctypes.Structure):
@@ -101,13 +111,16 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_paged_block_summaries.argtypes = [PP, PG, P, P, I32, I32, P]
         lib.ksa_paged_block_topk_decode.argtypes = [PP, PG, P, P, P, P, I32, I32, P, P, P, P]
         lib.ksa_paged_dense_decode.argtypes = [PP, PG, P, P, P, P, P, P, SZ, P]
+        lib.ksa_select_topk_ex.argtypes = [PP, P, P, ctypes.POINTER(SelectOptions), P, P, P, SZ, P]
+        lib.ksa_vote_select_heads.argtypes = [PP, P, P, I32, I32, P, I32, P, P, P, SZ, P]
+        lib.ksa_attention_recall.argtypes = [P, P, P, I32, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:9]:
+        for name in EXPORTED[:12]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -430,3 +443,71 @@ def ksa_paged_dense_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
         _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
         pws, nws, _stream(stream)), "ksa_paged_dense_decode")
     return out, lse
+
+
+# ----------------------------------------------------------------------------- variants, recall
+def ksa_select_topk_ex(q: torch.Tensor, summaries: torch.Tensor, seq_len: int, block_size: int,
+                       top_k: int, aggregate: int = KSA_AGG_SUM, force_last_block: bool = False,
+                       max_seq_len: Optional[int] = None, block_idx=None, block_scores=None,
+                       want_scores: bool = False, sm_scale: float = 0.0, workspace=None,
+                       stream=None):
+    """ksa_select_topk with the selection variants: aggregate KSA_AGG_MAX ranks
+    a block by its largest head, force_last_block always keeps the newest block."""
+    lib = load_library()
+    B, Hkv, nbcap, D = summaries.shape
+    Tcap = max_seq_len if max_seq_len is not None else nbcap * block_size
+    prob = Problem(B, q.shape[1], Hkv, D, int(seq_len), int(Tcap), int(block_size),
+                   _dtype_code(summaries), float(sm_scale))
+    nb = nblocks(seq_len, block_size)
+    keff = min(top_k, nb)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, keff), dtype=torch.int32, device=q.device)
+    if want_scores and block_scores is None:
+        block_scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=q.device)
+    opts = SelectOptions(int(top_k), int(aggregate), 1 if force_last_block else 0)
+    ws, pws, nws = _workspace(prob, KSA_OP_SELECT_TOPK, top_k, q.device, workspace)
+    _check(lib.ksa_select_topk_ex(ctypes.byref(prob),
+                                  _dev(q, "q", summaries.dtype, (B, prob.num_q_heads, D)),
+                                  _dev(summaries, "summaries"), ctypes.byref(opts),
+                                  _dev(block_idx, "block_idx", torch.int32, (B, Hkv, keff)),
+                                  _dev(block_scores, "block_scores", torch.float32, (B, Hkv, nb)),
+                                  pws, nws, _stream(stream)), "ksa_select_topk_ex")
+    return (block_idx, block_scores) if block_scores is not None else block_idx
+
+
+def ksa_vote_select_heads(q: torch.Tensor, k: torch.Tensor, seq_len: int, token_budget: int,
+                          recent_window: int, voting_heads, token_idx=None, votes=None,
+                          want_votes: bool = False, workspace=None, stream=None):
+    """ksa_vote_select with only the listed query heads voting."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len)
+    B = q.shape[0]
+    n_out = min(token_budget, seq_len)
+    heads = (ctypes.c_int32 * len(voting_heads))(*[int(h) for h in voting_heads])
+    if token_idx is None:
+        token_idx = torch.empty((B, n_out), dtype=torch.int32, device=q.device)
+    if want_votes and votes is None:
+        votes = torch.empty((B, seq_len), dtype=torch.uint8, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_SELECT, token_budget, q.device, workspace)
+    _check(lib.ksa_vote_select_heads(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
+                                     int(token_budget), int(recent_window),
+                                     ctypes.cast(heads, ctypes.c_void_p), len(voting_heads),
+                                     _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
+                                     _dev(votes, "votes", torch.uint8, (B, seq_len)), pws, nws,
+                                     _stream(stream)), "ksa_vote_select_heads")
+    return (token_idx, votes) if votes is not None else token_idx
+
+
+def ksa_attention_recall(lse_selected: torch.Tensor, lse_dense: torch.Tensor, recall=None,
+                         stream=None) -> torch.Tensor:
+    """Share of each head's dense softmax mass the selection covers:
+    exp(lse_selected - lse_dense), elementwise over [B, Hq]."""
+    lib = load_library()
+    if recall is None:
+        recall = torch.empty_like(lse_selected)
+    n = lse_selected.numel()
+    _check(lib.ksa_attention_recall(_dev(lse_selected, "lse_selected", torch.float32),
+                                    _dev(lse_dense, "lse_dense", torch.float32, lse_selected.shape),
+                                    _dev(recall, "recall", torch.float32, lse_selected.shape), int(n),
+                                    _stream(stream)), "ksa_attention_recall")
+    return recall

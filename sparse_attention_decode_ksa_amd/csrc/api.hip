@@ -304,4 +304,71 @@ ksa_status ksa_paged_dense_decode(const ksa_problem* problem, const ksa_paged_kv
                                    (hipStream_t)stream, &pk));
 }
 
+ksa_status ksa_select_topk_ex(const ksa_problem* problem, const void* q, const void* summaries,
+                              const ksa_select_options* options, int32_t* block_idx,
+                              float* block_scores, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!options) return KSA_ERR_INVALID_ARGUMENT;
+  if (options->aggregate != KSA_AGG_SUM && options->aggregate != KSA_AGG_MAX)
+    return KSA_ERR_INVALID_ARGUMENT;
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  const int32_t top_k = options->top_k;
+  if (!q || !summaries || !block_idx || top_k < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(summaries) || !aligned4(block_idx) ||
+      (block_scores && !aligned4(block_scores)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.NB > kSelectMaxBlocks) return KSA_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(*problem, KSA_OP_SELECT_TOPK, top_k);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  const int keff = top_k < d.NB ? top_k : d.NB;
+  SelectVariant var;
+  var.agg_max = options->aggregate == KSA_AGG_MAX ? 1 : 0;
+  var.forced_block = options->force_last_block ? (d.T - 1) / d.Bs : -1;
+  return from_hip(launch_select_topk(d, q, summaries, keff, block_idx, block_scores, workspace,
+                                     (hipStream_t)stream, var));
+}
+
+ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, const void* k,
+                                 int32_t token_budget, int32_t recent_window,
+                                 const int32_t* voting_heads, int32_t num_voting,
+                                 int32_t* token_idx, uint8_t* votes, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, false);
+  if (st != KSA_OK) return st;
+  if (!voting_heads || num_voting < 1 || num_voting > problem->num_q_heads)
+    return KSA_ERR_INVALID_ARGUMENT;
+  HeadMask mask;
+  for (int i = 0; i < 8; ++i) mask.w[i] = 0u;
+  for (int32_t i = 0; i < num_voting; ++i) {
+    const int32_t h = voting_heads[i];
+    if (h < 0 || h >= problem->num_q_heads || h > 255) return KSA_ERR_INVALID_ARGUMENT;
+    if ((mask.w[h >> 5] >> (h & 31)) & 1u) return KSA_ERR_INVALID_ARGUMENT;  // listed twice
+    mask.w[h >> 5] |= 1u << (h & 31);
+  }
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned4(token_idx)) return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan plan = plan_vote(d, token_budget, recent_window);
+  if (workspace_bytes < plan.total) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.total && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_vote_select(d, q, k, token_budget, recent_window, token_idx, votes,
+                                     workspace, plan, (hipStream_t)stream, mask));
+}
+
+ksa_status ksa_attention_recall(const float* lse_selected, const float* lse_dense, float* recall,
+                                int32_t count, void* stream) {
+  if (!lse_selected || !lse_dense || !recall || count < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned4(lse_selected) || !aligned4(lse_dense) || !aligned4(recall))
+    return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_attention_recall(lse_selected, lse_dense, recall, count,
+                                          (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -197,4 +197,20 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
   return launch_g<float, 128>(a, kind, plan, stream);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ lse_sel,
+                                                     const float* __restrict__ lse_dense,
+                                                     float* __restrict__ recall, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) recall[i] = expf(lse_sel[i] - lse_dense[i]);
+}
+}  // namespace
+
+hipError_t launch_attention_recall(const float* lse_sel, const float* lse_dense, float* recall,
+                                   int n, hipStream_t stream) {
+  hipLaunchKernelGGL(recall_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, lse_sel,
+                     lse_dense, recall, n);
+  return hipGetLastError();
+}
+
 }  // namespace ksa

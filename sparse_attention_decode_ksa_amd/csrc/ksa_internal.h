@@ -63,6 +63,10 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
                             void* workspace, const AttnPlan& plan, hipStream_t stream,
                             const PagedKv* paged = nullptr);
 
+// recall[i] = exp(lse_sel[i] - lse_dense[i]) for i < n.
+hipError_t launch_attention_recall(const float* lse_sel, const float* lse_dense, float* recall,
+                                   int n, hipStream_t stream);
+
 hipError_t launch_block_summaries(const Dims& d, const void* k, void* summaries, int first_block,
                                   int num_blocks, hipStream_t stream);
 // Paged: blocks [first, first + num) below each sequence's NB_b, or each
@@ -73,9 +77,15 @@ hipError_t launch_paged_block_summaries(const Dims& d, const PagedKv& p, const v
 
 constexpr int kSelectMaxBlocks = 15360;  // a row's keys fit the registers of one top-k workgroup
 size_t select_workspace_bytes(const Dims& d);
+// Selection variants (the ablations): rank a block by its largest head
+// instead of the group's sum; always keep one block (its key made maximal).
+struct SelectVariant {
+  int agg_max = 0;
+  int forced_block = -1;
+};
 hipError_t launch_select_topk(const Dims& d, const void* q, const void* summaries, int keff,
                               int32_t* block_idx, float* block_scores, void* workspace,
-                              hipStream_t stream);
+                              hipStream_t stream, const SelectVariant& var = SelectVariant());
 
 // Whole decode step in one launch (refresh + select + attend per row).
 constexpr int kStepMaxBlocks = 4096;  // blocks per row whose keys the step keeps in LDS
@@ -94,8 +104,13 @@ struct VotePlan {
   size_t keys_off, bits_off, votes_off, vhist_off, total;
 };
 VotePlan plan_vote(const Dims& d, int N, int W);
+// The query heads that vote (bit h of w[h / 32]); every head by default.
+struct HeadMask {
+  uint32_t w[8] = {~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u, ~0u};
+};
 hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N, int W,
                               int32_t* token_idx, uint8_t* votes, void* workspace,
-                              const VotePlan& plan, hipStream_t stream);
+                              const VotePlan& plan, hipStream_t stream,
+                              const HeadMask& voting = HeadMask());
 
 }  // namespace ksa

@@ -19,6 +19,8 @@
 //     ids winning among equal keys.
 // Integer work after phase 1 is exact, so the selection is a fixed function
 // of the fp32 scores.
+#include <float.h>
+
 #include "ksa_device.h"
 #include "ksa_internal.h"
 #include "ksa_topk.h"
@@ -37,11 +39,15 @@ constexpr int kScoreUnroll = KSA_SCORE_UNROLL;    // summaries in flight per lan
 constexpr int kTopkThreads = 256;  // one workgroup per row; also the histogram size
 
 // Relevance of a tile of blocks of one row.  Every LPT-lane group issues all
-// of its loads before consuming any.
-template <typename T, int D>
+// of its loads before consuming any.  MAXAGG: the selection variant that
+// ranks a block by its largest single-head dot product (each head's q kept
+// in registers) instead of the group's sum.  forced >= 0: that block's key
+// is the largest possible, so it is always selected (its score is still
+// reported as computed).
+template <typename T, int D, bool MAXAGG>
 __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
     const T* __restrict__ q, const T* __restrict__ summ, Dims d, uint32_t* __restrict__ keys,
-    float* __restrict__ block_scores, float score_scale) {
+    float* __restrict__ block_scores, float score_scale, int forced) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int NGRP = kScoreThreads / LPT;
@@ -58,6 +64,35 @@ __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
   for (int u = 0; u < kScoreUnroll; ++u)
     raw[u] = ld16_stream(sp + (int64_t)min(j0 + u * NGRP, NB - 1) * D);
 
+  if constexpr (MAXAGG) {
+    constexpr int GM = 8;  // largest group
+    float qv[GM][EPL];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      if (h < d.G) KV<T>::widen(ld16(q + ((int64_t)b * d.Hq + g * d.G + h) * D + li * EPL), qv[h]);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int j = j0 + u * NGRP;
+      float f[EPL];
+      KV<T>::widen(raw[u], f);
+      float best = -FLT_MAX;
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < d.G) {  // uniform
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
+          best = fmaxf(best, group_sum<LPT>(p));
+        }
+      }
+      if (li == 0 && j < NB) {
+        keys[(int64_t)row * NB + j] = j == forced ? 0xFFFFFFFFu : order_key(best);
+        if (block_scores) block_scores[(int64_t)row * NB + j] = best * score_scale;
+      }
+    }
+    return;
+  }
   // group query: sum of the G heads, fp32
   float qs[EPL];
 #pragma unroll
@@ -78,7 +113,7 @@ __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
     for (int e = 0; e < EPL; ++e) p = fmaf(qs[e], f[e], p);
     p = group_sum<LPT>(p);
     if (li == 0 && j < NB) {
-      keys[(int64_t)row * NB + j] = order_key(p);
+      keys[(int64_t)row * NB + j] = j == forced ? 0xFFFFFFFFu : order_key(p);
       if (block_scores) block_scores[(int64_t)row * NB + j] = p * score_scale;
     }
   }
@@ -103,14 +138,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
 
 template <typename T, int D>
 hipError_t launch_typed(const Dims& d, const void* q, const void* summ, int keff, int32_t* idx,
-                        float* scores, uint32_t* keys, hipStream_t s) {
+                        float* scores, uint32_t* keys, const SelectVariant& var, hipStream_t s) {
   constexpr int LPT = D / KV<T>::EPL;
   constexpr int TILE = (kScoreThreads / LPT) * kScoreUnroll;
-  const float score_scale = d.scale / (float)d.G;
   const int rows = d.B * d.Hkv;
-  hipLaunchKernelGGL((block_score_kernel<T, D>), dim3((d.NB + TILE - 1) / TILE, rows),
-                     dim3(kScoreThreads), 0, s, (const T*)q, (const T*)summ, d, keys, scores,
-                     score_scale);
+  const dim3 sgrid((d.NB + TILE - 1) / TILE, rows);
+  if (var.agg_max)
+    hipLaunchKernelGGL((block_score_kernel<T, D, true>), sgrid, dim3(kScoreThreads), 0, s,
+                       (const T*)q, (const T*)summ, d, keys, scores, d.scale, var.forced_block);
+  else
+    hipLaunchKernelGGL((block_score_kernel<T, D, false>), sgrid, dim3(kScoreThreads), 0, s,
+                       (const T*)q, (const T*)summ, d, keys, scores, d.scale / (float)d.G,
+                       var.forced_block);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(rows), block(kTopkThreads);
@@ -133,16 +172,16 @@ size_t select_workspace_bytes(const Dims& d) {
 
 hipError_t launch_select_topk(const Dims& d, const void* q, const void* summaries, int keff,
                               int32_t* block_idx, float* block_scores, void* workspace,
-                              hipStream_t stream) {
-  uint32_t* keys = (uint32_t*)workspace;
+                              hipStream_t stream, const SelectVariant& var) {
+  uint32_t* k = (uint32_t*)workspace;
   if (d.dtype == KSA_BF16) {
     if (d.D == 64)
-      return launch_typed<uint16_t, 64>(d, q, summaries, keff, block_idx, block_scores, keys, stream);
-    return launch_typed<uint16_t, 128>(d, q, summaries, keff, block_idx, block_scores, keys, stream);
+      return launch_typed<uint16_t, 64>(d, q, summaries, keff, block_idx, block_scores, k, var, stream);
+    return launch_typed<uint16_t, 128>(d, q, summaries, keff, block_idx, block_scores, k, var, stream);
   }
   if (d.D == 64)
-    return launch_typed<float, 64>(d, q, summaries, keff, block_idx, block_scores, keys, stream);
-  return launch_typed<float, 128>(d, q, summaries, keff, block_idx, block_scores, keys, stream);
+    return launch_typed<float, 64>(d, q, summaries, keff, block_idx, block_scores, k, var, stream);
+  return launch_typed<float, 128>(d, q, summaries, keff, block_idx, block_scores, k, var, stream);
 }
 
 }  // namespace ksa

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
     const uint32_t* __restrict__ keys, int hist, int kstride, int kv, int words, int Hq,
-    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist) {
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist, HeadMask voting) {
   constexpr int NWV = NT / 64;
   static_assert(4096 % NT == 0, "radix buckets per thread");
   __shared__ TopkShared sh;
@@ -225,7 +225,9 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
   if (hr % Hq == 0)
     for (int i = tid; i < 256; i += NT) vhist[(hr / Hq) * 256 + i] = 0u;
   uint32_t* br = bits + hr * words;
-  if (kv == 0) {  // the whole budget is the recency window: no picks
+  const int h = (int)(hr % Hq);
+  // no picks: the whole budget is the recency window, or the head does not vote
+  if (kv == 0 || !((voting.w[h >> 5] >> (h & 31)) & 1u)) {
     for (int w = tid; w < words; w += NT) br[w] = 0u;
     return;
   }
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
 template <bool kLdsKeys>
 __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
     const uint32_t* __restrict__ keys, int hist, int kstride, int kv, int words, int Hq,
-    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist) {
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist, HeadMask voting) {
   extern __shared__ uint32_t lkeys[];  // the head's keys (kLdsKeys)
   __shared__ uint32_t hbin[256];
   __shared__ uint32_t red[2][kHeadThreads / 64];
@@ -335,7 +337,9 @@ __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
   if (hr % Hq == 0)
     for (int i = tid; i < 256; i += kHeadThreads) vhist[(hr / Hq) * 256 + i] = 0u;
   uint32_t* br = bits + hr * words;
-  if (kv == 0) {  // the whole budget is the recency window: no picks
+  const int h = (int)(hr % Hq);
+  // no picks: the whole budget is the recency window, or the head does not vote
+  if (kv == 0 || !((voting.w[h >> 5] >> (h & 31)) & 1u)) {
     for (int w = tid; w < words; w += kHeadThreads) br[w] = 0u;
     return;
   }
@@ -796,12 +800,12 @@ hipError_t launch_scores_g(const Dims& d, const void* q, const void* k, int hist
 }
 
 hipError_t launch_head_select(const Dims& d, const VotePlan& p, const uint32_t* keys, uint32_t* bits,
-                              uint32_t* vhist, hipStream_t stream) {
+                              uint32_t* vhist, const HeadMask& voting, hipStream_t stream) {
   const dim3 grid(d.B * d.Hq), block(kHeadThreads);
   const int kpt = (p.hist + kHeadNT - 1) / kHeadNT;
 #define KSA_HEAD_TOPK(K)                                                                      \
   hipLaunchKernelGGL((vote_head_topk_kernel<kHeadNT, K>), grid, dim3(kHeadNT), 0, stream, keys, \
-                     p.hist, p.kstride, p.kv, p.words, d.Hq, bits, vhist)
+                     p.hist, p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting)
   if (kpt <= 8) {
     KSA_HEAD_TOPK(8);
   } else if (kpt <= 16) {
@@ -825,10 +829,10 @@ hipError_t launch_head_select(const Dims& d, const VotePlan& p, const uint32_t* 
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(vote_head_select_kernel<true>, grid, block, lds, stream, keys, p.hist,
-                       p.kstride, p.kv, p.words, d.Hq, bits, vhist);
+                       p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting);
   } else {
     hipLaunchKernelGGL(vote_head_select_kernel<false>, grid, block, 0, stream, keys, p.hist,
-                       p.kstride, p.kv, p.words, d.Hq, bits, vhist);
+                       p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting);
   }
   return hipGetLastError();
 }
@@ -855,7 +859,7 @@ VotePlan plan_vote(const Dims& d, int N, int W) {
 
 hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N, int W,
                               int32_t* token_idx, uint8_t* votes, void* workspace,
-                              const VotePlan& plan, hipStream_t stream) {
+                              const VotePlan& plan, hipStream_t stream, const HeadMask& voting) {
   if (d.T <= N) {
     hipLaunchKernelGGL(vote_all_kernel, dim3((d.T + 255) / 256, d.B), dim3(256), 0, stream, d.T,
                        token_idx, votes);
@@ -874,7 +878,7 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
     e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
                   : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
   if (e != hipSuccess) return e;
-  e = launch_head_select(d, plan, keys, bits, vhist, stream);
+  e = launch_head_select(d, plan, keys, bits, vhist, voting, stream);
   if (e != hipSuccess) return e;
   if (plan.words <= kSetThreads) {
     if (d.Hq < 64)

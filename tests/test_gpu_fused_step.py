@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 def stale_summaries(k, w, seed=0):
     """Summaries as they stood before token T-1 was appended: the newest block
     holds its mean over one token fewer, or garbage when T-1 opens it."""
-    s = torch.empty((w.B, w.Hkv, ksa.nblocks(w.cap, w.Bs), w.D), dtype=k.dtype, device=DEV)
+    s = torch.zeros((w.B, w.Hkv, ksa.nblocks(w.cap, w.Bs), w.D), dtype=k.dtype, device=DEV)
     jref = (w.T - 1) // w.Bs
     if w.T > 1:
         ksa.ksa_block_summaries(k, s, w.T - 1, w.Bs)
@@ -45,7 +45,7 @@ def separate_step(w, q, k, v, s, refresh=True):
 def fused_vs_separate(w, q, k, v, refresh=True, bitwise_out=False, seed=0):
     s0 = stale_summaries(k, w, seed) if refresh else None
     if s0 is None:
-        s0 = torch.empty((w.B, w.Hkv, ksa.nblocks(w.cap, w.Bs), w.D), dtype=k.dtype, device=DEV)
+        s0 = torch.zeros((w.B, w.Hkv, ksa.nblocks(w.cap, w.Bs), w.D), dtype=k.dtype, device=DEV)
         ksa.ksa_block_summaries(k, s0, w.T, w.Bs)
     s_sep, s_f = s0.clone(), s0.clone()
     idx_sep, out_sep, lse_sep = separate_step(w, q, k, v, s_sep, refresh)

@@ -70,7 +70,7 @@ def test_paged_step_matches_oracle_per_sequence(case):
     c = dict(case)
     lens, Bs, top_k = c.pop("lens"), c.pop("Bs"), c.pop("top_k")
     w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=lens[-1] + 11, **c)
-    s = torch.empty((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    s = torch.zeros((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
     ksa.ksa_paged_block_summaries(kp, s, table, seq)
     # the newest block of every sequence holds stale values until the refresh
     for b, T in enumerate(lens):
@@ -117,7 +117,7 @@ def test_paged_step_equals_contiguous_step_bitwise(G, D, dtype, Bs, T):
     w, q, k, v, kp, vp, table, seq = paged_inputs([T] * 6, Bs, seed=T, Hq=2 * G, Hkv=2, D=D,
                                                   dtype=dtype)
     nbc = table.shape[1]
-    s_c = torch.empty((w.B, w.Hkv, nbc, w.D), dtype=k.dtype, device=DEV)
+    s_c = torch.zeros((w.B, w.Hkv, nbc, w.D), dtype=k.dtype, device=DEV)
     ksa.ksa_block_summaries(k, s_c, T - 1, Bs) if T > 1 else None
     s_c[:, :, (T - 1) // Bs] = 0
     s_p = s_c.clone()
@@ -137,7 +137,7 @@ def test_paged_step_equals_contiguous_step_bitwise(G, D, dtype, Bs, T):
 def test_paged_step_without_refresh_keeps_summaries():
     w, q, k, v, kp, vp, table, seq = paged_inputs([700, 300, 90], 16, seed=70, Hq=4, Hkv=2, D=64,
                                                   dtype="bf16")
-    s = torch.empty((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    s = torch.zeros((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
     ksa.ksa_paged_block_summaries(kp, s, table, seq)
     before = s.clone()
     out, lse, idx = ksa.ksa_paged_block_topk_decode(q, kp, vp, s, table, seq, 10,

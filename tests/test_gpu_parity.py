@@ -267,7 +267,7 @@ def test_vote_integer_inputs_are_bit_exact(Hq, Hkv):
 
 # ----------------------------------------------------------------------------- full workloads
 def block_step(w, q, k, v):
-    s = torch.empty((w.B, w.Hkv, ksa.nblocks(w.cap, w.Bs), w.D), dtype=k.dtype, device=DEV)
+    s = torch.zeros((w.B, w.Hkv, ksa.nblocks(w.cap, w.Bs), w.D), dtype=k.dtype, device=DEV)
     ksa.ksa_block_summaries(k, s, w.T, w.Bs)
     idx = ksa.ksa_select_topk(q, s, w.T, w.Bs, w.top_k)
     out, lse = ksa.ksa_sparse_decode(q, k, v, w.T, idx, ksa.KSA_SEL_BLOCKS, block_size=w.Bs)

@@ -1,0 +1,149 @@
+"""GPU parity of the selection variants and the attention-recall diagnostic.
+
+* ksa_select_topk_ex: MAX group aggregation and the forced local block,
+  against the oracle's max-aggregated relevance and its forced-block rule
+  (near-tie rules of tests/parity.py).
+* ksa_vote_select_heads: votes of a subset of heads (one head: the
+  random-head ablation) against the oracle's vote of those heads.
+* ksa_attention_recall: exp(lse_selected - lse_dense) on the GPU against the
+  oracle's sum of dense softmax weights over the GPU's own selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_decode_ksa_amd as ksa
+from sparse_attention_decode_ksa_amd.inputs import WORKLOADS, small_workload
+from parity import check_block_selection, check_votes
+from test_gpu_parity import DEV, gpu_inputs, np_bits, run_summaries
+
+pytestmark = pytest.mark.gpu
+
+SEL_CASES = [
+    dict(B=2, Hq=4, Hkv=2, D=64, T=1000, Bs=16, dtype="f32", top_k=8),
+    dict(B=2, Hq=16, Hkv=2, D=128, T=3001, Bs=16, dtype="bf16", top_k=40),
+    dict(B=3, Hq=8, Hkv=2, D=128, T=777, Bs=7, dtype="bf16", top_k=20),
+    dict(B=1, Hq=2, Hkv=2, D=64, T=50, Bs=16, dtype="bf16", top_k=9),     # k > NB
+]
+
+
+def sel_id(c):
+    return "%s-G%d-D%d-T%d-Bs%d-k%d" % (c["dtype"], c["Hq"] // c["Hkv"], c["D"], c["T"], c["Bs"],
+                                        c["top_k"])
+
+
+@pytest.mark.parametrize("case", SEL_CASES, ids=sel_id)
+def test_max_aggregation_matches_oracle(case):
+    w = small_workload(seed=case["T"] + 1, **case)
+    q, k, v = gpu_inputs(w)
+    s = run_summaries(k, w)
+    idx, sc = ksa.ksa_select_topk_ex(q, s, w.T, w.Bs, w.top_k, aggregate=ksa.KSA_AGG_MAX,
+                                     want_scores=True)
+    torch.cuda.synchronize()
+    raw, scaled = oracle.group_scores(np_bits(q), np_bits(s), w.T, w.Bs, Tcap=w.cap,
+                                      aggregate="max")
+    check_block_selection(idx.cpu().numpy().reshape(w.B * w.Hkv, -1),
+                          raw.reshape(w.B * w.Hkv, -1), w.top_k)
+    np.testing.assert_allclose(sc.cpu().numpy(), scaled, rtol=0,
+                               atol=1e-5 * max(1.0, float(np.abs(scaled).max())))
+
+
+@pytest.mark.parametrize("agg", [ksa.KSA_AGG_SUM, ksa.KSA_AGG_MAX])
+@pytest.mark.parametrize("case", SEL_CASES, ids=sel_id)
+def test_forced_last_block(case, agg):
+    w = small_workload(seed=case["T"] + 2, **case)
+    q, k, v = gpu_inputs(w)
+    s = run_summaries(k, w)
+    idx = ksa.ksa_select_topk_ex(q, s, w.T, w.Bs, w.top_k, aggregate=agg, force_last_block=True)
+    torch.cuda.synchronize()
+    raw, _ = oracle.group_scores(np_bits(q), np_bits(s), w.T, w.Bs, Tcap=w.cap,
+                                 aggregate="max" if agg == ksa.KSA_AGG_MAX else "sum")
+    raw = raw.reshape(w.B * w.Hkv, -1)
+    forced = (w.T - 1) // w.Bs
+    ids = idx.cpu().numpy().reshape(w.B * w.Hkv, -1)
+    keff = ids.shape[1]
+    assert np.all(ids == np.sort(ids, axis=1)) and np.all(np.any(ids == forced, axis=1))
+    if keff == raw.shape[1]:
+        return
+    # the other k_eff - 1 blocks: the top of the rest (forced block pushed below everything)
+    rest = raw.copy()
+    rest[:, forced] = raw.min() - 1.0
+    others = np.array([[j for j in row if j != forced] for row in ids])
+    check_block_selection(others, rest, keff - 1)
+    # exact rule where nothing is near a tie
+    ref = oracle.topk_with_block(raw, w.top_k, forced)
+    assert (ref == ids).mean() > 0.9
+
+
+@pytest.mark.parametrize("heads", [[0], [5], [1, 6, 7], list(range(8))])
+def test_vote_of_chosen_heads_matches_oracle(heads):
+    w = small_workload(B=2, Hq=8, Hkv=2, D=128, T=3000, dtype="bf16", seed=len(heads))
+    q, k, v = gpu_inputs(w)
+    N, W = 512, 128
+    idx, votes = ksa.ksa_vote_select_heads(q, k, w.T, N, W, heads, want_votes=True)
+    torch.cuda.synchronize()
+    lg = oracle.head_logits(np_bits(q), np_bits(k), w.T)[:, heads]
+    check_votes(votes.cpu().numpy(), idx.cpu().numpy(), lg, N, W)
+    assert votes.max().item() <= len(heads)
+
+
+def test_vote_of_chosen_heads_integer_bit_exact():
+    w = small_workload(B=2, Hq=8, Hkv=4, D=64, T=1500, dtype="bf16", seed=3)
+    q, k, v = gpu_inputs(w, integer=True, lo=-1, hi=1)
+    for heads in ([2], [0, 3, 4]):
+        idx, votes = ksa.ksa_vote_select_heads(q, k, w.T, 256, 64, heads, want_votes=True)
+        sel, ref_votes = oracle.vote_select(np_bits(q), np_bits(k), w.T, 256, 64, heads=heads)
+        np.testing.assert_array_equal(votes.cpu().numpy().astype(np.int32), ref_votes)
+        np.testing.assert_array_equal(idx.cpu().numpy(), sel)
+
+
+def test_vote_heads_validation():
+    w = small_workload(B=1, Hq=4, Hkv=2, D=64, T=300, dtype="bf16", seed=1)
+    q, k, v = gpu_inputs(w)
+    for bad in ([], [4], [-1], [1, 1]):
+        with pytest.raises(ksa.KsaError):
+            ksa.ksa_vote_select_heads(q, k, w.T, 64, 16, bad)
+
+
+def test_recall_of_the_fused_step_matches_oracle():
+    w = small_workload(B=2, Hq=8, Hkv=2, D=128, T=3000, Bs=16, dtype="bf16", top_k=32, seed=12)
+    q, k, v = gpu_inputs(w)
+    s = run_summaries(k, w)
+    out, lse, idx = ksa.ksa_block_topk_decode(q, k, v, s, w.T, w.Bs, w.top_k, want_block_idx=True)
+    dout, dlse = ksa.ksa_dense_decode(q, k, v, w.T)
+    rec = ksa.ksa_attention_recall(lse, dlse)
+    torch.cuda.synchronize()
+    ids = idx.cpu().numpy()
+    G = w.G
+    ref = oracle.attention_recall(np_bits(q), np_bits(k), w.T, lambda b, h: [
+        t for j in ids[b, h // G] for t in range(j * w.Bs, min((j + 1) * w.Bs, w.T))])
+    np.testing.assert_allclose(rec.cpu().numpy(), ref, rtol=0, atol=1e-4)
+    assert np.all(rec.cpu().numpy() <= 1.0 + 1e-5)
+
+
+def test_recall_of_every_block_is_one():
+    w = small_workload(B=2, Hq=4, Hkv=2, D=64, T=400, Bs=16, dtype="f32", top_k=25, seed=4)
+    q, k, v = gpu_inputs(w)
+    s = run_summaries(k, w)
+    out, lse, _ = ksa.ksa_block_topk_decode(q, k, v, s, w.T, w.Bs, w.top_k)
+    _, dlse = ksa.ksa_dense_decode(q, k, v, w.T)
+    rec = ksa.ksa_attention_recall(lse, dlse)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(rec.cpu().numpy(), 1.0, atol=2e-5)
+
+
+def test_recall_on_the_c2_workload_is_high():
+    """The recall the pages judge selections by, on the planted c2 caches
+    (first 8 sequences): between 0 and 1, and for most heads above the 1/16
+    share of tokens the 64 of 1024 blocks hold (the selection beats a
+    uniform one)."""
+    w = WORKLOADS["c2"].with_(B=8)
+    q, k, v = gpu_inputs(w)
+    s = run_summaries(k, w)
+    out, lse, _ = ksa.ksa_block_topk_decode(q, k, v, s, w.T, w.Bs, w.top_k)
+    _, dlse = ksa.ksa_dense_decode(q, k, v, w.T)
+    rec = ksa.ksa_attention_recall(lse, dlse).cpu().numpy()
+    assert rec.min() > 0.0 and rec.max() <= 1.0 + 1e-5
+    print("c2 recall: median %.3f, min %.3f" % (float(np.median(rec)), float(rec.min())))
+    assert float(np.median(rec)) > 64 / 1024

@@ -295,8 +295,9 @@ def test_token_attention_matches_masked_sdpa():
 
 
 # ----------------------------------------------------------------------------- votes
-def brute_vote(q64, k64, T, N, W):
-    """Python-sorted per-head picks, Counter tally, sorted ranking."""
+def brute_vote(q64, k64, T, N, W, heads=None):
+    """Python-sorted per-head picks, Counter tally, sorted ranking (over the
+    listed heads only, when given)."""
     B, Hq, D = q64.shape
     Hkv = k64.shape[1]
     G = Hq // Hkv
@@ -308,7 +309,7 @@ def brute_vote(q64, k64, T, N, W):
             continue
         C, Kv = T - W, N - W
         tally = Counter()
-        for h in range(Hq):
+        for h in (range(Hq) if heads is None else heads):
             lg = [float(np.dot(q64[b, h], k64[b, h // G, t])) for t in range(C)]
             order = sorted(range(C), key=lambda t: (-lg[t], t))
             tally.update(order[:Kv])
@@ -429,3 +430,107 @@ def test_gather_pages_reads_each_token_from_its_page():
         for t in range(T):
             for c in range(D):
                 assert seq[0, h, t, c] == table[1, t // Bs] * 1000 + h * 100 + (t % Bs) * 10 + c
+
+
+# ----------------------------------------------------------------------------- selection variants
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_max_aggregation_is_the_largest_single_head_score(G):
+    """The MAX group aggregation equals, block by block, the largest of the
+    group's single-head relevances (each a G = 1 problem, whose sum over one
+    head is the plain dot product)."""
+    w, q, k, v = rand_problem(B=2, Hq=2 * G, Hkv=2, D=16, T=90, dtype="bf16", seed=G)
+    summ = oracle.block_summaries(k, 90, 8)
+    raw, scaled = oracle.group_scores(q, summ, 90, 8, aggregate="max")
+    per_head = []
+    for hh in range(G):
+        qh = np.ascontiguousarray(q.reshape(2, 2, G, 16)[:, :, hh])
+        r1, _ = oracle.group_scores(qh, summ, 90, 8)
+        per_head.append(r1)
+    np.testing.assert_array_equal(raw, np.max(np.stack(per_head), axis=0))
+    np.testing.assert_allclose(scaled, raw / 4.0, rtol=1e-15)  # sm_scale = 1/sqrt(16)
+
+
+def test_max_aggregation_integer_example():
+    """Two heads, two blocks of one token: q = (1,0), (0,2); keys (3,1), (1,1).
+    Head dots: block 0 -> 3 and 2, block 1 -> 1 and 2; max -> 3 and 2
+    (the sum would give 5 and 3)."""
+    q = np.array([[[1, 0], [0, 2]]], np.float32)
+    k = np.array([[[[3, 1], [1, 1]]]], np.float32)
+    summ = oracle.block_summaries(k, 2, 1)
+    raw, _ = oracle.group_scores(q, summ, 2, 1, aggregate="max")
+    assert raw.tolist() == [[[3.0, 2.0]]]
+    raw_sum, _ = oracle.group_scores(q, summ, 2, 1)
+    assert raw_sum.tolist() == [[[5.0, 3.0]]]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_forced_block_selection_matches_brute_force(seed):
+    """The forced-local-block variant: every (k-1)-subset of the other blocks
+    with the maximum score sum, lowest sorted index tuple on ties, plus the
+    forced block."""
+    rng = np.random.default_rng(seed + 20)
+    n = int(rng.integers(3, 10))
+    scores = rng.integers(-3, 4, size=(3, n)).astype(np.float64)
+    forced = n - 1
+    for k in range(1, n + 1):
+        got = oracle.topk_with_block(scores, k, forced)
+        for r in range(3):
+            rest = [i for i in range(n) if i != forced]
+            best, best_t = None, None
+            for comb in itertools.combinations(rest, k - 1):
+                sm = sum(scores[r, i] for i in comb)
+                if best is None or sm > best or (sm == best and comb < best_t):
+                    best, best_t = sm, comb
+            assert list(got[r]) == sorted(list(best_t) + [forced]), (r, k)
+
+
+@pytest.mark.parametrize("heads", [[0], [2], [1, 3], [0, 1, 2, 3]])
+@pytest.mark.parametrize("integer", [False, True])
+def test_votes_of_chosen_heads_match_brute_force(heads, integer):
+    """Votes restricted to a list of heads (one head: the random-head
+    ablation of the LessIsMore explainer, section 五)."""
+    T, N, W = 40, 12, 3
+    w = small_workload(B=2, Hq=4, Hkv=2, D=8, T=T, dtype="bf16", seed=len(heads) + 7)
+    x = integer_inputs(w, -1, 1) if integer else make_inputs(w)
+    q, k = as_numpy_bits(x["q"]), as_numpy_bits(x["k"])
+    sel, vc = oracle.vote_select(q, k, T, N, W, heads=heads)
+    sets, tallies = brute_vote(bits_to_f64(q), bits_to_f64(k), T, N, W, heads=heads)
+    for b in range(2):
+        assert list(sel[b]) == sets[b]
+        for t in range(T):
+            assert vc[b, t] == tallies[b][t]
+
+
+def test_single_head_vote_is_that_heads_own_top_tokens():
+    """One voting head: the set is that head's own first N-W history tokens by
+    (logit desc, t asc), then the window (numpy lexsort)."""
+    T, N, W = 60, 20, 5
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=8, T=T, dtype="f32", seed=31)
+    sel, _ = oracle.vote_select(q, k, T, N, W, heads=[3])
+    for b in range(2):
+        lg = bits_to_f64(q)[b, 3] @ bits_to_f64(k)[b, 1, :T - W].T
+        order = np.lexsort((np.arange(T - W), -lg))
+        assert list(sel[b]) == sorted(order[:N - W].tolist()) + list(range(T - W, T))
+
+
+# ----------------------------------------------------------------------------- attention recall
+def test_attention_recall_closed_forms():
+    """Recall of every token is 1; of one token, its dense softmax weight
+    (torch.softmax in float64); of a block selection, exp(lse_sel - lse_dense)
+    from the oracle's own two-pass attentions."""
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=16, T=70, dtype="bf16", seed=17)
+    T = 70
+    full = oracle.attention_recall(q, k, T, lambda b, h: range(T))
+    np.testing.assert_allclose(full, 1.0, rtol=0, atol=1e-13)
+    one = oracle.attention_recall(q, k, T, lambda b, h: [5])
+    q64, k64 = torch.from_numpy(bits_to_f64(q)), torch.from_numpy(bits_to_f64(k))
+    for b in range(2):
+        for h in range(4):
+            lg = (k64[b, h // 2, :T] @ q64[b, h]) / math.sqrt(16)
+            assert abs(one[b, h] - float(torch.softmax(lg, 0)[5])) < 1e-14
+    idx = np.array([[[0, 3, 7], [1, 2, 8]], [[4, 5, 6], [0, 1, 2]]], np.int32)
+    rec = oracle.attention_recall(q, k, T, lambda b, h: [
+        t for j in idx[b, h // 2] for t in range(j * 8, min((j + 1) * 8, T))])
+    _, lse_s = oracle.attend_blocks(q, k, v, T, 8, idx)
+    _, lse_d = oracle.attend_dense(q, k, v, T)
+    np.testing.assert_allclose(rec, np.exp(lse_s - lse_d), rtol=1e-12)
