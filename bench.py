@@ -33,6 +33,7 @@ Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--path fused|calls]
     python bench.py --paged uniform|ragged [--workload c2|c3|c5]  # the step on a paged cache
+    python bench.py --schedule [--schedule-layers 36 --select-every 8]  # LessIsMore layers (c4)
     python bench.py --copy-probe      # a plain 1 GiB copy, to calibrate HBM counters
 """
 from __future__ import annotations
@@ -68,6 +69,12 @@ def parse():
     ap.add_argument("--paged", default="none", choices=["none", "uniform", "ragged"],
                     help="block top-k step on a paged cache (random page order): every "
                          "sequence at T, or lengths drawn in [T/2, T]")
+    ap.add_argument("--schedule", action="store_true",
+                    help="c4 shape: a LessIsMore layer schedule (2 dense layers, then a "
+                         "selection layer every --select-every layers, sparse layers between), "
+                         "amortized per layer")
+    ap.add_argument("--schedule-layers", type=int, default=36)
+    ap.add_argument("--select-every", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of 1 GiB (counter calibration)")
     ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -208,6 +215,9 @@ def main():
         return
     if args.paged != "none":
         paged_main(args)
+        return
+    if args.schedule:
+        schedule_main(args)
         return
     if args.counter_summary:
         counter_summary(args)
@@ -612,6 +622,108 @@ def paged_main(args):
                      "bytes_per_launch": step_bytes},
         "cpu_baseline": None,
         "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def schedule_main(args):
+    """One decode step of a whole LessIsMore model at the c4 shape: layers 0
+    and 1 attend densely, layer 2 and every --select-every-th layer after it
+    is a selection layer (dense attention plus the vote, one K read:
+    ksa_vote_layer_decode), and every other layer attends the set chosen by
+    the last selection layer (ksa_sparse_decode, TOKENS).  Each layer has
+    its own KV cache (distinct caches are cycled so no layer reads bytes the
+    previous ones left in the caches).  Compared with every layer dense."""
+    import torch
+
+    import sparse_attention_decode_ksa_amd as ksa
+    from sparse_attention_decode_ksa_amd.inputs import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = ksa.load_library()
+    R = Runner(lib, ksa)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS["c4"]
+    B, Hq, Hkv, D, T, N, W = w.B, w.Hq, w.Hkv, w.D, w.T, w.token_budget, w.recent_window
+    nL, every = args.schedule_layers, args.select_every
+    kinds = []
+    for l in range(nL):
+        if l < 2:
+            kinds.append("dense")
+        elif (l - 2) % every == 0:
+            kinds.append("select")
+        else:
+            kinds.append("sparse")
+    ncache = args.layers or 8
+    t0 = time.time()
+    C = [make_inputs(w, device=dev, seed=w.seed * 1000 + c) for c in range(ncache)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    prob = ksa.Problem(B, Hq, Hkv, D, T, w.cap, 1, ksa.KSA_BF16, 0.0)
+    pp = ctypes.byref(prob)
+    stream = torch.cuda.Stream(device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = lambda t: ctypes.c_void_p(t.data_ptr())
+    n_sel = min(N, T)
+    ws_layer = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_VOTE_LAYER, N), dev)
+    ws_attn = ksa.new_workspace(max(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SPARSE_TOKENS, n_sel),
+                                    ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_DENSE, 0)), dev)
+    idx = torch.empty((B, n_sel), dtype=torch.int32, device=dev)
+    sel = ksa.Selection(ksa.KSA_SEL_TOKENS, V(idx).value, n_sel)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    calls, dense_calls = [], []
+    for l, kind in enumerate(kinds):
+        x = C[l % ncache]
+        dense = (lib.ksa_dense_decode, (pp, V(x["q"]), V(x["k"]), V(x["v"]), V(out), V(lse),
+                                        V(ws_attn), ws_attn.numel(), sp))
+        dense_calls.append(dense)
+        if kind == "dense":
+            calls.append(dense)
+        elif kind == "select":
+            calls.append((lib.ksa_vote_layer_decode,
+                          (pp, V(x["q"]), V(x["k"]), V(x["v"]), N, W, V(out), V(lse), V(idx), None,
+                           V(ws_layer), ws_layer.numel(), sp)))
+        else:
+            calls.append((lib.ksa_sparse_decode,
+                          (pp, V(x["q"]), V(x["k"]), V(x["v"]), ctypes.byref(sel), V(out), V(lse),
+                           V(ws_attn), ws_attn.numel(), sp)))
+
+    def model_step(i):
+        for c in calls:
+            R.run(c)
+
+    def dense_step(i):
+        for c in dense_calls:
+            R.run(c)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(max(1, args.warmup // 4)):
+            model_step(i)
+        steps = max(2, args.steps // 10)
+        ms_model = timed(torch, stream, steps, model_step)
+        dense_step(0)
+        ms_dense = timed(torch, stream, max(2, args.dense_steps // 4), dense_step)
+    per_layer = ms_model / nL
+    cfg = {"workload": "c4 shape, LessIsMore schedule: %d layers, 2 dense, a selection layer every "
+                       "%d from layer 2, sparse layers between" % (nL, every),
+           "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "context": T,
+           "token_budget": N, "recent_window": W, "layers": nL,
+           "selection_layers": kinds.count("select"), "sparse_layers": kinds.count("sparse"),
+           "kv_caches_cycled": ncache}
+    line = {
+        "metric": "decode seqs*steps/s per layer, amortized over the layer schedule, vs every "
+                  "layer dense",
+        "value": round(B / (per_layer * 1e-3), 1), "unit": "seqs*steps/s", "n_gpus": 1,
+        "steps": steps, "warmup": max(1, args.warmup // 4), "ms_per_step": round(ms_model, 5),
+        "ms_per_layer": round(per_layer, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q with planted tokens)", "config": cfg,
+        "dense": {"ms_per_step": round(ms_dense, 5), "ms_per_layer": round(ms_dense / nL, 5)},
+        "speedup_vs_dense": round(ms_dense / ms_model, 3),
+        "roofline": None, "cpu_baseline": None, "input_gen_s": round(gen_s, 2),
     }
     print(json.dumps(line), flush=True)
 

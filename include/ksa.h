@@ -301,6 +301,25 @@ ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, cons
 ksa_status ksa_attention_recall(const float* lse_selected, const float* lse_dense, float* recall,
                                 int32_t count, void* stream);
 
+/* ---------------------------------------------------------------------
+ * ksa_vote_layer_decode -- a token-selection layer of the LessIsMore
+ * schedule (LessIsMore explainer, section 五: full-attention layers first,
+ * then selection layers that compute the full score matrix, let every head
+ * pick, pool and rank the picks and append the most recent tokens, and
+ * sparse layers that attend only that set).  In one call:
+ *   out, lse   = ksa_dense_decode (the layer attends every token);
+ *   token_idx, votes = ksa_vote_select(token_budget, recent_window) on the
+ *                same queries, the set the following sparse layers attend.
+ * For bf16, D = 128 and G in {4, 8} the vote's per-head scores are the
+ * dense attention's own logits (MFMA), so K is read once for both; other
+ * shapes run the dense attention and the vote's scoring as two passes.
+ * token_idx and votes are bitwise those of ksa_vote_select.
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_VOTE_LAYER, token_budget). */
+ksa_status ksa_vote_layer_decode(const ksa_problem* problem, const void* q, const void* k,
+                                 const void* v, int32_t token_budget, int32_t recent_window,
+                                 float* out, float* lse, int32_t* token_idx, uint8_t* votes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Operations for ksa_workspace_bytes. */
 enum {
   KSA_OP_SELECT_TOPK = 0,    /* param: top_k */
@@ -308,7 +327,8 @@ enum {
   KSA_OP_SPARSE_TOKENS = 2,  /* param: selection count (tokens per sequence) */
   KSA_OP_VOTE_SELECT = 3,    /* param: token_budget */
   KSA_OP_DENSE = 4,          /* param: unused */
-  KSA_OP_PAGED_DENSE = 5     /* param: unused */
+  KSA_OP_PAGED_DENSE = 5,    /* param: unused */
+  KSA_OP_VOTE_LAYER = 6      /* param: token_budget */
 };
 
 /* Workspace bytes a call needs for this problem; a pure host function of its

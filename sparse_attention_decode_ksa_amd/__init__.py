@@ -12,7 +12,8 @@ Function names match the C entry points: ``ksa_block_summaries``,
 ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
 ``ksa_paged_dense_decode``, the selection variants ``ksa_select_topk_ex`` and
-``ksa_vote_select_heads``, the diagnostic ``ksa_attention_recall``,
+``ksa_vote_select_heads``, the diagnostic ``ksa_attention_recall``, the
+selection layer ``ksa_vote_layer_decode``,
 ``ksa_workspace_bytes``, ``ksa_status_string``.
 """
 from __future__ import annotations
@@ -32,14 +33,14 @@ KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMA
 KSA_F32, KSA_BF16 = 0, 1
 KSA_SEL_BLOCKS, KSA_SEL_TOKENS = 0, 1
 (KSA_OP_SELECT_TOPK, KSA_OP_SPARSE_BLOCKS, KSA_OP_SPARSE_TOKENS, KSA_OP_VOTE_SELECT,
- KSA_OP_DENSE, KSA_OP_PAGED_DENSE) = range(6)
+ KSA_OP_DENSE, KSA_OP_PAGED_DENSE, KSA_OP_VOTE_LAYER) = range(7)
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode",
             "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
-            "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+            "ksa_vote_layer_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -114,13 +115,14 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_select_topk_ex.argtypes = [PP, P, P, ctypes.POINTER(SelectOptions), P, P, P, SZ, P]
         lib.ksa_vote_select_heads.argtypes = [PP, P, P, I32, I32, P, I32, P, P, P, SZ, P]
         lib.ksa_attention_recall.argtypes = [P, P, P, I32, P]
+        lib.ksa_vote_layer_decode.argtypes = [PP, P, P, P, I32, I32, P, P, P, P, P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:12]:
+        for name in EXPORTED[:13]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -511,3 +513,34 @@ def ksa_attention_recall(lse_selected: torch.Tensor, lse_dense: torch.Tensor, re
                                     _dev(recall, "recall", torch.float32, lse_selected.shape), int(n),
                                     _stream(stream)), "ksa_attention_recall")
     return recall
+
+
+def ksa_vote_layer_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: int,
+                          token_budget: int, recent_window: int, out=None, lse=None,
+                          want_lse: bool = True, token_idx=None, votes=None,
+                          want_votes: bool = False, sm_scale: float = 0.0, workspace=None,
+                          stream=None):
+    """A token-selection layer: dense attention of every head plus the
+    vote-union set from the same logits.  Returns (out [B,Hq,D] fp32,
+    lse [B,Hq] or None, token_idx [B,min(N,T)] int32, votes [B,T] uint8 or None)."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len, 1, sm_scale)
+    B, Hq, D = q.shape
+    n_out = min(token_budget, seq_len)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if token_idx is None:
+        token_idx = torch.empty((B, n_out), dtype=torch.int32, device=q.device)
+    if want_votes and votes is None:
+        votes = torch.empty((B, seq_len), dtype=torch.uint8, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_LAYER, token_budget, q.device, workspace)
+    _check(lib.ksa_vote_layer_decode(
+        ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"), _dev(v, "v", k.dtype, k.shape),
+        int(token_budget), int(recent_window), _dev(out, "out", torch.float32, (B, Hq, D)),
+        _dev(lse, "lse", torch.float32, (B, Hq)),
+        _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
+        _dev(votes, "votes", torch.uint8, (B, seq_len)), pws, nws, _stream(stream)),
+        "ksa_vote_layer_decode")
+    return out, lse, token_idx, votes

@@ -77,6 +77,10 @@ size_t workspace_for(const ksa_problem& p, int32_t op, int32_t param) {
       return attention_workspace_bytes(d, plan_attention(d, 2, d.T));
     case KSA_OP_PAGED_DENSE:
       return attention_workspace_bytes(d, plan_attention(d, 3, (int64_t)d.NB * d.Bs));
+    case KSA_OP_VOTE_LAYER:
+      // the vote's workspace (bound over every window), then the dense partials
+      return ((plan_vote(d, param, 0).total + 255) & ~(size_t)255) +
+             attention_workspace_bytes(d, plan_attention(d, 2, d.T));
     default:
       return SIZE_MAX;
   }
@@ -123,7 +127,7 @@ size_t ksa_workspace_bytes(const ksa_problem* problem, int32_t op, int32_t param
   const bool blocks =
       op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS || op == KSA_OP_PAGED_DENSE;
   if (check_problem(problem, blocks) != KSA_OK) return SIZE_MAX;
-  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_PAGED_DENSE) return SIZE_MAX;
+  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_VOTE_LAYER) return SIZE_MAX;
   if (op != KSA_OP_DENSE && op != KSA_OP_PAGED_DENSE && param < 1) return SIZE_MAX;
   return workspace_for(*problem, op, param);
 }
@@ -369,6 +373,50 @@ ksa_status ksa_attention_recall(const float* lse_selected, const float* lse_dens
     return KSA_ERR_INVALID_ARGUMENT;
   return from_hip(launch_attention_recall(lse_selected, lse_dense, recall, count,
                                           (hipStream_t)stream));
+}
+
+ksa_status ksa_vote_layer_decode(const ksa_problem* problem, const void* q, const void* k,
+                                 const void* v, int32_t token_budget, int32_t recent_window,
+                                 float* out, float* lse, int32_t* token_idx, uint8_t* votes,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, false);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !v || !out || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(out) || !aligned4(token_idx) ||
+      (lse && !aligned4(lse)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan vplan = plan_vote(d, token_budget, recent_window);
+  const size_t voff = (vplan.total + 255) & ~(size_t)255;
+  const AttnPlan aplan = plan_attention(d, 2, d.T);
+  const size_t need = voff + attention_workspace_bytes(d, aplan);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = (hipStream_t)stream;
+  void* aws = (char*)workspace + voff;
+  if (d.T <= token_budget) {
+    hipError_t e = launch_attention(d, 2, q, k, v, nullptr, 0, out, lse, aws, aplan, s);
+    if (e != hipSuccess) return KSA_ERR_HIP;
+    return from_hip(launch_vote_all(d, token_idx, votes, s));
+  }
+  if (dense_emits_vote_keys(d)) {
+    VoteKeys vk;
+    vk.keys = (uint32_t*)((char*)workspace + vplan.keys_off);
+    vk.kstride = vplan.kstride;
+    vk.hist = vplan.hist;
+    hipError_t e = launch_attention(d, 2, q, k, v, nullptr, 0, out, lse, aws, aplan, s, nullptr, &vk);
+    if (e != hipSuccess) return KSA_ERR_HIP;
+    return from_hip(launch_vote_finish(d, token_budget, recent_window, token_idx, votes, workspace,
+                                       vplan, s));
+  }
+  hipError_t e = launch_attention(d, 2, q, k, v, nullptr, 0, out, lse, aws, aplan, s);
+  if (e != hipSuccess) return KSA_ERR_HIP;
+  return from_hip(launch_vote_select(d, q, k, token_budget, recent_window, token_idx, votes,
+                                     workspace, vplan, s));
 }
 
 }  // extern "C"

@@ -182,12 +182,18 @@ size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p) {
 
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse, void* workspace,
-                            const AttnPlan& plan, hipStream_t stream, const PagedKv* paged) {
+                            const AttnPlan& plan, hipStream_t stream, const PagedKv* paged,
+                            const VoteKeys* vote_keys) {
   AttnArgs a = make_attn_args(d, kind, q, k, v, idx, count, out, lse, workspace, plan);
   if (paged) {
     a.table = paged->table;
     a.seq_lens = paged->seq_lens;
     a.tstride = paged->max_blocks;
+  }
+  if (vote_keys) {
+    a.vkeys = vote_keys->keys;
+    a.vkstride = vote_keys->kstride;
+    a.vhist = vote_keys->hist;
   }
   if (d.dtype == KSA_BF16) {
     if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);

@@ -71,6 +71,11 @@ struct AttnArgs {
   const int32_t* seq_lens; // [B]
   int tstride;             // max_blocks
   int page_rows;           // Hkv * Bs: token rows per page
+  // dense (kind 2) on MFMA: the order keys of the raw logits of history
+  // tokens t < vhist go to vkeys [B, Hq, vkstride] (the vote's scores)
+  uint32_t* vkeys;
+  int vkstride;
+  int vhist;
 };
 
 // Kernel arguments of one attention call (host side).  kind: 0 = selected
@@ -106,6 +111,9 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.seq_lens = nullptr;
   a.tstride = 0;
   a.page_rows = d.Hkv * d.Bs;
+  a.vkeys = nullptr;
+  a.vkstride = 0;
+  a.vhist = 0;
   return a;
 }
 
@@ -490,6 +498,22 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
     f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[i]), qop[i], S, 0, 0, 0);
+    if constexpr (KIND == 2) {
+      // the selection layer: keys of head r's raw logits of tokens 4kg..4kg+3
+      // (the vote scorer's arithmetic, so the same keys), 16 bytes at a time
+      if (a.vkeys != nullptr && r < G) {
+        const int t = (c0 + j * nw) * CH + 4 * kg;
+        uint32_t* kout = a.vkeys + ((int64_t)b * d.Hq + g * G + r) * a.vkstride;
+        if (t + 3 < a.vhist) {
+          st16(kout + t, make_uint4(order_key(S[0]), order_key(S[1]), order_key(S[2]),
+                                    order_key(S[3])));
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (t + jj < a.vhist) kout[t + jj] = order_key(S[jj]);
+        }
+      }
+    }
     const uint64_t vm = __ballot(okc);  // bit t (t < 16): chunk token t is attended
     float sv[4];
     bool val[4];

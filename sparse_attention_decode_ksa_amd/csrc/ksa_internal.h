@@ -58,10 +58,16 @@ struct PagedKv {
 // Attention over a row-wise token list.  kind: 0 = selected blocks,
 // 1 = shared token list, 2 = dense range [0, T), 3 = dense over a paged
 // cache (`paged` given; d.T is the longest sequence).
+// Order keys of the raw logits the dense MFMA body writes for the vote.
+struct VoteKeys {
+  uint32_t* keys;  // [B, Hq, kstride]
+  int kstride;
+  int hist;        // tokens t < hist get keys
+};
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse,
                             void* workspace, const AttnPlan& plan, hipStream_t stream,
-                            const PagedKv* paged = nullptr);
+                            const PagedKv* paged = nullptr, const VoteKeys* vote_keys = nullptr);
 
 // recall[i] = exp(lse_sel[i] - lse_dense[i]) for i < n.
 hipError_t launch_attention_recall(const float* lse_sel, const float* lse_dense, float* recall,
@@ -112,5 +118,16 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
                               int32_t* token_idx, uint8_t* votes, void* workspace,
                               const VotePlan& plan, hipStream_t stream,
                               const HeadMask& voting = HeadMask());
+// The vote after the keys are in the workspace (per-head picks, tally, set).
+hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, uint8_t* votes,
+                              void* workspace, const VotePlan& plan, hipStream_t stream,
+                              const HeadMask& voting = HeadMask());
+// T <= N: the whole context, no vote.
+hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hipStream_t stream);
+// Whether dense attention of this shape runs the MFMA body (and can emit the
+// vote's keys while it attends).
+inline bool dense_emits_vote_keys(const Dims& d) {
+  return d.dtype == KSA_BF16 && d.D == 128 && (d.G == 4 || d.G == 8);
+}
 
 }  // namespace ksa

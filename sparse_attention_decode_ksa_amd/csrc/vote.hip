@@ -857,28 +857,15 @@ VotePlan plan_vote(const Dims& d, int N, int W) {
   return p;
 }
 
-hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N, int W,
-                              int32_t* token_idx, uint8_t* votes, void* workspace,
-                              const VotePlan& plan, hipStream_t stream, const HeadMask& voting) {
-  if (d.T <= N) {
-    hipLaunchKernelGGL(vote_all_kernel, dim3((d.T + 255) / 256, d.B), dim3(256), 0, stream, d.T,
-                       token_idx, votes);
-    return hipGetLastError();
-  }
+hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, uint8_t* votes,
+                              void* workspace, const VotePlan& plan, hipStream_t stream,
+                              const HeadMask& voting) {
   char* ws = (char*)workspace;
   uint32_t* keys = (uint32_t*)(ws + plan.keys_off);
   uint32_t* bits = (uint32_t*)(ws + plan.bits_off);
   uint8_t* votes8 = (uint8_t*)(ws + plan.votes_off);
   uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
-  hipError_t e;
-  if (d.dtype == KSA_BF16)
-    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
-                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
-  else
-    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
-                  : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
-  if (e != hipSuccess) return e;
-  e = launch_head_select(d, plan, keys, bits, vhist, voting, stream);
+  hipError_t e = launch_head_select(d, plan, keys, bits, vhist, voting, stream);
   if (e != hipSuccess) return e;
   if (plan.words <= kSetThreads) {
     if (d.Hq < 64)
@@ -897,6 +884,28 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
   hipLaunchKernelGGL(vote_set_kernel, dim3(d.B), dim3(kSetThreads), 0, stream, votes8, vhist, d.T,
                      plan.hist, plan.kv, N, W, token_idx, votes);
   return hipGetLastError();
+}
+
+hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hipStream_t stream) {
+  hipLaunchKernelGGL(vote_all_kernel, dim3((d.T + 255) / 256, d.B), dim3(256), 0, stream, d.T,
+                     token_idx, votes);
+  return hipGetLastError();
+}
+
+hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N, int W,
+                              int32_t* token_idx, uint8_t* votes, void* workspace,
+                              const VotePlan& plan, hipStream_t stream, const HeadMask& voting) {
+  if (d.T <= N) return launch_vote_all(d, token_idx, votes, stream);
+  uint32_t* keys = (uint32_t*)((char*)workspace + plan.keys_off);
+  hipError_t e;
+  if (d.dtype == KSA_BF16)
+    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
+                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
+  else
+    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
+                  : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
+  if (e != hipSuccess) return e;
+  return launch_vote_finish(d, N, W, token_idx, votes, workspace, plan, stream, voting);
 }
 
 }  // namespace ksa

@@ -147,3 +147,42 @@ def test_recall_on_the_c2_workload_is_high():
     assert rec.min() > 0.0 and rec.max() <= 1.0 + 1e-5
     print("c2 recall: median %.3f, min %.3f" % (float(np.median(rec)), float(rec.min())))
     assert float(np.median(rec)) > 64 / 1024
+
+
+# ----------------------------------------------------------------------------- selection layer
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,T,N,W", [
+    (32, 8, 128, "bf16", 5000, 1024, 256),    # G = 4, MFMA: one K read
+    (16, 2, 128, "bf16", 3001, 512, 128),     # G = 8, MFMA, ragged key tail
+    (8, 4, 128, "bf16", 4000, 512, 128),      # G = 2: dense and the vote's scoring apart
+    (4, 2, 64, "f32", 1500, 256, 64),
+    (8, 2, 128, "bf16", 300, 512, 128),       # T <= N: every token, no vote
+])
+def test_vote_layer_equals_dense_plus_vote(Hq, Hkv, D, dtype, T, N, W):
+    """The selection layer's output is ksa_dense_decode's and its set and
+    votes are ksa_vote_select's, bit for bit; the set also passes the
+    oracle's vote rule."""
+    w = small_workload(B=2, Hq=Hq, Hkv=Hkv, D=D, T=T, dtype=dtype, seed=T + N)
+    q, k, v = gpu_inputs(w)
+    out, lse, idx, votes = ksa.ksa_vote_layer_decode(q, k, v, w.T, N, W, want_votes=True)
+    dout, dlse = ksa.ksa_dense_decode(q, k, v, w.T)
+    ridx, rvotes = ksa.ksa_vote_select(q, k, w.T, N, W, want_votes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dout) and torch.equal(lse, dlse)
+    assert torch.equal(idx, ridx) and torch.equal(votes, rvotes)
+    if T > N:
+        lg = oracle.head_logits(np_bits(q), np_bits(k), w.T)
+        check_votes(votes.cpu().numpy(), idx.cpu().numpy(), lg, N, W)
+
+
+def test_vote_layer_on_c4():
+    w = WORKLOADS["c4"]
+    q, k, v = gpu_inputs(w)
+    N, W = w.token_budget, w.recent_window
+    out, lse, idx, votes = ksa.ksa_vote_layer_decode(q, k, v, w.T, N, W, want_votes=True)
+    dout, dlse = ksa.ksa_dense_decode(q, k, v, w.T)
+    ridx, rvotes = ksa.ksa_vote_select(q, k, w.T, N, W, want_votes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dout) and torch.equal(lse, dlse)
+    assert torch.equal(idx, ridx) and torch.equal(votes, rvotes)
+    del q, k, v
+    torch.cuda.empty_cache()
