@@ -90,7 +90,7 @@ typedef struct {
   float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(D) */
 } ksa_problem;
 
-typedef enum { KSA_SEL_BLOCKS = 0, KSA_SEL_TOKENS = 1 } ksa_sel_kind;
+typedef enum { KSA_SEL_BLOCKS = 0, KSA_SEL_TOKENS = 1, KSA_SEL_HEAD_TOKENS = 2 } ksa_sel_kind;
 
 /* What ksa_sparse_decode attends.
  *   BLOCKS: idx is [B, Hkv, count] int32 -- for each (sequence, KV head) the
@@ -98,7 +98,11 @@ typedef enum { KSA_SEL_BLOCKS = 0, KSA_SEL_TOKENS = 1 } ksa_sel_kind;
  *           ksa_select_topk); all G query heads of the group attend them.
  *   TOKENS: idx is [B, count] int32 -- for each sequence `count` distinct
  *           token ids < T, ascending (the output of ksa_vote_select); every
- *           query head of the sequence attends them. */
+ *           query head of the sequence attends them.
+ *   HEAD_TOKENS: idx is [B, Hq, count] int32 -- a list per query head
+ *           (distinct, ascending, < T; the output of ksa_vote_select_per_head);
+ *           the per-head-sets ablation, which reads K/V once per query head
+ *           rather than once per group. */
 typedef struct {
   ksa_sel_kind kind;
   const int32_t* idx; /* device pointer */
@@ -291,6 +295,17 @@ ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, cons
                                  int32_t* token_idx, uint8_t* votes, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ksa_vote_select_per_head -- the per-head-sets ablation (LessIsMore
+ * explainer, section 五: each head keeps its own set): every query head h
+ * keeps its own first Kv = N - W history tokens by (q_h . k desc, t asc),
+ * ascending, followed by the W most recent tokens; token_idx is
+ * [B, Hq, min(N, T)] int32 (all tokens when T <= N), for ksa_sparse_decode
+ * with KSA_SEL_HEAD_TOKENS.  Same limits and workspace as ksa_vote_select. */
+ksa_status ksa_vote_select_per_head(const ksa_problem* problem, const void* q, const void* k,
+                                    int32_t token_budget, int32_t recent_window,
+                                    int32_t* token_idx, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* ksa_attention_recall -- the share of each query head's dense softmax mass
  * that a selection covers (the attention recall the LessIsMore explainer,
  * sections 四 and 五, judges selections by): with lse_selected from
@@ -328,7 +343,8 @@ enum {
   KSA_OP_VOTE_SELECT = 3,    /* param: token_budget */
   KSA_OP_DENSE = 4,          /* param: unused */
   KSA_OP_PAGED_DENSE = 5,    /* param: unused */
-  KSA_OP_VOTE_LAYER = 6      /* param: token_budget */
+  KSA_OP_VOTE_LAYER = 6,     /* param: token_budget */
+  KSA_OP_SPARSE_HEAD_TOKENS = 7 /* param: selection count (tokens per query head) */
 };
 
 /* Workspace bytes a call needs for this problem; a pure host function of its

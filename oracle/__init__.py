@@ -288,6 +288,42 @@ def set_from_votes(vote_counts: np.ndarray, N: int, W: int) -> np.ndarray:
     return out
 
 
+def head_sets(logits: np.ndarray, N: int, W: int) -> np.ndarray:
+    """The per-head-sets ablation (LessIsMore explainer, section 五: each
+    head keeps its own set): for every head, its first N-W history tokens by
+    (logit desc, t asc), ascending, then the W most recent tokens; all of
+    [0, T) when T <= N.  logits [B,Hq,T] -> [B,Hq,min(N,T)] int32."""
+    B, Hq, T = logits.shape
+    if T <= N:
+        return np.broadcast_to(np.arange(T, dtype=np.int32), (B, Hq, T)).copy()
+    C, Kv = T - W, N - W
+    out = np.zeros((B, Hq, N), np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            picks = topk(logits[b, h, :C][None], Kv)[0]
+            out[b, h] = np.concatenate([picks, np.arange(C, T)])
+    return out
+
+
+def attend_head_tokens(q, k, v, T: int, token_idx: np.ndarray, sm_scale: float = 0.0):
+    """Exact softmax attention of every query head over its own list
+    token_idx[b, h] (the per-head-sets ablation): the shared-list attention
+    of a one-head problem per (b, h).  Returns (out [B,Hq,D], lse [B,Hq])."""
+    B, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros(q.shape, np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            o, l = attend_tokens(np.ascontiguousarray(q[b:b + 1, h:h + 1]),
+                                 np.ascontiguousarray(k[b:b + 1, g:g + 1]),
+                                 np.ascontiguousarray(v[b:b + 1, g:g + 1]), T,
+                                 np.ascontiguousarray(token_idx[b:b + 1, h]), sm_scale)
+            out[b, h], lse[b, h] = o[0, 0], l[0, 0]
+    return out, lse
+
+
 def vote_select(q, k, T: int, N: int, W: int, heads=None):
     """Whole vote-union selection: returns (token_idx [B,min(N,T)], votes [B,T]);
     `heads` as in votes."""

@@ -31,16 +31,17 @@ LIB_PATH = os.environ.get("KSA_LIB", os.path.join(_HERE, "libksa.so"))
 
 KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMALL, KSA_ERR_HIP = range(5)
 KSA_F32, KSA_BF16 = 0, 1
-KSA_SEL_BLOCKS, KSA_SEL_TOKENS = 0, 1
+KSA_SEL_BLOCKS, KSA_SEL_TOKENS, KSA_SEL_HEAD_TOKENS = 0, 1, 2
 (KSA_OP_SELECT_TOPK, KSA_OP_SPARSE_BLOCKS, KSA_OP_SPARSE_TOKENS, KSA_OP_VOTE_SELECT,
- KSA_OP_DENSE, KSA_OP_PAGED_DENSE, KSA_OP_VOTE_LAYER) = range(7)
+ KSA_OP_DENSE, KSA_OP_PAGED_DENSE, KSA_OP_VOTE_LAYER, KSA_OP_SPARSE_HEAD_TOKENS) = range(8)
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode",
             "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
-            "ksa_vote_layer_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+            "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_workspace_bytes",
+            "ksa_status_string", "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -116,13 +117,14 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_vote_select_heads.argtypes = [PP, P, P, I32, I32, P, I32, P, P, P, SZ, P]
         lib.ksa_attention_recall.argtypes = [P, P, P, I32, P]
         lib.ksa_vote_layer_decode.argtypes = [PP, P, P, P, I32, I32, P, P, P, P, P, SZ, P]
+        lib.ksa_vote_select_per_head.argtypes = [PP, P, P, I32, I32, P, P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:13]:
+        for name in EXPORTED[:14]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -256,7 +258,8 @@ def ksa_sparse_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len
                       out=None, lse=None, want_lse: bool = True, sm_scale: float = 0.0,
                       workspace=None, stream=None):
     """Attention of every query head over the selected blocks (kind BLOCKS,
-    idx [B,Hkv,count]) or the shared token list (kind TOKENS, idx [B,count]).
+    idx [B,Hkv,count]), the shared token list (kind TOKENS, idx [B,count]) or
+    a list per query head (kind HEAD_TOKENS, idx [B,Hq,count]).
     Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None)."""
     lib = load_library()
     prob = make_problem(q, k, seq_len, block_size, sm_scale)
@@ -266,9 +269,11 @@ def ksa_sparse_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ishape = (B, prob.num_kv_heads, count) if kind == KSA_SEL_BLOCKS else (B, count)
+    ishape = {KSA_SEL_BLOCKS: (B, prob.num_kv_heads, count), KSA_SEL_TOKENS: (B, count),
+              KSA_SEL_HEAD_TOKENS: (B, Hq, count)}[kind]
     sel = Selection(int(kind), _dev(idx, "idx", torch.int32, ishape), int(count))
-    op = KSA_OP_SPARSE_BLOCKS if kind == KSA_SEL_BLOCKS else KSA_OP_SPARSE_TOKENS
+    op = {KSA_SEL_BLOCKS: KSA_OP_SPARSE_BLOCKS, KSA_SEL_TOKENS: KSA_OP_SPARSE_TOKENS,
+          KSA_SEL_HEAD_TOKENS: KSA_OP_SPARSE_HEAD_TOKENS}[kind]
     ws, pws, nws = _workspace(prob, op, count, q.device, workspace)
     _check(lib.ksa_sparse_decode(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
                                  _dev(v, "v", k.dtype, k.shape), ctypes.byref(sel),
@@ -544,3 +549,21 @@ def ksa_vote_layer_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq
         _dev(votes, "votes", torch.uint8, (B, seq_len)), pws, nws, _stream(stream)),
         "ksa_vote_layer_decode")
     return out, lse, token_idx, votes
+
+
+def ksa_vote_select_per_head(q: torch.Tensor, k: torch.Tensor, seq_len: int, token_budget: int,
+                             recent_window: int, token_idx=None, workspace=None, stream=None):
+    """Per-head sets [B, Hq, min(N,T)] int32: every head's own picks plus the
+    recency window (attend them with ksa_sparse_decode, KSA_SEL_HEAD_TOKENS)."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len)
+    B, Hq = q.shape[0], q.shape[1]
+    n_out = min(token_budget, seq_len)
+    if token_idx is None:
+        token_idx = torch.empty((B, Hq, n_out), dtype=torch.int32, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_SELECT, token_budget, q.device, workspace)
+    _check(lib.ksa_vote_select_per_head(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
+                                        int(token_budget), int(recent_window),
+                                        _dev(token_idx, "token_idx", torch.int32, (B, Hq, n_out)),
+                                        pws, nws, _stream(stream)), "ksa_vote_select_per_head")
+    return token_idx

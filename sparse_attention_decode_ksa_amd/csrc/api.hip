@@ -77,6 +77,12 @@ size_t workspace_for(const ksa_problem& p, int32_t op, int32_t param) {
       return attention_workspace_bytes(d, plan_attention(d, 2, d.T));
     case KSA_OP_PAGED_DENSE:
       return attention_workspace_bytes(d, plan_attention(d, 3, (int64_t)d.NB * d.Bs));
+    case KSA_OP_SPARSE_HEAD_TOKENS: {
+      Dims dh = d;
+      dh.Hkv = d.Hq;
+      dh.G = 1;
+      return attention_workspace_bytes(dh, plan_attention(dh, 4, param));
+    }
     case KSA_OP_VOTE_LAYER:
       // the vote's workspace (bound over every window), then the dense partials
       return ((plan_vote(d, param, 0).total + 255) & ~(size_t)255) +
@@ -127,7 +133,7 @@ size_t ksa_workspace_bytes(const ksa_problem* problem, int32_t op, int32_t param
   const bool blocks =
       op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS || op == KSA_OP_PAGED_DENSE;
   if (check_problem(problem, blocks) != KSA_OK) return SIZE_MAX;
-  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_VOTE_LAYER) return SIZE_MAX;
+  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_SPARSE_HEAD_TOKENS) return SIZE_MAX;
   if (op != KSA_OP_DENSE && op != KSA_OP_PAGED_DENSE && param < 1) return SIZE_MAX;
   return workspace_for(*problem, op, param);
 }
@@ -168,7 +174,8 @@ ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const vo
                              void* workspace, size_t workspace_bytes, void* stream) {
   if (!sel) return KSA_ERR_INVALID_ARGUMENT;
   const bool blocks = sel->kind == KSA_SEL_BLOCKS;
-  if (!blocks && sel->kind != KSA_SEL_TOKENS) return KSA_ERR_INVALID_ARGUMENT;
+  if (!blocks && sel->kind != KSA_SEL_TOKENS && sel->kind != KSA_SEL_HEAD_TOKENS)
+    return KSA_ERR_INVALID_ARGUMENT;
   ksa_status st = check_problem(problem, blocks);
   if (st != KSA_OK) return st;
   const Dims d = make_dims(*problem);
@@ -180,6 +187,17 @@ ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const vo
   if (blocks && sel->count > d.NB) return KSA_ERR_INVALID_ARGUMENT;
   if (!blocks && sel->count > d.T) return KSA_ERR_INVALID_ARGUMENT;
   if (blocks && (int64_t)sel->count * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
+  if (sel->kind == KSA_SEL_HEAD_TOKENS) {  // rows are query heads, each its own group
+    Dims dh = d;
+    dh.Hkv = d.Hq;
+    dh.G = 1;
+    const AttnPlan plan = plan_attention(dh, 4, sel->count);
+    const size_t need = attention_workspace_bytes(dh, plan);
+    if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+    if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+    return from_hip(launch_attention(dh, 4, q, k, v, sel->idx, sel->count, out, lse, workspace,
+                                     plan, (hipStream_t)stream, nullptr, nullptr, d.G));
+  }
   const int64_t ltot = blocks ? (int64_t)sel->count * d.Bs : sel->count;
   const AttnPlan plan = plan_attention(d, blocks ? 0 : 1, ltot);
   const size_t need = attention_workspace_bytes(d, plan);
@@ -417,6 +435,26 @@ ksa_status ksa_vote_layer_decode(const ksa_problem* problem, const void* q, cons
   if (e != hipSuccess) return KSA_ERR_HIP;
   return from_hip(launch_vote_select(d, q, k, token_budget, recent_window, token_idx, votes,
                                      workspace, vplan, s));
+}
+
+ksa_status ksa_vote_select_per_head(const ksa_problem* problem, const void* q, const void* k,
+                                    int32_t token_budget, int32_t recent_window,
+                                    int32_t* token_idx, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  ksa_status st = check_problem(problem, false);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned4(token_idx)) return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan plan = plan_vote(d, token_budget, recent_window);
+  if (workspace_bytes < plan.total) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.total && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_vote_per_head(d, q, k, token_budget, recent_window, token_idx, workspace,
+                                       plan, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -107,6 +107,9 @@ hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStrea
   constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
   if (kind == 3) {
     hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G>), grid, block, 0, s, a);
+  } else if (kind == 4) {  // rows are query heads: one head per row
+    if constexpr (G == 1)
+      hipLaunchKernelGGL((attn_partial_kernel<T, D, 1, 4>), grid, block, 0, s, a);
   } else if constexpr (mfma) {
     switch (kind) {
       case 0: hipLaunchKernelGGL((attn_mfma_kernel<G, 0>), grid, block, 0, s, a); break;
@@ -165,7 +168,7 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   }
   // a workgroup's index slice must fit the LDS stage
   int64_t cap = INT64_MAX;
-  if (kind == 1) cap = kIdxStage / ch;
+  if (kind == 1 || kind == 4) cap = kIdxStage / ch;
   if (kind == 0 || kind == 3) cap = ((int64_t)(kIdxStage - 2) * d.Bs) / ch;
   if (cps > cap) cps = cap;
   if (cps < 1) cps = 1;
@@ -183,7 +186,7 @@ size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p) {
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse, void* workspace,
                             const AttnPlan& plan, hipStream_t stream, const PagedKv* paged,
-                            const VoteKeys* vote_keys) {
+                            const VoteKeys* vote_keys, int kv_div) {
   AttnArgs a = make_attn_args(d, kind, q, k, v, idx, count, out, lse, workspace, plan);
   if (paged) {
     a.table = paged->table;
@@ -195,6 +198,7 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
     a.vkstride = vote_keys->kstride;
     a.vhist = vote_keys->hist;
   }
+  if (kind == 4) a.kv_div = kv_div;
   if (d.dtype == KSA_BF16) {
     if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);
     return launch_g<uint16_t, 128>(a, kind, plan, stream);

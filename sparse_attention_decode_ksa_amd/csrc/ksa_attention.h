@@ -76,12 +76,15 @@ struct AttnArgs {
   uint32_t* vkeys;
   int vkstride;
   int vhist;
+  // kind 4 (one token list per query head): the rows are query heads
+  // (d.Hkv = Hq, d.G = 1) and row (b, h) reads KV head h / kv_div
+  int kv_div;
 };
 
 // Kernel arguments of one attention call (host side).  kind: 0 = selected
 // blocks, 1 = shared token list, 2 = dense range [0, T), 3 = blocks of a
 // paged cache (logical ids and their pages staged in LDS; the per-row
-// length is set by the kernel).
+// length is set by the kernel), 4 = a token list per query head.
 inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const void* k, const void* v,
                                const int32_t* idx, int count, float* out, float* lse,
                                void* workspace, const AttnPlan& plan) {
@@ -92,7 +95,7 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.idx = idx;
   a.count = count;
   a.d = d;
-  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs : (kind == 1 ? count : d.T);
+  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs : ((kind == 1 || kind == 4) ? count : d.T);
   a.bs_shift = -1;
   if ((kind == 0 || kind == 3) && (d.Bs & (d.Bs - 1)) == 0) {
     int sh = 0;
@@ -114,6 +117,7 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.vkeys = nullptr;
   a.vkstride = 0;
   a.vhist = 0;
+  a.kv_div = 1;
   return a;
 }
 
@@ -130,7 +134,7 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_id
     if constexpr (KIND == 2) {
       ok[i] = p < a.d.T;
       tok[i] = ok[i] ? p : 0;
-    } else if constexpr (KIND == 1) {
+    } else if constexpr (KIND == 1 || KIND == 4) {
       ok[i] = p < a.ltot;
       const int at = min(max(p - e0, 0), kIdxStage - 1);  // in range whenever ok
       tok[i] = ok[i] ? s_idx[at] : 0;
@@ -280,7 +284,8 @@ __device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int spl
     const int b = row / d.Hkv;
     e0 = c_begin * CH;
     e1 = min(a.ltot, c_end * CH);
-    src = a.idx + (int64_t)b * a.count;
+    // kind 1: the sequence's list; kind 4: the row's (query head's) own list
+    src = a.idx + (int64_t)(KIND == 4 ? row : b) * a.count;
   }
   for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
   return e0;
@@ -310,7 +315,10 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   const int slot = lane / LPT, li = lane % LPT;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const int64_t kvrow =
-      (KIND == 3 ? (int64_t)g * d.Bs * D : (int64_t)row * d.Tcap * D) + li * EPL;
+      (KIND == 3   ? (int64_t)g * d.Bs * D
+       : KIND == 4 ? ((int64_t)b * (d.Hkv / a.kv_div) + g / a.kv_div) * d.Tcap * D
+                   : (int64_t)row * d.Tcap * D) +
+      li * EPL;
   const T* kbase = (const T*)a.k + kvrow;
   const T* vbase = (const T*)a.v + kvrow;
 

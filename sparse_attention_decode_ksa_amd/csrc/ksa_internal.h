@@ -64,10 +64,13 @@ struct VoteKeys {
   int kstride;
   int hist;        // tokens t < hist get keys
 };
+// kind 4 (a token list per query head) takes d with Hkv = Hq and G = 1 and
+// kv_div = the real G: row (b, h) reads KV head h / kv_div.
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse,
                             void* workspace, const AttnPlan& plan, hipStream_t stream,
-                            const PagedKv* paged = nullptr, const VoteKeys* vote_keys = nullptr);
+                            const PagedKv* paged = nullptr, const VoteKeys* vote_keys = nullptr,
+                            int kv_div = 1);
 
 // recall[i] = exp(lse_sel[i] - lse_dense[i]) for i < n.
 hipError_t launch_attention_recall(const float* lse_sel, const float* lse_dense, float* recall,
@@ -124,6 +127,10 @@ hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, u
                               const HeadMask& voting = HeadMask());
 // T <= N: the whole context, no vote.
 hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hipStream_t stream);
+// Per-head sets: every head's own picks plus the window, token_idx [B, Hq, min(N, T)].
+hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
+                                int32_t* token_idx, void* workspace, const VotePlan& plan,
+                                hipStream_t stream);
 // Whether dense attention of this shape runs the MFMA body (and can emit the
 // vote's keys while it attends).
 inline bool dense_emits_vote_keys(const Dims& d) {

@@ -26,6 +26,7 @@
 // Everything after the fp32 scores is exact integer work.
 #include <float.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ksa_device.h"
@@ -855,6 +856,77 @@ VotePlan plan_vote(const Dims& d, int N, int W) {
   p.total = p.vhist_off + (size_t)d.B * 256 * sizeof(uint32_t);
   if (d.T <= N) p.total = 0;
   return p;
+}
+
+namespace {
+// Per (b, h), the per-head-sets ablation: the head's own picks (its bitmask,
+// exactly Kv bits) in ascending order, then the W most recent tokens.
+// Thread t owns words [t*R, (t+1)*R) of the bitmask; one workgroup scan.
+constexpr int kHeadSetThreads = 256;
+__global__ __launch_bounds__(kHeadSetThreads) void head_set_kernel(
+    const uint32_t* __restrict__ bits, int words, int hist, int kv, int W, int n_out,
+    int32_t* __restrict__ token_idx) {
+  __shared__ uint32_t s_scan[16];
+  const int tid = threadIdx.x;
+  const int64_t hr = blockIdx.x;
+  const uint32_t* br = bits + hr * words;
+  int32_t* out = token_idx + hr * n_out;
+  for (int i = tid; i < W; i += kHeadSetThreads) out[kv + i] = hist + i;
+  const int R = (words + kHeadSetThreads - 1) / kHeadSetThreads;
+  uint32_t n = 0;
+  for (int r = 0; r < R; ++r) {
+    const int w = tid * R + r;
+    if (w < words) n += (uint32_t)__popc(br[w]);
+  }
+  uint32_t pos = block_excl_scan32(n, s_scan);
+  for (int r = 0; r < R; ++r) {
+    const int w = tid * R + r;
+    if (w >= words) break;
+    uint32_t m = br[w];
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1u;
+      if (pos < (uint32_t)kv) out[pos] = w * 32 + j;
+      ++pos;
+    }
+  }
+}
+
+// T <= N: every head attends the whole context.
+__global__ void head_all_kernel(int T, int rows, int32_t* __restrict__ token_idx) {
+  const int64_t n = (int64_t)rows * T;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    token_idx[i] = (int32_t)(i % T);
+}
+}  // namespace
+
+hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
+                                int32_t* token_idx, void* workspace, const VotePlan& plan,
+                                hipStream_t stream) {
+  const int rows = d.B * d.Hq;
+  if (d.T <= N) {
+    hipLaunchKernelGGL(head_all_kernel, dim3(std::min<int64_t>(4096, ((int64_t)rows * d.T + 255) / 256)),
+                       dim3(256), 0, stream, d.T, rows, token_idx);
+    return hipGetLastError();
+  }
+  char* ws = (char*)workspace;
+  uint32_t* keys = (uint32_t*)(ws + plan.keys_off);
+  uint32_t* bits = (uint32_t*)(ws + plan.bits_off);
+  uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
+  hipError_t e;
+  if (d.dtype == KSA_BF16)
+    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
+                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
+  else
+    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
+                  : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
+  if (e != hipSuccess) return e;
+  e = launch_head_select(d, plan, keys, bits, vhist, HeadMask(), stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_set_kernel, dim3(rows), dim3(kHeadSetThreads), 0, stream, bits,
+                     plan.words, plan.hist, plan.kv, W, N, token_idx);
+  return hipGetLastError();
 }
 
 hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, uint8_t* votes,

@@ -186,3 +186,66 @@ def test_vote_layer_on_c4():
     assert torch.equal(idx, ridx) and torch.equal(votes, rvotes)
     del q, k, v
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- per-head sets
+def check_head_sets(gpu, lg, N, W):
+    """Every head's set is the oracle's except at near-ties of that head's
+    threshold (relative gap < 1e-5 of its max |logit|)."""
+    from parity import REL_TIE
+    ref = oracle.head_sets(lg, N, W)
+    B, Hq, T = lg.shape
+    assert gpu.shape == ref.shape
+    for b in range(B):
+        for h in range(Hq):
+            g_, r_ = set(gpu[b, h].tolist()), set(ref[b, h].tolist())
+            assert np.all(np.diff(gpu[b, h]) > 0)
+            if g_ == r_:
+                continue
+            C = T - W
+            thr = np.sort(lg[b, h, :C])[::-1][N - W - 1]
+            tol = REL_TIE * np.abs(lg[b, h, :C]).max()
+            for t in g_ ^ r_:
+                assert t < C and abs(lg[b, h, t] - thr) <= tol, (b, h, t)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,T,N,W", [
+    (32, 8, 128, "bf16", 4000, 512, 128),
+    (8, 2, 64, "f32", 2100, 300, 60),
+    (4, 4, 128, "bf16", 1000, 100, 0),
+    (8, 2, 128, "bf16", 300, 512, 128),   # T <= N
+])
+def test_per_head_sets_and_their_attention(Hq, Hkv, D, dtype, T, N, W):
+    w = small_workload(B=2, Hq=Hq, Hkv=Hkv, D=D, T=T, dtype=dtype, seed=T + Hq)
+    q, k, v = gpu_inputs(w)
+    idx = ksa.ksa_vote_select_per_head(q, k, w.T, N, W)
+    out, lse = ksa.ksa_sparse_decode(q, k, v, w.T, idx, ksa.KSA_SEL_HEAD_TOKENS)
+    torch.cuda.synchronize()
+    lg = oracle.head_logits(np_bits(q), np_bits(k), w.T)
+    ids = idx.cpu().numpy()
+    check_head_sets(ids, lg, N, W)
+    ro, rl = oracle.attend_head_tokens(np_bits(q), np_bits(k), np_bits(v), w.T, ids)
+    from parity import check_attention
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
+
+
+def test_per_head_sets_integer_bit_exact():
+    w = small_workload(B=2, Hq=8, Hkv=2, D=64, T=1500, dtype="bf16", seed=8)
+    q, k, v = gpu_inputs(w, integer=True, lo=-1, hi=1)
+    idx = ksa.ksa_vote_select_per_head(q, k, w.T, 256, 64)
+    torch.cuda.synchronize()
+    lg = oracle.head_logits(np_bits(q), np_bits(k), w.T)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.head_sets(lg, 256, 64))
+
+
+def test_head_token_attention_with_one_list_per_head_equals_shared_list():
+    """Giving every head the same list reproduces the shared-list attention
+    (to fp32 merge order: the two read K/V in different row groupings)."""
+    w = small_workload(B=2, Hq=8, Hkv=2, D=128, T=3000, dtype="bf16", seed=13)
+    q, k, v = gpu_inputs(w)
+    shared = ksa.ksa_vote_select(q, k, w.T, 512, 128)
+    per_head = shared[:, None, :].expand(w.B, w.Hq, shared.shape[1]).contiguous()
+    o1, l1 = ksa.ksa_sparse_decode(q, k, v, w.T, shared, ksa.KSA_SEL_TOKENS)
+    o2, l2 = ksa.ksa_sparse_decode(q, k, v, w.T, per_head, ksa.KSA_SEL_HEAD_TOKENS)
+    torch.cuda.synchronize()
+    assert float((o1 - o2).abs().max()) <= 1e-5 and float((l1 - l2).abs().max()) <= 1e-5

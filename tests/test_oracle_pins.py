@@ -534,3 +534,41 @@ def test_attention_recall_closed_forms():
     _, lse_s = oracle.attend_blocks(q, k, v, T, 8, idx)
     _, lse_d = oracle.attend_dense(q, k, v, T)
     np.testing.assert_allclose(rec, np.exp(lse_s - lse_d), rtol=1e-12)
+
+
+def test_head_sets_match_brute_force():
+    """Per-head sets (LessIsMore explainer §五 ablation): each head's own first
+    N-W history tokens by Python sorted (logit desc, t asc), then the window."""
+    T, N, W = 50, 14, 4
+    w = small_workload(B=2, Hq=4, Hkv=2, D=8, T=T, dtype="bf16", seed=44)
+    x = integer_inputs(w, -1, 1)
+    q, k = as_numpy_bits(x["q"]), as_numpy_bits(x["k"])
+    lg = oracle.head_logits(q, k, T)
+    got = oracle.head_sets(lg, N, W)
+    q64, k64 = bits_to_f64(q), bits_to_f64(k)
+    for b in range(2):
+        for h in range(4):
+            l = [float(np.dot(q64[b, h], k64[b, h // 2, t])) for t in range(T - W)]
+            order = sorted(range(T - W), key=lambda t: (-l[t], t))
+            assert list(got[b, h]) == sorted(order[:N - W]) + list(range(T - W, T))
+    assert oracle.head_sets(lg, 60, 4).tolist() == [[list(range(50))] * 4] * 2  # T <= N
+
+
+def test_head_token_attention_matches_masked_sdpa():
+    """Attention over a list per query head = SDPA (float64) with a per-head
+    mask keeping exactly that head's tokens."""
+    T = 40
+    w, q, k, v = rand_problem(B=2, Hq=4, Hkv=2, D=16, T=T, dtype="f32", seed=5)
+    rng = np.random.default_rng(3)
+    idx = np.stack([np.stack([np.sort(rng.choice(T, 9, replace=False)) for _ in range(4)])
+                    for _ in range(2)]).astype(np.int32)
+    out, lse = oracle.attend_head_tokens(q, k, v, T, idx)
+    q64, k64, v64 = (torch.from_numpy(bits_to_f64(a)) for a in (q, k, v))
+    for b in range(2):
+        for h in range(4):
+            mask = torch.full((T,), float("-inf"), dtype=torch.float64)
+            mask[torch.from_numpy(idx[b, h].astype(np.int64))] = 0.0
+            lg = (k64[b, h // 2, :T] @ q64[b, h]) / math.sqrt(16) + mask
+            p = torch.softmax(lg, 0)
+            np.testing.assert_allclose(out[b, h], (p @ v64[b, h // 2, :T]).numpy(), atol=1e-12)
+            assert abs(lse[b, h] - float(torch.logsumexp(lg, 0))) < 1e-12
