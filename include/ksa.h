@@ -260,6 +260,29 @@ ksa_status ksa_paged_dense_decode(const ksa_problem* problem, const ksa_paged_kv
                                   const void* q, const void* k_pool, const void* v_pool, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ksa_paged_vote_select -- ksa_vote_select on a paged cache with
+ * per-sequence lengths: sequence b votes over its own history [0, T_b - W)
+ * when T_b > N, else takes all of [0, T_b).  token_idx is [B, min(N, T)]
+ * int32 (T the longest sequence), each row ascending and padded with -1;
+ * votes (nullable) is [B, T] uint8, zero past each sequence's history.
+ * Requires T - W <= 32768 here (else KSA_ERR_UNSUPPORTED).
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_VOTE_SELECT, token_budget). */
+ksa_status ksa_paged_vote_select(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                 const void* q, const void* k_pool, int32_t token_budget,
+                                 int32_t recent_window, int32_t* token_idx, uint8_t* votes,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ksa_paged_sparse_decode -- ksa_sparse_decode on a paged cache with
+ * per-sequence lengths, for BLOCKS (logical block ids [B, Hkv, count], e.g.
+ * ksa_paged_block_topk_decode's) and TOKENS (token ids [B, count], e.g.
+ * ksa_paged_vote_select's); negative entries are padding and are skipped,
+ * as are tokens at or past T_b.  workspace: ksa_workspace_bytes(problem,
+ * KSA_OP_SPARSE_BLOCKS or KSA_OP_SPARSE_TOKENS, sel->count). */
+ksa_status ksa_paged_sparse_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                   const void* q, const void* k_pool, const void* v_pool,
+                                   const ksa_selection* sel, float* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------
  * Selection variants (the ablations the pages report) and a quality signal.
  *

@@ -40,8 +40,8 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_block_topk_decode", "ksa_vote_select", "ksa_dense_decode",
             "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
-            "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_workspace_bytes",
-            "ksa_status_string", "ksa_version")
+            "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
+            "ksa_paged_sparse_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -118,13 +118,16 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_attention_recall.argtypes = [P, P, P, I32, P]
         lib.ksa_vote_layer_decode.argtypes = [PP, P, P, P, I32, I32, P, P, P, P, P, SZ, P]
         lib.ksa_vote_select_per_head.argtypes = [PP, P, P, I32, I32, P, P, SZ, P]
+        lib.ksa_paged_vote_select.argtypes = [PP, PG, P, P, I32, I32, P, P, P, SZ, P]
+        lib.ksa_paged_sparse_decode.argtypes = [PP, PG, P, P, P, ctypes.POINTER(Selection), P, P,
+                                                P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:14]:
+        for name in EXPORTED[:16]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -567,3 +570,55 @@ def ksa_vote_select_per_head(q: torch.Tensor, k: torch.Tensor, seq_len: int, tok
                                         _dev(token_idx, "token_idx", torch.int32, (B, Hq, n_out)),
                                         pws, nws, _stream(stream)), "ksa_vote_select_per_head")
     return token_idx
+
+
+def ksa_paged_vote_select(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                          seq_lens: torch.Tensor, token_budget: int, recent_window: int,
+                          max_len: Optional[int] = None, token_idx=None, votes=None,
+                          want_votes: bool = False, workspace=None, stream=None):
+    """The vote-union set on a paged cache with per-sequence lengths:
+    token_idx [B, min(N, T_max)] int32 (-1 padded), votes [B, T_max] uint8."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, 0.0)
+    B, T = q.shape[0], prob.seq_len
+    n_out = min(token_budget, T)
+    if token_idx is None:
+        token_idx = torch.empty((B, n_out), dtype=torch.int32, device=q.device)
+    if want_votes and votes is None:
+        votes = torch.empty((B, T), dtype=torch.uint8, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_SELECT, token_budget, q.device, workspace)
+    _check(lib.ksa_paged_vote_select(ctypes.byref(prob), ctypes.byref(pg),
+                                     _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+                                     int(token_budget), int(recent_window),
+                                     _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
+                                     _dev(votes, "votes", torch.uint8, (B, T)), pws, nws,
+                                     _stream(stream)), "ksa_paged_vote_select")
+    return (token_idx, votes) if votes is not None else token_idx
+
+
+def ksa_paged_sparse_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_table: torch.Tensor, seq_lens: torch.Tensor, idx: torch.Tensor,
+                            kind: int = KSA_SEL_TOKENS, max_len: Optional[int] = None, out=None,
+                            lse=None, want_lse: bool = True, sm_scale: float = 0.0,
+                            workspace=None, stream=None):
+    """Attention over selected blocks ([B,Hkv,count]) or a shared token list
+    ([B,count]) of a paged cache; negative entries are skipped."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, sm_scale)
+    B, Hq, D = q.shape
+    count = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ishape = (B, k_pool.shape[1], count) if kind == KSA_SEL_BLOCKS else (B, count)
+    sel = Selection(int(kind), _dev(idx, "idx", torch.int32, ishape), int(count))
+    op = KSA_OP_SPARSE_BLOCKS if kind == KSA_SEL_BLOCKS else KSA_OP_SPARSE_TOKENS
+    ws, pws, nws = _workspace(prob, op, count, q.device, workspace)
+    _check(lib.ksa_paged_sparse_decode(ctypes.byref(prob), ctypes.byref(pg),
+                                       _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+                                       _dev(v_pool, "v_pool", k_pool.dtype, k_pool.shape),
+                                       ctypes.byref(sel), _dev(out, "out", torch.float32, (B, Hq, D)),
+                                       _dev(lse, "lse", torch.float32, (B, Hq)), pws, nws,
+                                       _stream(stream)), "ksa_paged_sparse_decode")
+    return out, lse

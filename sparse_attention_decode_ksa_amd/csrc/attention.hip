@@ -74,6 +74,55 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_d
     attn_row_valu<T, D, G, 3>(a, row, split, s_idx, s_pg, e0, true);
 }
 
+// Attention over a given list on a paged cache: kind 3 = block ids
+// [B, Hkv, count] (logical, -1 = padding), kind 5 = token ids [B, count]
+// shared by the sequence's heads (-1 = padding).  The row's length comes from
+// seq_lens; the ids of this split's range and their pages (kind 3) or pool
+// rows (kind 5) are staged in LDS.
+template <typename T, int D, int G, int KIND>
+__global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_list_kernel(
+    AttnArgs a0) {
+  constexpr bool kMfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
+  constexpr int CH = kMfma ? 16 : (64 / (D / KV<T>::EPL)) * kLoadsPerChunk;
+  __shared__ int s_idx[kIdxStage];
+  __shared__ int s_pg[kIdxStage];
+  const int split = blockIdx.x % a0.splits;
+  const int row = blockIdx.x / a0.splits;
+  const int b = row / a0.d.Hkv;
+  const int Bs = a0.d.Bs;
+  AttnArgs a = a0;
+  const int Tb = min(max(a0.seq_lens[b], 1), a0.tstride * Bs);
+  a.d.T = Tb;
+  const int nchunks = (a.ltot + CH - 1) / CH;
+  const int c_begin = split * a.cps;
+  const int c_end = min(c_begin + a.cps, nchunks);
+  const int32_t* tb = a.table + (int64_t)b * a.tstride;
+  int e0, e1;
+  const int32_t* src;
+  if constexpr (KIND == 3) {
+    e0 = (c_begin * CH) / Bs;
+    e1 = min(a.count, (c_end * CH + Bs - 1) / Bs);
+    src = a.idx + (int64_t)row * a.count;
+  } else {
+    e0 = c_begin * CH;
+    e1 = min(a.ltot, c_end * CH);
+    src = a.idx + (int64_t)b * a.count;
+  }
+  const int nbb = (Tb + Bs - 1) / Bs;
+  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) {
+    const int x = src[e0 + i];
+    s_idx[i] = x;
+    if constexpr (KIND == 3)
+      s_pg[i] = (x >= 0 && x < nbb) ? tb[x] : 0;
+    else
+      s_pg[i] = (x >= 0 && x < Tb) ? tb[x / Bs] * a.page_rows + x % Bs : 0;
+  }
+  if constexpr (kMfma)
+    attn_row_mfma<G, KIND>(a, row, split, s_idx, s_pg, e0, true);
+  else
+    attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, s_pg, e0, true);
+}
+
 // Fixed-order merge of the split partial states of each row.
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_acc,
@@ -105,8 +154,12 @@ hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStrea
   const int rows = a.d.B * a.d.Hkv;
   const dim3 grid(rows * p.splits), block(p.nw * 64);
   constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
-  if (kind == 3) {
+  if (kind == 3 && a.idx == nullptr) {  // paged dense: every block of the row
     hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G>), grid, block, 0, s, a);
+  } else if (kind == 3) {
+    hipLaunchKernelGGL((attn_paged_list_kernel<T, D, G, 3>), grid, block, 0, s, a);
+  } else if (kind == 5) {
+    hipLaunchKernelGGL((attn_paged_list_kernel<T, D, G, 5>), grid, block, 0, s, a);
   } else if (kind == 4) {  // rows are query heads: one head per row
     if constexpr (G == 1)
       hipLaunchKernelGGL((attn_partial_kernel<T, D, 1, 4>), grid, block, 0, s, a);
@@ -168,7 +221,7 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   }
   // a workgroup's index slice must fit the LDS stage
   int64_t cap = INT64_MAX;
-  if (kind == 1 || kind == 4) cap = kIdxStage / ch;
+  if (kind == 1 || kind == 4 || kind == 5) cap = kIdxStage / ch;
   if (kind == 0 || kind == 3) cap = ((int64_t)(kIdxStage - 2) * d.Bs) / ch;
   if (cps > cap) cps = cap;
   if (cps < 1) cps = 1;

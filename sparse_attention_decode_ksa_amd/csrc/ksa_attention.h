@@ -84,7 +84,8 @@ struct AttnArgs {
 // Kernel arguments of one attention call (host side).  kind: 0 = selected
 // blocks, 1 = shared token list, 2 = dense range [0, T), 3 = blocks of a
 // paged cache (logical ids and their pages staged in LDS; the per-row
-// length is set by the kernel), 4 = a token list per query head.
+// length is set by the kernel), 4 = a token list per query head, 5 = a
+// shared token list over a paged cache (ids and pool rows staged in LDS).
 inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const void* k, const void* v,
                                const int32_t* idx, int count, float* out, float* lse,
                                void* workspace, const AttnPlan& plan) {
@@ -95,7 +96,8 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.idx = idx;
   a.count = count;
   a.d = d;
-  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs : ((kind == 1 || kind == 4) ? count : d.T);
+  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs
+                                     : ((kind == 1 || kind == 4 || kind == 5) ? count : d.T);
   a.bs_shift = -1;
   if ((kind == 0 || kind == 3) && (d.Bs & (d.Bs - 1)) == 0) {
     int sh = 0;
@@ -138,6 +140,12 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_id
       ok[i] = p < a.ltot;
       const int at = min(max(p - e0, 0), kIdxStage - 1);  // in range whenever ok
       tok[i] = ok[i] ? s_idx[at] : 0;
+    } else if constexpr (KIND == 5) {
+      // a shared token list over a paged cache: s_idx holds the token ids
+      // (negative: padding, skipped), s_pg their pool rows
+      const int at = min(max(p - e0, 0), kIdxStage - 1);
+      ok[i] = p < a.ltot && s_idx[at] >= 0 && s_idx[at] < a.d.T;
+      tok[i] = ok[i] ? s_pg[at] : 0;
     } else {
       ok[i] = p < a.ltot;
       int q, r;
@@ -151,7 +159,7 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_id
       const int at = min(max(q - e0, 0), kIdxStage - 1);  // in range whenever ok
       const int blk = ok[i] ? s_idx[at] : 0;
       const int t = blk * a.d.Bs + r;
-      ok[i] = ok[i] && t < a.d.T;
+      ok[i] = ok[i] && t < a.d.T && (KIND != 3 || blk >= 0);  // paged lists pad with -1
       if constexpr (KIND == 3)
         tok[i] = ok[i] ? s_pg[at] * a.page_rows + r : 0;
       else
@@ -315,7 +323,7 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   const int slot = lane / LPT, li = lane % LPT;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const int64_t kvrow =
-      (KIND == 3   ? (int64_t)g * d.Bs * D
+      ((KIND == 3 || KIND == 5) ? (int64_t)g * d.Bs * D
        : KIND == 4 ? ((int64_t)b * (d.Hkv / a.kv_div) + g / a.kv_div) * d.Tcap * D
                    : (int64_t)row * d.Tcap * D) +
       li * EPL;
@@ -447,7 +455,8 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
   const int r = lane & 15, kg = lane >> 4;  // MFMA: row/column and k-group / row quad
   const int slot = kg, li = r;             // V layout: token slot and 16-byte piece
   const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const int64_t kvrow = KIND == 3 ? (int64_t)g * d.Bs * D : (int64_t)row * d.Tcap * D;
+  const int64_t kvrow =
+      (KIND == 3 || KIND == 5) ? (int64_t)g * d.Bs * D : (int64_t)row * d.Tcap * D;
   const uint16_t* kbase = (const uint16_t*)a.k + kvrow + 8 * kg;
   const uint16_t* vbase = (const uint16_t*)a.v + kvrow + li * EPL;
 

@@ -127,6 +127,14 @@ hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, u
                               const HeadMask& voting = HeadMask());
 // T <= N: the whole context, no vote.
 hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hipStream_t stream);
+// The vote on a paged cache with per-sequence lengths (d.T the longest):
+// token_idx [B, min(N, T)], -1 past a sequence shorter than N.  Needs
+// plan.words <= 1024 (the one-kernel vote set).
+hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void* q,
+                                    const void* k_pool, int N, int W, int32_t* token_idx,
+                                    uint8_t* votes, void* workspace, const VotePlan& plan,
+                                    hipStream_t stream);
+constexpr int kPagedVoteMaxHistory = 32768;
 // Per-head sets: every head's own picks plus the window, token_idx [B, Hq, min(N, T)].
 hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
                                 int32_t* token_idx, void* workspace, const VotePlan& plan,

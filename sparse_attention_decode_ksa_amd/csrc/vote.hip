@@ -65,11 +65,41 @@ constexpr int kSetStage = 8192;  // picks per sequence the vote set stages in LD
 #endif
 constexpr int kSetSteps = KSA_SET_STEPS;  // steps of four tokens per thread per piece of the vote set
 
+// A paged cache for the vote (table == nullptr: contiguous): each sequence
+// has its own length T_b and history T_b - W (none when T_b <= N).
+struct VotePaging {
+  const int32_t* table;     // [B, tstride] pages of logical blocks
+  const int32_t* seq_lens;  // [B]
+  int tstride;
+  int N, W;
+};
+
+// The history length of sequence b (0: no vote for it).
+__device__ __forceinline__ int vote_hist(const VotePaging& pg, const Dims& d, int b, int hist) {
+  if (!pg.seq_lens) return hist;
+  const int Tb = min(max(pg.seq_lens[b], 1), pg.tstride * d.Bs);
+  return Tb > pg.N ? Tb - pg.W : 0;
+}
+
+// Element offset of token t's K row of (b, g): contiguous [B, Hkv, T_cap, D]
+// or a pool [num_pages, Hkv, Bs, D] through the block table.
+template <bool PAGED>
+__device__ __forceinline__ int64_t vote_row(const VotePaging& pg, const Dims& d, int b, int g,
+                                            int t) {
+  if constexpr (PAGED) {
+    const int j = t / d.Bs;
+    return (((int64_t)pg.table[(int64_t)b * pg.tstride + j] * d.Hkv + g) * d.Bs + (t - j * d.Bs)) *
+           d.D;
+  } else {
+    return ((int64_t)(b * d.Hkv + g) * d.Tcap + t) * d.D;
+  }
+}
+
 // ------------------------------------------------------------------ 1 (VALU)
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool PAGED>
 __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
     const T* __restrict__ q, const T* __restrict__ k, Dims d, int hist, int kstride,
-    uint32_t* __restrict__ keys) {
+    uint32_t* __restrict__ keys, VotePaging pg) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int SPW = 64 / LPT;
@@ -80,7 +110,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
   const int slot = lane / LPT, li = lane % LPT;
   const int row = blockIdx.y;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const T* kb = k + (int64_t)row * d.Tcap * D + li * EPL;
+  const T* kb = k + li * EPL;
+  hist = vote_hist(pg, d, b, hist);
 
   float qv[G][EPL];
 #pragma unroll
@@ -97,7 +128,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
   uint4 kr[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    kr[i] = ld16_stream(kb + (int64_t)min(c0 * CH + i * SPW + slot, hist - 1) * D);
+    kr[i] = ld16_stream(kb + vote_row<PAGED>(pg, d, b, g, min(c0 * CH + i * SPW + slot, hist - 1)));
   for (int c = c0; c < c1; ++c) {
     uint4 kc[NI];
 #pragma unroll
@@ -105,7 +136,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
     if (c + 1 < c1) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        kr[i] = ld16_stream(kb + (int64_t)min((c + 1) * CH + i * SPW + slot, hist - 1) * D);
+        kr[i] = ld16_stream(
+            kb + vote_row<PAGED>(pg, d, b, g, min((c + 1) * CH + i * SPW + slot, hist - 1)));
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -135,10 +167,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_kernel(
 // wave owns kVoteChunks consecutive chunks and keeps kVotePrefetch of them
 // in flight; loads past its range re-read its last token (in cache), so
 // every load is unconditional.
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Dims d, int hist, int kstride,
-    uint32_t* __restrict__ keys) {
+    uint32_t* __restrict__ keys, VotePaging pg) {
   constexpr int D = 128;
   constexpr int CH = 16;
   constexpr int P = kVotePrefetch;
@@ -148,7 +180,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
   const int r = lane & 15, kg = lane >> 4;  // MFMA row / k-group; also row layout piece / slot
   const int row = blockIdx.y;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const uint16_t* kb = k + (int64_t)row * d.Tcap * D + 8 * r;
+  const uint16_t* kb = k + 8 * r;
+  hist = vote_hist(pg, d, b, hist);
 
   const int c0 = (blockIdx.x * kScoreWaves + wave) * Q;
   if (c0 * CH >= hist) return;
@@ -176,7 +209,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
   uint4 kr[P][4];
   auto load = [&](int c, uint4(&dst)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = ld16_stream(kb + (int64_t)min(c * CH + 4 * i + kg, tend) * D);
+    for (int i = 0; i < 4; ++i)
+      dst[i] = ld16_stream(kb + vote_row<PAGED>(pg, d, b, g, min(c * CH + 4 * i + kg, tend)));
   };
 #pragma unroll
   for (int s = 0; s < P; ++s) load(c0 + s, kr[s]);
@@ -215,7 +249,8 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
     const uint32_t* __restrict__ keys, int hist, int kstride, int kv, int words, int Hq,
-    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist, HeadMask voting) {
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist, HeadMask voting, Dims d,
+    VotePaging pg) {
   constexpr int NWV = NT / 64;
   static_assert(4096 % NT == 0, "radix buckets per thread");
   __shared__ TopkShared sh;
@@ -227,8 +262,10 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
     for (int i = tid; i < 256; i += NT) vhist[(hr / Hq) * 256 + i] = 0u;
   uint32_t* br = bits + hr * words;
   const int h = (int)(hr % Hq);
-  // no picks: the whole budget is the recency window, or the head does not vote
-  if (kv == 0 || !((voting.w[h >> 5] >> (h & 31)) & 1u)) {
+  hist = vote_hist(pg, d, (int)(hr / Hq), hist);
+  // no picks: the whole budget is the recency window, the sequence is too
+  // short to vote, or the head does not vote
+  if (kv == 0 || hist == 0 || !((voting.w[h >> 5] >> (h & 31)) & 1u)) {
     for (int w = tid; w < words; w += NT) br[w] = 0u;
     return;
   }
@@ -327,7 +364,8 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
 template <bool kLdsKeys>
 __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
     const uint32_t* __restrict__ keys, int hist, int kstride, int kv, int words, int Hq,
-    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist, HeadMask voting) {
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ vhist, HeadMask voting, Dims d,
+    VotePaging pg) {
   extern __shared__ uint32_t lkeys[];  // the head's keys (kLdsKeys)
   __shared__ uint32_t hbin[256];
   __shared__ uint32_t red[2][kHeadThreads / 64];
@@ -339,8 +377,10 @@ __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
     for (int i = tid; i < 256; i += kHeadThreads) vhist[(hr / Hq) * 256 + i] = 0u;
   uint32_t* br = bits + hr * words;
   const int h = (int)(hr % Hq);
-  // no picks: the whole budget is the recency window, or the head does not vote
-  if (kv == 0 || !((voting.w[h >> 5] >> (h & 31)) & 1u)) {
+  hist = vote_hist(pg, d, (int)(hr / Hq), hist);
+  // no picks: the whole budget is the recency window, the sequence is too
+  // short to vote, or the head does not vote
+  if (kv == 0 || hist == 0 || !((voting.w[h >> 5] >> (h & 31)) & 1u)) {
     for (int w = tid; w < words; w += kHeadThreads) br[w] = 0u;
     return;
   }
@@ -649,14 +689,27 @@ __device__ __forceinline__ uint32_t votes_at_least(const uint32_t (&c)[NP], int 
 template <int NP>
 __global__ __launch_bounds__(kSetThreads) void vote_tally_set_kernel(
     const uint32_t* __restrict__ bits, int Hq, int T, int hist, int words, int kv, int N, int W,
-    int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
+    int n_out, int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes, Dims d,
+    VotePaging pg) {
   constexpr int NWV = kSetThreads / 64;
   __shared__ uint32_t s_red[2][NWV];
   __shared__ uint32_t s_scan[16];
   __shared__ int32_t s_pick[kSetStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
-  int32_t* out = token_idx + (int64_t)b * N;
+  int32_t* out = token_idx + (int64_t)b * n_out;
+  if (pg.seq_lens) {  // this sequence's own length (T is then the longest)
+    const int Tb = min(max(pg.seq_lens[b], 1), pg.tstride * d.Bs);
+    if (Tb <= N) {  // no vote: the whole sequence, then -1
+      for (int i = tid; i < n_out; i += kSetThreads) out[i] = i < Tb ? i : -1;
+      if (votes)
+        for (int t = tid; t < T; t += kSetThreads) votes[(int64_t)b * T + t] = 0;
+      return;
+    }
+    hist = Tb - W;
+    if (votes)
+      for (int t = Tb + tid; t < T; t += kSetThreads) votes[(int64_t)b * T + t] = 0;
+  }
   for (int i = tid; i < W; i += kSetThreads) {
     out[kv + i] = hist + i;
     if (votes) votes[(int64_t)b * T + hist + i] = 0;
@@ -664,9 +717,10 @@ __global__ __launch_bounds__(kSetThreads) void vote_tally_set_kernel(
 
   // bit-sliced vote totals of the thread's word
   const int w = tid;
-  const uint32_t valid = w >= words ? 0u
-                         : (w == words - 1 && (hist & 31)) ? (1u << (hist & 31)) - 1u
-                                                            : 0xFFFFFFFFu;
+  const int words_b = (hist + 31) / 32;
+  const uint32_t valid = w >= words_b ? 0u
+                         : (w == words_b - 1 && (hist & 31)) ? (1u << (hist & 31)) - 1u
+                                                              : 0xFFFFFFFFu;
   uint32_t c[NP];
 #pragma unroll
   for (int k = 0; k < NP; ++k) c[k] = 0u;
@@ -771,42 +825,61 @@ __global__ void vote_all_kernel(int T, int32_t* __restrict__ token_idx, uint8_t*
 
 template <typename T, int D, int G>
 hipError_t launch_scores(const Dims& d, const void* q, const void* k, int hist, int kstride,
-                         uint32_t* keys, hipStream_t s) {
+                         uint32_t* keys, hipStream_t s, const VotePaging& pg) {
   constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
+  const bool paged = pg.table != nullptr;
   if constexpr (mfma) {
     const int nchunks = (hist + 15) / 16;
     const int per_wg = kScoreWaves * kVoteChunks;
     const dim3 grid((nchunks + per_wg - 1) / per_wg, d.B * d.Hkv);
-    hipLaunchKernelGGL((vote_scores_mfma_kernel<G>), grid, dim3(kScoreWaves * 64), 0, s,
-                       (const uint16_t*)q, (const uint16_t*)k, d, hist, kstride, keys);
+    if (paged)
+      hipLaunchKernelGGL((vote_scores_mfma_kernel<G, true>), grid, dim3(kScoreWaves * 64), 0, s,
+                         (const uint16_t*)q, (const uint16_t*)k, d, hist, kstride, keys, pg);
+    else
+      hipLaunchKernelGGL((vote_scores_mfma_kernel<G, false>), grid, dim3(kScoreWaves * 64), 0, s,
+                         (const uint16_t*)q, (const uint16_t*)k, d, hist, kstride, keys, pg);
   } else {
     const int nchunks = (hist + chunk_tokens(d) - 1) / chunk_tokens(d);
     const int per_wg = kScoreWaves * kScoreChunksPerWave;
     const dim3 grid((nchunks + per_wg - 1) / per_wg, d.B * d.Hkv);
-    hipLaunchKernelGGL((vote_scores_kernel<T, D, G>), grid, dim3(kScoreWaves * 64), 0, s,
-                       (const T*)q, (const T*)k, d, hist, kstride, keys);
+    if (paged)
+      hipLaunchKernelGGL((vote_scores_kernel<T, D, G, true>), grid, dim3(kScoreWaves * 64), 0, s,
+                         (const T*)q, (const T*)k, d, hist, kstride, keys, pg);
+    else
+      hipLaunchKernelGGL((vote_scores_kernel<T, D, G, false>), grid, dim3(kScoreWaves * 64), 0, s,
+                         (const T*)q, (const T*)k, d, hist, kstride, keys, pg);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_scores_g(const Dims& d, const void* q, const void* k, int hist, int kstride,
-                           uint32_t* keys, hipStream_t s) {
+                           uint32_t* keys, hipStream_t s, const VotePaging& pg) {
   switch (d.G) {
-    case 1: return launch_scores<T, D, 1>(d, q, k, hist, kstride, keys, s);
-    case 2: return launch_scores<T, D, 2>(d, q, k, hist, kstride, keys, s);
-    case 4: return launch_scores<T, D, 4>(d, q, k, hist, kstride, keys, s);
-    default: return launch_scores<T, D, 8>(d, q, k, hist, kstride, keys, s);
+    case 1: return launch_scores<T, D, 1>(d, q, k, hist, kstride, keys, s, pg);
+    case 2: return launch_scores<T, D, 2>(d, q, k, hist, kstride, keys, s, pg);
+    case 4: return launch_scores<T, D, 4>(d, q, k, hist, kstride, keys, s, pg);
+    default: return launch_scores<T, D, 8>(d, q, k, hist, kstride, keys, s, pg);
   }
 }
 
+hipError_t launch_scores_any(const Dims& d, const void* q, const void* k, int hist, int kstride,
+                             uint32_t* keys, hipStream_t s, const VotePaging& pg) {
+  if (d.dtype == KSA_BF16)
+    return d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, hist, kstride, keys, s, pg)
+                     : launch_scores_g<uint16_t, 128>(d, q, k, hist, kstride, keys, s, pg);
+  return d.D == 64 ? launch_scores_g<float, 64>(d, q, k, hist, kstride, keys, s, pg)
+                   : launch_scores_g<float, 128>(d, q, k, hist, kstride, keys, s, pg);
+}
+
 hipError_t launch_head_select(const Dims& d, const VotePlan& p, const uint32_t* keys, uint32_t* bits,
-                              uint32_t* vhist, const HeadMask& voting, hipStream_t stream) {
+                              uint32_t* vhist, const HeadMask& voting, hipStream_t stream,
+                              const VotePaging& pg) {
   const dim3 grid(d.B * d.Hq), block(kHeadThreads);
   const int kpt = (p.hist + kHeadNT - 1) / kHeadNT;
 #define KSA_HEAD_TOPK(K)                                                                      \
   hipLaunchKernelGGL((vote_head_topk_kernel<kHeadNT, K>), grid, dim3(kHeadNT), 0, stream, keys, \
-                     p.hist, p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting)
+                     p.hist, p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting, d, pg)
   if (kpt <= 8) {
     KSA_HEAD_TOPK(8);
   } else if (kpt <= 16) {
@@ -830,10 +903,10 @@ hipError_t launch_head_select(const Dims& d, const VotePlan& p, const uint32_t* 
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(vote_head_select_kernel<true>, grid, block, lds, stream, keys, p.hist,
-                       p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting);
+                       p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting, d, pg);
   } else {
     hipLaunchKernelGGL(vote_head_select_kernel<false>, grid, block, 0, stream, keys, p.hist,
-                       p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting);
+                       p.kstride, p.kv, p.words, d.Hq, bits, vhist, voting, d, pg);
   }
   return hipGetLastError();
 }
@@ -914,38 +987,39 @@ hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int
   uint32_t* keys = (uint32_t*)(ws + plan.keys_off);
   uint32_t* bits = (uint32_t*)(ws + plan.bits_off);
   uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
-  hipError_t e;
-  if (d.dtype == KSA_BF16)
-    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
-                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
-  else
-    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
-                  : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
+  const VotePaging none{nullptr, nullptr, 0, N, W};
+  hipError_t e = launch_scores_any(d, q, k, plan.hist, plan.kstride, keys, stream, none);
   if (e != hipSuccess) return e;
-  e = launch_head_select(d, plan, keys, bits, vhist, HeadMask(), stream);
+  e = launch_head_select(d, plan, keys, bits, vhist, HeadMask(), stream, none);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(head_set_kernel, dim3(rows), dim3(kHeadSetThreads), 0, stream, bits,
                      plan.words, plan.hist, plan.kv, W, N, token_idx);
   return hipGetLastError();
 }
 
-hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, uint8_t* votes,
-                              void* workspace, const VotePlan& plan, hipStream_t stream,
-                              const HeadMask& voting) {
+namespace {
+hipError_t vote_finish(const Dims& d, int N, int W, int n_out, int32_t* token_idx, uint8_t* votes,
+                       void* workspace, const VotePlan& plan, hipStream_t stream,
+                       const HeadMask& voting, const VotePaging& pg, bool scored) {
   char* ws = (char*)workspace;
   uint32_t* keys = (uint32_t*)(ws + plan.keys_off);
   uint32_t* bits = (uint32_t*)(ws + plan.bits_off);
   uint8_t* votes8 = (uint8_t*)(ws + plan.votes_off);
   uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
-  hipError_t e = launch_head_select(d, plan, keys, bits, vhist, voting, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (scored) {
+    e = launch_head_select(d, plan, keys, bits, vhist, voting, stream, pg);
+    if (e != hipSuccess) return e;
+  }
   if (plan.words <= kSetThreads) {
     if (d.Hq < 64)
       hipLaunchKernelGGL(vote_tally_set_kernel<6>, dim3(d.B), dim3(kSetThreads), 0, stream, bits,
-                         d.Hq, d.T, plan.hist, plan.words, plan.kv, N, W, token_idx, votes);
+                         d.Hq, d.T, plan.hist, plan.words, plan.kv, N, W, n_out, token_idx, votes,
+                         d, pg);
     else
       hipLaunchKernelGGL(vote_tally_set_kernel<8>, dim3(d.B), dim3(kSetThreads), 0, stream, bits,
-                         d.Hq, d.T, plan.hist, plan.words, plan.kv, N, W, token_idx, votes);
+                         d.Hq, d.T, plan.hist, plan.words, plan.kv, N, W, n_out, token_idx, votes,
+                         d, pg);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(vote_count_kernel, dim3((plan.hist + kCountThreads - 1) / kCountThreads, d.B),
@@ -956,6 +1030,14 @@ hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, u
   hipLaunchKernelGGL(vote_set_kernel, dim3(d.B), dim3(kSetThreads), 0, stream, votes8, vhist, d.T,
                      plan.hist, plan.kv, N, W, token_idx, votes);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, uint8_t* votes,
+                              void* workspace, const VotePlan& plan, hipStream_t stream,
+                              const HeadMask& voting) {
+  const VotePaging none{nullptr, nullptr, 0, N, W};
+  return vote_finish(d, N, W, N, token_idx, votes, workspace, plan, stream, voting, none, true);
 }
 
 hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hipStream_t stream) {
@@ -969,15 +1051,26 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
                               const VotePlan& plan, hipStream_t stream, const HeadMask& voting) {
   if (d.T <= N) return launch_vote_all(d, token_idx, votes, stream);
   uint32_t* keys = (uint32_t*)((char*)workspace + plan.keys_off);
-  hipError_t e;
-  if (d.dtype == KSA_BF16)
-    e = d.D == 64 ? launch_scores_g<uint16_t, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
-                  : launch_scores_g<uint16_t, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
-  else
-    e = d.D == 64 ? launch_scores_g<float, 64>(d, q, k, plan.hist, plan.kstride, keys, stream)
-                  : launch_scores_g<float, 128>(d, q, k, plan.hist, plan.kstride, keys, stream);
+  const VotePaging none{nullptr, nullptr, 0, N, W};
+  hipError_t e = launch_scores_any(d, q, k, plan.hist, plan.kstride, keys, stream, none);
   if (e != hipSuccess) return e;
-  return launch_vote_finish(d, N, W, token_idx, votes, workspace, plan, stream, voting);
+  return vote_finish(d, N, W, N, token_idx, votes, workspace, plan, stream, voting, none, true);
+}
+
+hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void* q,
+                                    const void* k_pool, int N, int W, int32_t* token_idx,
+                                    uint8_t* votes, void* workspace, const VotePlan& plan,
+                                    hipStream_t stream) {
+  const VotePaging pg{p.table, p.seq_lens, p.max_blocks, N, W};
+  const int n_out = d.T < N ? d.T : N;
+  const bool any_vote = d.T > N;  // d.T is the longest sequence
+  if (any_vote) {
+    uint32_t* keys = (uint32_t*)((char*)workspace + plan.keys_off);
+    hipError_t e = launch_scores_any(d, q, k_pool, plan.hist, plan.kstride, keys, stream, pg);
+    if (e != hipSuccess) return e;
+  }
+  return vote_finish(d, N, W, n_out, token_idx, votes, workspace, plan, stream, HeadMask(), pg,
+                     any_vote);
 }
 
 }  // namespace ksa

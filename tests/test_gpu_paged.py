@@ -167,3 +167,66 @@ def test_paged_newest_block_refresh_only():
         np.testing.assert_array_equal(got[b, :, j], ref[0, :, j])
         others = [i for i in range(table.shape[1]) if i != j]
         assert np.all(s[b, :, others].float().cpu().numpy() == 3)
+
+
+# ----------------------------------------------------------------------------- the vote path
+VOTE_PAGED = [
+    dict(lens=[5000, 3000, 900, 1], Bs=16, Hq=32, Hkv=8, D=128, dtype="bf16", N=1024, W=256),  # MFMA
+    dict(lens=[2100, 700, 1500], Bs=7, Hq=8, Hkv=2, D=64, dtype="f32", N=512, W=128),
+    dict(lens=[400, 300], Bs=16, Hq=4, Hkv=2, D=64, dtype="bf16", N=512, W=64),    # all T_b <= N
+]
+
+
+@pytest.mark.parametrize("case", VOTE_PAGED, ids=lambda c: "G%d-Bs%d-%s" % (
+    c["Hq"] // c["Hkv"], c["Bs"], "_".join(map(str, c["lens"]))))
+def test_paged_vote_and_token_attention_match_oracle_per_sequence(case):
+    c = dict(case)
+    lens, Bs, N, W = c.pop("lens"), c.pop("Bs"), c.pop("N"), c.pop("W")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=sum(lens) % 997, **c)
+    idx, votes = ksa.ksa_paged_vote_select(q, kp, table, seq, N, W, want_votes=True)
+    out, lse = ksa.ksa_paged_sparse_decode(q, kp, vp, table, seq, idx, ksa.KSA_SEL_TOKENS)
+    torch.cuda.synchronize()
+    ids, vts = idx.cpu().numpy(), votes.cpu().numpy()
+    from parity import check_votes
+    for b, T in enumerate(lens):
+        kb, vb = gathered(kp, table, b, T, Bs), gathered(vp, table, b, T, Bs)
+        qb = np_bits(q[b:b + 1])
+        row = ids[b][ids[b] >= 0]
+        if T <= N:
+            assert row.tolist() == list(range(T)) and np.all(vts[b] == 0)
+        else:
+            lg = oracle.head_logits(qb, kb, T)
+            assert row.shape[0] == N and np.all(ids[b] >= 0)
+            check_votes(vts[b:b + 1, :T], row[None], lg, N, W)
+            assert np.all(vts[b, T - W:] == 0)
+        ro, rl = oracle.attend_tokens(qb, kb, vb, T, row[None].astype(np.int32))
+        check_attention(out[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), ro, rl)
+
+
+def test_paged_vote_equals_contiguous_vote_bitwise():
+    T, Bs, N, W = 4000, 16, 512, 128
+    w, q, k, v, kp, vp, table, seq = paged_inputs([T] * 3, Bs, seed=77, Hq=32, Hkv=8, D=128,
+                                                  dtype="bf16")
+    pi, pv = ksa.ksa_paged_vote_select(q, kp, table, seq, N, W, want_votes=True)
+    ci, cv = ksa.ksa_vote_select(q, k, T, N, W, want_votes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pi, ci) and torch.equal(pv[:, :T], cv)
+    po, pl = ksa.ksa_paged_sparse_decode(q, kp, vp, table, seq, pi, ksa.KSA_SEL_TOKENS)
+    co, cl = ksa.ksa_sparse_decode(q, k, v, T, ci, ksa.KSA_SEL_TOKENS)
+    torch.cuda.synchronize()
+    assert torch.equal(po, co) and torch.equal(pl, cl)
+
+
+def test_paged_sparse_decode_of_the_steps_blocks_equals_the_step():
+    """Attending the paged step's own ids (padding included) with the
+    separate paged call gives the step's outputs (to fp32 merge order)."""
+    lens = [3000, 700, 40]
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, 16, seed=31, Hq=8, Hkv=2, D=128,
+                                                  dtype="bf16")
+    s = torch.zeros((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    out, lse, idx = ksa.ksa_paged_block_topk_decode(q, kp, vp, s, table, seq, 32,
+                                                    want_block_idx=True)
+    o2, l2 = ksa.ksa_paged_sparse_decode(q, kp, vp, table, seq, idx, ksa.KSA_SEL_BLOCKS)
+    torch.cuda.synchronize()
+    assert float((out - o2).abs().max()) <= 1e-5 and float((lse - l2).abs().max()) <= 1e-5
