@@ -198,3 +198,50 @@ def test_paged_validation():
     assert need > 0
     assert dense(P(B=1, Hkv=1, Hq=1, T=1 << 15, Tcap=1 << 15), pg(max_blocks=2048)) == \
         ksa.KSA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_variant_and_layer_validation():
+    """Host-side checks of the variant, selection-layer and paged-vote calls."""
+    lib = ksa.load_library()
+    null = None
+    E = ksa.KSA_ERR_INVALID_ARGUMENT
+    U = ksa.KSA_ERR_UNSUPPORTED
+    W_ = ksa.KSA_ERR_WORKSPACE_TOO_SMALL
+    p = P(B=2, Hq=8, Hkv=2, D=128, T=4096, Tcap=4096, dtype=ksa.KSA_BF16)
+    pp = ctypes.byref(p)
+    # select options: bad aggregate, no options, k < 1
+    bad = ksa.SelectOptions(4, 7, 0)
+    assert lib.ksa_select_topk_ex(pp, FAKE, FAKE, ctypes.byref(bad), FAKE, null, FAKE, 1 << 30,
+                                  null) == E
+    assert lib.ksa_select_topk_ex(pp, FAKE, FAKE, null, FAKE, null, FAKE, 1 << 30, null) == E
+    zero = ksa.SelectOptions(0, 0, 0)
+    assert lib.ksa_select_topk_ex(pp, FAKE, FAKE, ctypes.byref(zero), FAKE, null, FAKE, 1 << 30,
+                                  null) == E
+    # voting heads: empty, out of range, repeated
+    for heads in ([], [8], [-1], [2, 2]):
+        arr = (ctypes.c_int32 * max(1, len(heads)))(*(heads or [0]))
+        st = lib.ksa_vote_select_heads(pp, FAKE, FAKE, 512, 128, ctypes.cast(arr, ctypes.c_void_p),
+                                       len(heads), FAKE, null, FAKE, 1 << 30, null)
+        assert st == E, heads
+    # selection layer: W > N, and a workspace smaller than asked
+    assert lib.ksa_vote_layer_decode(pp, FAKE, FAKE, FAKE, 100, 200, FAKE, null, FAKE, null, FAKE,
+                                     1 << 30, null) == E
+    need = ksa.ksa_workspace_bytes(p, ksa.KSA_OP_VOTE_LAYER, 512)
+    assert need > ksa.ksa_workspace_bytes(p, ksa.KSA_OP_VOTE_SELECT, 512)
+    assert lib.ksa_vote_layer_decode(pp, FAKE, FAKE, FAKE, 512, 128, FAKE, null, FAKE, null, FAKE,
+                                     0, null) == W_
+    # paged vote: histories longer than the one-kernel vote set
+    pl = P(B=1, Hq=8, Hkv=2, D=128, T=40000, Tcap=40000, dtype=ksa.KSA_BF16)
+    g = ksa.PagedKv(FAKE, FAKE, 2500, 3000)
+    assert lib.ksa_paged_vote_select(ctypes.byref(pl), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,
+                                     null, FAKE, 1 << 34, null) == U
+    # paged sparse decode: per-head lists are not a paged kind; more blocks than the table holds
+    sel = ksa.Selection(ksa.KSA_SEL_HEAD_TOKENS, FAKE.value, 4)
+    g2 = ksa.PagedKv(FAKE, FAKE, 256, 1000)
+    assert lib.ksa_paged_sparse_decode(pp, ctypes.byref(g2), FAKE, FAKE, FAKE, ctypes.byref(sel),
+                                       FAKE, null, FAKE, 1 << 30, null) == E
+    sel = ksa.Selection(ksa.KSA_SEL_BLOCKS, FAKE.value, 257)
+    assert lib.ksa_paged_sparse_decode(pp, ctypes.byref(g2), FAKE, FAKE, FAKE, ctypes.byref(sel),
+                                       FAKE, null, FAKE, 1 << 30, null) == E
+    # recall: count < 1
+    assert lib.ksa_attention_recall(FAKE, FAKE, FAKE, 0, null) == E
