@@ -10,10 +10,11 @@
 //     16-byte loads that the waves take from a shared counter; each block's
 //     relevance (sum_h q_h) . S_j (fp32) becomes an order-preserving key in
 //     LDS, and the keys' range is gathered with LDS atomics;
-//  2. refresh (optional): the token rows of block (T-1)/Bs, loaded at the
-//     start (one per LPT-lane group) and held in registers during scoring,
-//     go through LDS to one group that sums them in fp64 in token order; the
-//     rounded mean is written to the summaries and scored from registers;
+//  2. refresh (optional), by wave 0 before it joins the scoring (the other
+//     waves start scoring at once, so the refresh is off the row's critical
+//     path): the token rows of block (T-1)/Bs go through LDS, each lane sums
+//     its channels in fp64 in token order, and the rounded mean is written
+//     to the summaries and scored;
 //  3. top-k: the bucket search of ksa_topk.h on the LDS keys (over the
 //     gathered range, so no separate min/max pass) writes the
 //     selected block ids, ascending, into the attention's LDS index stage
@@ -70,12 +71,11 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   constexpr int kStepKPT = (kStepMaxBlocks + kStepThreads - 1) / kStepThreads;  // keys per thread
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
-  constexpr int NGRP = kStepThreads / LPT;
   constexpr int U = kStepUnroll;
-  constexpr int RP = (kStepMaxBs + NGRP - 1) / NGRP;  // refresh rows per group
   constexpr bool kMfma = std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
   __shared__ uint32_t s_keys[kStepMaxBlocks];
   __shared__ uint4 s_buf[ref_stage_slots<T, D>()];
+  __shared__ uint4 s_mean[D / EPL];  // the refreshed block's rounded mean
   __shared__ TopkShared s_topk;
   __shared__ int s_next;           // next free scoring unit
   __shared__ uint32_t s_lo, s_hi;  // range of the row's keys
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   const Dims& d = s.a.d;
   const int row = blockIdx.x;
   const int b = row / d.Hkv, g = row - b * d.Hkv;
-  const int tid = threadIdx.x, li = tid % LPT, grp = tid / LPT;
+  const int tid = threadIdx.x, li = tid % LPT;
   // the row's length, blocks and k_eff; for a paged cache the attention
   // sees this row's length
   AttnArgs a = s.a;
@@ -105,22 +105,6 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   T* srow = (T*)s.summ + (int64_t)row * d.NBcap * D + li * EPL;
   const int jref = s.refresh ? (Trow - 1) / d.Bs : -1;
   const int nref = s.refresh ? Trow - jref * d.Bs : 0;
-
-  // The refresh block's rows are loaded up front (branch-free: without a
-  // refresh the row's first token stands in, unused) and consumed only
-  // after the scoring loop, so no wave waits on them before scoring.
-  uint4 rr[RP];
-  {
-    const int t0 = s.refresh ? jref * d.Bs : 0;
-    const int last = s.refresh ? nref - 1 : 0;
-    const T* kp;
-    if constexpr (PAGED)  // the block's page; its rows start the page's KV-head slab
-      kp = (const T*)a.k + ((int64_t)ptab[max(jref, 0)] * d.Hkv + g) * d.Bs * D + li * EPL;
-    else
-      kp = (const T*)a.k + ((int64_t)row * d.Tcap + t0) * D + li * EPL;
-#pragma unroll
-    for (int r = 0; r < RP; ++r) rr[r] = ld16(kp + (int64_t)min(grp + r * NGRP, last) * D);
-  }
 
   // the group's query rows (kept for the attention) and their fp32 sum, the
   // group query of block_score_kernel
@@ -180,7 +164,7 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   };
 
   // 1. scoring, two units in flight per wave (the refresh block is scored
-  // below).  Loads are unconditional (past the last unit they re-read the
+  // by step 2).  Loads are unconditional (past the last unit they re-read the
   // last block), so each unit waits only for its own loads.
   uint4 bufA[U], bufB[U];
   int ua = wave;
@@ -192,38 +176,39 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   }
   topk_clear(s_topk);
   __syncthreads();
-  for (;;) {
-    const int ub = grab();
-    load_unit(ub, bufB);
-    if (ua >= nu) break;
-    score_unit(ua, bufA);
-    ua = grab();
-    load_unit(ua, bufA);
-    if (ub >= nu) break;
-    score_unit(ub, bufB);
-  }
 
-  // 2. refresh: the block's rows go through LDS to group 0, which sums them
-  // in fp64 in token order (as block_summaries_kernel), stores the rounded
-  // mean and scores it
-  if (s.refresh) {
+  // 2. refresh, by wave 0 while the others score: the block's rows go to
+  // LDS (SPW rows per load instruction), lane c sums channels c, c+64, ...
+  // in fp64 in token order (as block_summaries_kernel), and group 0 stores
+  // the rounded mean and scores it as score_unit does
+  if (s.refresh && wave == 0) {
+    const T* kp;
+    if constexpr (PAGED)  // the block's page; its rows start the page's KV-head slab
+      kp = (const T*)a.k + ((int64_t)ptab[jref] * d.Hkv + g) * d.Bs * D + li * EPL;
+    else
+      kp = (const T*)a.k + ((int64_t)row * d.Tcap + (int64_t)jref * d.Bs) * D + li * EPL;
+    constexpr int RB = 4;  // load instructions in flight
+    for (int t0 = 0; t0 < nref; t0 += RB * SPW) {
+      uint4 r[RB];
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int t = grp + r * NGRP;
-      if (t < nref) s_ref[t * LPT + li] = rr[r];
-    }
-    __syncthreads();
-    if (tid < LPT) {
-      double acc[EPL];
+      for (int i = 0; i < RB; ++i) r[i] = ld16(kp + (int64_t)min(t0 + i * SPW + slot, nref - 1) * D);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
-      for (int t = 0; t < nref; ++t) {
-        float f[EPL];
-        KV<T>::widen(s_ref[t * LPT + li], f);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += (double)f[e];
+      for (int i = 0; i < RB; ++i) {
+        const int t = t0 + i * SPW + slot;
+        if (t < nref) s_ref[t * LPT + li] = r[i];
       }
-      const uint4 mb = mean_bits<T>(acc, nref);
+    }
+    wave_lds_fence();
+    const T* sr = reinterpret_cast<const T*>(s_ref);
+    T* sm = reinterpret_cast<T*>(s_mean);
+    for (int c = lane; c < D; c += 64) {
+      double acc = 0.0;
+      for (int t = 0; t < nref; ++t) acc += (double)KV<T>::widen1(sr[t * D + c]);
+      sm[c] = mean_elem<T>(acc, nref);
+    }
+    wave_lds_fence();
+    if (lane < LPT) {
+      const uint4 mb = s_mean[li];
       st16(srow + (int64_t)jref * D, mb);
       float f[EPL];
       KV<T>::widen(mb, f);
@@ -239,6 +224,18 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
       }
     }
   }
+
+  for (;;) {
+    const int ub = grab();
+    load_unit(ub, bufB);
+    if (ua >= nu) break;
+    score_unit(ua, bufA);
+    ua = grab();
+    load_unit(ua, bufA);
+    if (ub >= nu) break;
+    score_unit(ub, bufB);
+  }
+
   if (li == 0) {
     atomicMin(&s_lo, kmin);
     atomicMax(&s_hi, kmax);

@@ -28,6 +28,7 @@ struct KV<uint16_t> {
     f[6] = __uint_as_float(u.w << 16);
     f[7] = __uint_as_float(u.w & 0xffff0000u);
   }
+  __device__ __forceinline__ static float widen1(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 };
 
 template <>
@@ -39,6 +40,7 @@ struct KV<float> {
     f[2] = __uint_as_float(u.z);
     f[3] = __uint_as_float(u.w);
   }
+  __device__ __forceinline__ static float widen1(float x) { return x; }
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -155,6 +157,20 @@ __device__ __forceinline__ uint4 mean_bits<float>(const double* acc, int n) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = __float_as_uint((float)(acc[i] / (double)n));
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// One channel of mean_bits: the same division and rounding, as a T.
+template <typename T>
+__device__ __forceinline__ T mean_elem(double acc, int n);
+
+template <>
+__device__ __forceinline__ uint16_t mean_elem<uint16_t>(double acc, int n) {
+  return bf16_rne_from_f64(acc / (double)n);
+}
+
+template <>
+__device__ __forceinline__ float mean_elem<float>(double acc, int n) {
+  return (float)(acc / (double)n);
 }
 
 // ---------------------------------------------------------------- keys
