@@ -265,7 +265,7 @@ ksa_status ksa_paged_dense_decode(const ksa_problem* problem, const ksa_paged_kv
  * when T_b > N, else takes all of [0, T_b).  token_idx is [B, min(N, T)]
  * int32 (T the longest sequence), each row ascending and padded with -1;
  * votes (nullable) is [B, T] uint8, zero past each sequence's history.
- * Requires T - W <= 32768 here (else KSA_ERR_UNSUPPORTED).
+ * Same limits as ksa_vote_select, with T the longest sequence.
  * workspace: ksa_workspace_bytes(problem, KSA_OP_VOTE_SELECT, token_budget). */
 ksa_status ksa_paged_vote_select(const ksa_problem* problem, const ksa_paged_kv* paged,
                                  const void* q, const void* k_pool, int32_t token_budget,

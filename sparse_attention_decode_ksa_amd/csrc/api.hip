@@ -472,7 +472,6 @@ ksa_status ksa_paged_vote_select(const ksa_problem* problem, const ksa_paged_kv*
   if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
     return KSA_ERR_INVALID_ARGUMENT;
   if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
-  if (d.T > token_budget && d.T - recent_window > kPagedVoteMaxHistory) return KSA_ERR_UNSUPPORTED;
   const VotePlan plan = plan_vote(d, token_budget, recent_window);
   if (workspace_bytes < plan.total) return KSA_ERR_WORKSPACE_TOO_SMALL;
   if (plan.total && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;

@@ -134,7 +134,6 @@ hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void*
                                     const void* k_pool, int N, int W, int32_t* token_idx,
                                     uint8_t* votes, void* workspace, const VotePlan& plan,
                                     hipStream_t stream);
-constexpr int kPagedVoteMaxHistory = 32768;
 // Per-head sets: every head's own picks plus the window, token_idx [B, Hq, min(N, T)].
 hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
                                 int32_t* token_idx, void* workspace, const VotePlan& plan,

@@ -491,11 +491,13 @@ __global__ __launch_bounds__(kHeadThreads) void vote_head_select_kernel(
 // ------------------------------------------------------------------ 3
 __global__ __launch_bounds__(kCountThreads) void vote_count_kernel(
     const uint32_t* __restrict__ bits, int Hq, int hist, int words, int T,
-    uint8_t* __restrict__ votes8, uint8_t* __restrict__ votes, uint32_t* __restrict__ vhist) {
+    uint8_t* __restrict__ votes8, uint8_t* __restrict__ votes, uint32_t* __restrict__ vhist,
+    Dims d, VotePaging pg) {
   __shared__ uint32_t lh[256];
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const int t = blockIdx.x * kCountThreads + tid;
+  hist = vote_hist(pg, d, b, hist);  // this sequence's history (0: it does not vote)
   lh[tid] = 0u;  // kCountThreads == 256 bins
   __syncthreads();
   if (t < hist) {
@@ -515,14 +517,28 @@ __global__ __launch_bounds__(kCountThreads) void vote_count_kernel(
 // ------------------------------------------------------------------ 4
 __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
     const uint8_t* __restrict__ votes8, const uint32_t* __restrict__ vhist, int T, int hist, int kv,
-    int N, int W, int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes) {
+    int N, int W, int n_out, int32_t* __restrict__ token_idx, uint8_t* __restrict__ votes, Dims d,
+    VotePaging pg) {
   __shared__ uint32_t sh_v, sh_above;
   __shared__ int32_t s_pick[kSetStage];
   __shared__ uint32_t s_cnt[2][kSetSteps * (kSetThreads / 64)];  // per (step, wave): above, on
   __shared__ uint32_t s_tot[2];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  int32_t* out = token_idx + (int64_t)b * N;
+  int32_t* out = token_idx + (int64_t)b * n_out;
+  const int64_t vstride = (int64_t)((hist + 31) / 32) * 32;  // votes8 row stride (longest history)
+  if (pg.seq_lens) {  // this sequence's own length (T is then the longest)
+    const int Tb = min(max(pg.seq_lens[b], 1), pg.tstride * d.Bs);
+    if (Tb <= N) {  // no vote: the whole sequence, then -1
+      for (int i = tid; i < n_out; i += kSetThreads) out[i] = i < Tb ? i : -1;
+      if (votes)
+        for (int t = tid; t < T; t += kSetThreads) votes[(int64_t)b * T + t] = 0;
+      return;
+    }
+    hist = Tb - W;
+    if (votes)
+      for (int t = Tb + tid; t < T; t += kSetThreads) votes[(int64_t)b * T + t] = 0;
+  }
   for (int i = tid; i < W; i += kSetThreads) {
     out[kv + i] = hist + i;
     if (votes) votes[(int64_t)b * T + hist + i] = 0;
@@ -570,7 +586,7 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
   constexpr int NWV = kSetThreads / 64;
   const int lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
-  const uint32_t* vb = reinterpret_cast<const uint32_t*>(votes8 + (int64_t)b * ((hist + 31) / 32) * 32);
+  const uint32_t* vb = reinterpret_cast<const uint32_t*>(votes8 + (int64_t)b * vstride);
   const int nq = (hist + 3) / 4;  // vote words of four tokens
   const bool stage = kv <= kSetStage;  // uniform
   uint32_t carry_gt = 0, carry_eq = 0;
@@ -1024,11 +1040,11 @@ hipError_t vote_finish(const Dims& d, int N, int W, int n_out, int32_t* token_id
   }
   hipLaunchKernelGGL(vote_count_kernel, dim3((plan.hist + kCountThreads - 1) / kCountThreads, d.B),
                      dim3(kCountThreads), 0, stream, bits, d.Hq, plan.hist, plan.words, d.T, votes8,
-                     votes, vhist);
+                     votes, vhist, d, pg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(vote_set_kernel, dim3(d.B), dim3(kSetThreads), 0, stream, votes8, vhist, d.T,
-                     plan.hist, plan.kv, N, W, token_idx, votes);
+                     plan.hist, plan.kv, N, W, n_out, token_idx, votes, d, pg);
   return hipGetLastError();
 }
 }  // namespace

@@ -230,10 +230,15 @@ def test_variant_and_layer_validation():
     assert need > ksa.ksa_workspace_bytes(p, ksa.KSA_OP_VOTE_SELECT, 512)
     assert lib.ksa_vote_layer_decode(pp, FAKE, FAKE, FAKE, 512, 128, FAKE, null, FAKE, null, FAKE,
                                      0, null) == W_
-    # paged vote: histories longer than the one-kernel vote set
+    # paged vote: histories longer than the one-kernel vote set are supported,
+    # so only the workspace check stops this call
     pl = P(B=1, Hq=8, Hkv=2, D=128, T=40000, Tcap=40000, dtype=ksa.KSA_BF16)
     g = ksa.PagedKv(FAKE, FAKE, 2500, 3000)
     assert lib.ksa_paged_vote_select(ctypes.byref(pl), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,
+                                     null, FAKE, 0, null) == W_
+    # more query heads than a uint8 vote total counts
+    ph = P(B=1, Hq=256, Hkv=32, D=128, T=4000, Tcap=40000, dtype=ksa.KSA_BF16)
+    assert lib.ksa_paged_vote_select(ctypes.byref(ph), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,
                                      null, FAKE, 1 << 34, null) == U
     # paged sparse decode: per-head lists are not a paged kind; more blocks than the table holds
     sel = ksa.Selection(ksa.KSA_SEL_HEAD_TOKENS, FAKE.value, 4)

@@ -174,6 +174,8 @@ VOTE_PAGED = [
     dict(lens=[5000, 3000, 900, 1], Bs=16, Hq=32, Hkv=8, D=128, dtype="bf16", N=1024, W=256),  # MFMA
     dict(lens=[2100, 700, 1500], Bs=7, Hq=8, Hkv=2, D=64, dtype="f32", N=512, W=128),
     dict(lens=[400, 300], Bs=16, Hq=4, Hkv=2, D=64, dtype="bf16", N=512, W=64),    # all T_b <= N
+    # histories past 32768 tokens: the two-kernel tally and set, per-sequence lengths
+    dict(lens=[40000, 34000, 2000, 600], Bs=16, Hq=8, Hkv=2, D=128, dtype="bf16", N=1024, W=256),
 ]
 
 
@@ -215,6 +217,18 @@ def test_paged_vote_equals_contiguous_vote_bitwise():
     co, cl = ksa.ksa_sparse_decode(q, k, v, T, ci, ksa.KSA_SEL_TOKENS)
     torch.cuda.synchronize()
     assert torch.equal(po, co) and torch.equal(pl, cl)
+
+
+def test_paged_vote_equals_contiguous_vote_bitwise_long_history():
+    """Histories past 32768 tokens take the two-kernel tally; at one length
+    the paged and contiguous calls still agree bit for bit."""
+    T, Bs, N, W = 36000, 16, 2048, 512
+    w, q, k, v, kp, vp, table, seq = paged_inputs([T] * 2, Bs, seed=78, Hq=8, Hkv=2, D=128,
+                                                  dtype="bf16")
+    pi, pv = ksa.ksa_paged_vote_select(q, kp, table, seq, N, W, want_votes=True)
+    ci, cv = ksa.ksa_vote_select(q, k, T, N, W, want_votes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pi, ci) and torch.equal(pv[:, :T], cv)
 
 
 def test_paged_sparse_decode_of_the_steps_blocks_equals_the_step():
