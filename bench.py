@@ -67,8 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     ap.add_argument("--paged", default="none", choices=["none", "uniform", "ragged"],
-                    help="block top-k step on a paged cache (random page order): every "
-                         "sequence at T, or lengths drawn in [T/2, T]")
+                    help="the step on a paged cache (random page order; for c4 the vote "
+                         "path): every sequence at T, or lengths drawn in [T/2, T]")
     ap.add_argument("--schedule", action="store_true",
                     help="c4 shape: a LessIsMore layer schedule (2 dense layers, then a "
                          "selection layer every --select-every layers, sparse layers between), "
@@ -516,7 +516,8 @@ def paged_main(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
-    assert w.plant == "blocks", "--paged runs the block top-k workloads"
+    if w.plant == "tokens":
+        return paged_vote_main(args, w)
     B, Hq, Hkv, D, T, Bs, K = w.B, w.Hq, w.Hkv, w.D, w.T, w.Bs, w.top_k
     elt = 2 if w.dtype == "bf16" else 4
     rows = B * Hkv
@@ -620,6 +621,125 @@ def paged_main(args):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None, "avg_launch_ms": round(ms_step, 5),
                      "bytes_per_launch": step_bytes},
+        "cpu_baseline": None,
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def paged_vote_main(args, w):
+    """The vote-union workload on a paged cache (pages of 16 tokens in a seeded
+    random order, each sequence its own length): the selection step is
+    ksa_paged_vote_select + ksa_paged_sparse_decode over the set; the sparse
+    layer is the attention alone; the selection layer of the schedule is
+    ksa_paged_vote_layer_decode (dense attention plus the vote); dense is
+    ksa_paged_dense_decode."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_decode_ksa_amd as ksa
+    from sparse_attention_decode_ksa_amd.inputs import make_inputs, to_paged
+
+    lib = ksa.load_library()
+    R = Runner(lib, ksa)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, Hq, Hkv, D, T = w.B, w.Hq, w.Hkv, w.D, w.T
+    N, W, Bs = w.token_budget, w.recent_window, 16
+    elt = 2 if w.dtype == "bf16" else 4
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed * 7 + 1)
+    lens = (torch.randint(T // 2, T + 1, (B,), generator=gen).tolist() if args.paged == "ragged"
+            else [T] * B)
+    n_out = min(N, T)
+    layers = args.layers or 4
+    t0 = time.time()
+    L = []
+    for l in range(layers):
+        x = make_inputs(w, device=dev, seed=w.seed * 1000 + l)
+        kp, vp, table = to_paged(x["k"], x["v"], Bs, seed=w.seed * 1000 + l + 1)
+        del x["k"], x["v"]
+        x.update(kp=kp, vp=vp, table=table, seq=torch.tensor(lens, dtype=torch.int32, device=dev),
+                 idx=torch.empty((B, n_out), dtype=torch.int32, device=dev),
+                 out=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
+                 lse=torch.empty((B, Hq), dtype=torch.float32, device=dev))
+        L.append(x)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    prob = ksa.Problem(B, Hq, Hkv, D, T, L[0]["table"].shape[1] * Bs, Bs,
+                       ksa.KSA_BF16 if elt == 2 else ksa.KSA_F32, 0.0)
+    pp = ctypes.byref(prob)
+    stream = torch.cuda.Stream(device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    V = lambda t: ctypes.c_void_p(t.data_ptr())
+    ws_v = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_VOTE_SELECT, N), dev)
+    ws_a = ksa.new_workspace(max(1, ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_SPARSE_TOKENS, n_out)), dev)
+    ws_l = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_PAGED_VOTE_LAYER, N), dev)
+    ws_d = ksa.new_workspace(max(1, ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_PAGED_DENSE, 0)), dev)
+    for x in L:
+        x["pg"] = ksa.PagedKv(V(x["table"]).value, V(x["seq"]).value, x["table"].shape[1],
+                              x["kp"].shape[0])
+        pg = ctypes.byref(x["pg"])
+        x["sel"] = ksa.Selection(ksa.KSA_SEL_TOKENS, V(x["idx"]).value, n_out)
+        x["vote"] = (lib.ksa_paged_vote_select, (pp, pg, V(x["q"]), V(x["kp"]), N, W, V(x["idx"]),
+                                                 None, V(ws_v), ws_v.numel(), sp))
+        x["attn"] = (lib.ksa_paged_sparse_decode, (pp, pg, V(x["q"]), V(x["kp"]), V(x["vp"]),
+                                                   ctypes.byref(x["sel"]), V(x["out"]), V(x["lse"]),
+                                                   V(ws_a), ws_a.numel(), sp))
+        x["layer"] = (lib.ksa_paged_vote_layer_decode, (pp, pg, V(x["q"]), V(x["kp"]), V(x["vp"]), N,
+                                                        W, V(x["out"]), V(x["lse"]), V(x["idx"]),
+                                                        None, V(ws_l), ws_l.numel(), sp))
+        x["dense"] = (lib.ksa_paged_dense_decode, (pp, pg, V(x["q"]), V(x["kp"]), V(x["vp"]),
+                                                   V(x["out"]), V(x["lse"]), V(ws_d), ws_d.numel(),
+                                                   sp))
+    run = lambda key: (lambda i: R.run(L[i % layers][key]))
+
+    def sel_step(i):
+        R.run(L[i % layers]["vote"])
+        R.run(L[i % layers]["attn"])
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            sel_step(i)
+        ms_step = timed(torch, stream, args.steps, sel_step)
+        ms_sparse = timed(torch, stream, args.steps, run("attn"))
+        run("layer")(0)
+        ms_layer = timed(torch, stream, max(3, args.dense_steps), run("layer"))
+        run("dense")(0)
+        ms_dense = timed(torch, stream, args.dense_steps, run("dense"))
+    tl = np.array(lens)
+    hist = np.where(tl > N, tl - W, 0)
+    sel = np.minimum(tl, N)
+    q_bytes, out_bytes = B * Hq * D * elt, B * Hq * (D + 1) * 4
+    sparse_bytes = int(sel.sum()) * Hkv * D * elt * 2 + q_bytes + out_bytes + B * n_out * 4
+    step_bytes = int(hist.sum()) * Hkv * D * elt + q_bytes + sparse_bytes
+    dense_bytes = int(tl.sum()) * Hkv * D * elt * 2 + q_bytes + out_bytes
+    gbps = lambda n, ms: round(n / (ms * 1e-3) / 1e9, 1)
+    cfg = {"workload": "%s: %s" % (w.name, w.description), "batch": B, "q_heads": Hq,
+           "kv_heads": Hkv, "head_dim": D, "context": T, "layers_cycled": layers,
+           "token_budget": N, "recent_window": W, "page_size": Bs, "paged": args.paged,
+           "seq_len_mean": round(float(tl.mean()), 1), "seq_len_min": int(tl.min()),
+           "pages_per_layer": int(L[0]["kp"].shape[0])}
+    sparse_gbps = gbps(sparse_bytes, ms_sparse)
+    line = {
+        "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
+        "value": round(B / (ms_step * 1e-3), 1), "unit": "seqs*steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if elt == 2 else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q with planted tokens), paged in a random page order",
+        "config": cfg, "step_bytes": step_bytes, "step_gbps": gbps(step_bytes, ms_step),
+        "sparse_layer_step": {"ms": round(ms_sparse, 5), "value": round(B / (ms_sparse * 1e-3), 1),
+                              "gbps": sparse_gbps, "speedup_vs_dense": round(ms_dense / ms_sparse, 3)},
+        "selection_layer": {"ms": round(ms_layer, 5), "call": "ksa_paged_vote_layer_decode"},
+        "dense": {"ms_per_step": round(ms_dense, 5), "value": round(B / (ms_dense * 1e-3), 1),
+                  "gbps": gbps(dense_bytes, ms_dense)},
+        "speedup_vs_dense": round(ms_dense / ms_step, 3),
+        "roofline": {"kernel": "ksa_paged_sparse_decode over the shared set (sparse layer)",
+                     "bound": "hbm", "achieved": sparse_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(sparse_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms_sparse, 5), "bytes_per_launch": sparse_bytes},
         "cpu_baseline": None,
         "input_gen_s": round(gen_s, 2),
     }

@@ -358,6 +358,24 @@ ksa_status ksa_vote_layer_decode(const ksa_problem* problem, const void* q, cons
                                  float* out, float* lse, int32_t* token_idx, uint8_t* votes,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ksa_paged_vote_layer_decode -- ksa_vote_layer_decode on a paged cache with
+ * per-sequence lengths (the selection layer of the schedule above over the
+ * block-table layout the Kinetics explainer's section 五 says block sparsity
+ * fits):
+ *   out, lse   = ksa_paged_dense_decode (sequence b attends its T_b tokens);
+ *   token_idx, votes = ksa_paged_vote_select(token_budget, recent_window).
+ * For bf16, D = 128 and G in {4, 8} the paged dense walk writes the vote's
+ * keys from its own logits (K read once); other shapes run the two passes.
+ * token_idx and votes are bitwise those of ksa_paged_vote_select, out and
+ * lse those of ksa_paged_dense_decode.  Same limits as those two calls.
+ * workspace: ksa_workspace_bytes(problem, KSA_OP_PAGED_VOTE_LAYER,
+ * token_budget). */
+ksa_status ksa_paged_vote_layer_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       int32_t token_budget, int32_t recent_window, float* out,
+                                       float* lse, int32_t* token_idx, uint8_t* votes,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Operations for ksa_workspace_bytes. */
 enum {
   KSA_OP_SELECT_TOPK = 0,    /* param: top_k */
@@ -367,7 +385,8 @@ enum {
   KSA_OP_DENSE = 4,          /* param: unused */
   KSA_OP_PAGED_DENSE = 5,    /* param: unused */
   KSA_OP_VOTE_LAYER = 6,     /* param: token_budget */
-  KSA_OP_SPARSE_HEAD_TOKENS = 7 /* param: selection count (tokens per query head) */
+  KSA_OP_SPARSE_HEAD_TOKENS = 7, /* param: selection count (tokens per query head) */
+  KSA_OP_PAGED_VOTE_LAYER = 8    /* param: token_budget */
 };
 
 /* Workspace bytes a call needs for this problem; a pure host function of its

@@ -33,7 +33,8 @@ KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMA
 KSA_F32, KSA_BF16 = 0, 1
 KSA_SEL_BLOCKS, KSA_SEL_TOKENS, KSA_SEL_HEAD_TOKENS = 0, 1, 2
 (KSA_OP_SELECT_TOPK, KSA_OP_SPARSE_BLOCKS, KSA_OP_SPARSE_TOKENS, KSA_OP_VOTE_SELECT,
- KSA_OP_DENSE, KSA_OP_PAGED_DENSE, KSA_OP_VOTE_LAYER, KSA_OP_SPARSE_HEAD_TOKENS) = range(8)
+ KSA_OP_DENSE, KSA_OP_PAGED_DENSE, KSA_OP_VOTE_LAYER, KSA_OP_SPARSE_HEAD_TOKENS,
+ KSA_OP_PAGED_VOTE_LAYER) = range(9)
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
@@ -41,7 +42,8 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
             "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
-            "ksa_paged_sparse_decode", "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+            "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_workspace_bytes",
+            "ksa_status_string", "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -121,13 +123,15 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_paged_vote_select.argtypes = [PP, PG, P, P, I32, I32, P, P, P, SZ, P]
         lib.ksa_paged_sparse_decode.argtypes = [PP, PG, P, P, P, ctypes.POINTER(Selection), P, P,
                                                 P, SZ, P]
+        lib.ksa_paged_vote_layer_decode.argtypes = [PP, PG, P, P, P, I32, I32, P, P, P, P, P, SZ,
+                                                    P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:16]:
+        for name in EXPORTED[:17]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -594,6 +598,41 @@ def ksa_paged_vote_select(q: torch.Tensor, k_pool: torch.Tensor, block_table: to
                                      _dev(votes, "votes", torch.uint8, (B, T)), pws, nws,
                                      _stream(stream)), "ksa_paged_vote_select")
     return (token_idx, votes) if votes is not None else token_idx
+
+
+def ksa_paged_vote_layer_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                token_budget: int, recent_window: int,
+                                max_len: Optional[int] = None, out=None, lse=None,
+                                want_lse: bool = True, token_idx=None, votes=None,
+                                want_votes: bool = False, sm_scale: float = 0.0, workspace=None,
+                                stream=None):
+    """A token-selection layer on a paged cache: paged dense attention plus
+    the paged vote-union set from the same logits.  Returns (out [B,Hq,D]
+    fp32, lse [B,Hq] or None, token_idx [B,min(N,T_max)] int32 (-1 padded),
+    votes [B,T_max] uint8 or None)."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, sm_scale)
+    B, Hq, D = q.shape
+    T = prob.seq_len
+    n_out = min(token_budget, T)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if token_idx is None:
+        token_idx = torch.empty((B, n_out), dtype=torch.int32, device=q.device)
+    if want_votes and votes is None:
+        votes = torch.empty((B, T), dtype=torch.uint8, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_PAGED_VOTE_LAYER, token_budget, q.device, workspace)
+    _check(lib.ksa_paged_vote_layer_decode(
+        ctypes.byref(prob), ctypes.byref(pg), _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool", k_pool.dtype, k_pool.shape), int(token_budget), int(recent_window),
+        _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
+        _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
+        _dev(votes, "votes", torch.uint8, (B, T)), pws, nws, _stream(stream)),
+        "ksa_paged_vote_layer_decode")
+    return out, lse, token_idx, votes
 
 
 def ksa_paged_sparse_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

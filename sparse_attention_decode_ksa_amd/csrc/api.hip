@@ -87,6 +87,9 @@ size_t workspace_for(const ksa_problem& p, int32_t op, int32_t param) {
       // the vote's workspace (bound over every window), then the dense partials
       return ((plan_vote(d, param, 0).total + 255) & ~(size_t)255) +
              attention_workspace_bytes(d, plan_attention(d, 2, d.T));
+    case KSA_OP_PAGED_VOTE_LAYER:
+      return ((plan_vote(d, param, 0).total + 255) & ~(size_t)255) +
+             attention_workspace_bytes(d, plan_attention(d, 3, (int64_t)d.NB * d.Bs));
     default:
       return SIZE_MAX;
   }
@@ -130,10 +133,10 @@ const char* ksa_status_string(ksa_status status) {
 }
 
 size_t ksa_workspace_bytes(const ksa_problem* problem, int32_t op, int32_t param) {
-  const bool blocks =
-      op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS || op == KSA_OP_PAGED_DENSE;
+  const bool blocks = op == KSA_OP_SELECT_TOPK || op == KSA_OP_SPARSE_BLOCKS ||
+                      op == KSA_OP_PAGED_DENSE || op == KSA_OP_PAGED_VOTE_LAYER;
   if (check_problem(problem, blocks) != KSA_OK) return SIZE_MAX;
-  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_SPARSE_HEAD_TOKENS) return SIZE_MAX;
+  if (op < KSA_OP_SELECT_TOPK || op > KSA_OP_PAGED_VOTE_LAYER) return SIZE_MAX;
   if (op != KSA_OP_DENSE && op != KSA_OP_PAGED_DENSE && param < 1) return SIZE_MAX;
   return workspace_for(*problem, op, param);
 }
@@ -435,6 +438,53 @@ ksa_status ksa_vote_layer_decode(const ksa_problem* problem, const void* q, cons
   if (e != hipSuccess) return KSA_ERR_HIP;
   return from_hip(launch_vote_select(d, q, k, token_budget, recent_window, token_idx, votes,
                                      workspace, vplan, s));
+}
+
+ksa_status ksa_paged_vote_layer_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       int32_t token_budget, int32_t recent_window, float* out,
+                                       float* lse, int32_t* token_idx, uint8_t* votes,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k_pool || !v_pool || !out || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned4(out) ||
+      !aligned4(token_idx) || (lse && !aligned4(lse)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan vplan = plan_vote(d, token_budget, recent_window);
+  const size_t voff = (vplan.total + 255) & ~(size_t)255;
+  const AttnPlan aplan = plan_attention(d, 3, (int64_t)d.NB * d.Bs);
+  const size_t need = voff + attention_workspace_bytes(d, aplan);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = (hipStream_t)stream;
+  void* aws = (char*)workspace + voff;
+  if (dense_emits_vote_keys(d) && d.T > token_budget) {
+    // the paged dense walk writes each sequence's vote keys as it attends
+    VoteKeys vk;
+    vk.keys = (uint32_t*)((char*)workspace + vplan.keys_off);
+    vk.kstride = vplan.kstride;
+    vk.hist = vplan.hist;
+    vk.budget = token_budget;
+    vk.window = recent_window;
+    hipError_t e = launch_attention(d, 3, q, k_pool, v_pool, nullptr, 0, out, lse, aws, aplan, s,
+                                    &pk, &vk);
+    if (e != hipSuccess) return KSA_ERR_HIP;
+    return from_hip(launch_paged_vote_finish(d, pk, token_budget, recent_window, token_idx, votes,
+                                             workspace, vplan, s));
+  }
+  hipError_t e = launch_attention(d, 3, q, k_pool, v_pool, nullptr, 0, out, lse, aws, aplan, s, &pk);
+  if (e != hipSuccess) return KSA_ERR_HIP;
+  return from_hip(launch_paged_vote_select(d, pk, q, k_pool, token_budget, recent_window, token_idx,
+                                           votes, workspace, vplan, s));
 }
 
 ksa_status ksa_vote_select_per_head(const ksa_problem* problem, const void* q, const void* k,

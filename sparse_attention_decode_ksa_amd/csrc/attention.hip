@@ -24,13 +24,13 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_partial
   attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, nullptr, e0, KIND != 2);
 }
 
-template <int G, int KIND>
+template <int G, int KIND, bool VK = false>
 __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
   __shared__ int s_idx[kIdxStage];
   const int split = blockIdx.x % a.splits;
   const int row = blockIdx.x / a.splits;
   const int e0 = stage_indices<KIND, 16>(a, row, split, s_idx);
-  attn_row_mfma<G, KIND>(a, row, split, s_idx, nullptr, e0, KIND != 2);
+  attn_row_mfma<G, KIND, VK>(a, row, split, s_idx, nullptr, e0, KIND != 2);
 }
 
 #ifndef KSA_MFMA
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void attn_mfma_kernel(AttnArgs a) {
 // and the logical ids and pages of the blocks in this split's range are
 // staged in LDS (splits past a short row's end write an empty partial
 // state, which the merge weighs by zero).
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool VK = false>
 __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_dense_kernel(
     AttnArgs a0) {
   constexpr bool kMfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
@@ -58,6 +58,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_d
   a.d.T = Tb;
   a.ltot = nb * Bs;
   a.count = nb;
+  if constexpr (VK) a.vhist = Tb > a.vbudget ? Tb - a.vwindow : 0;  // this sequence's vote history
   const int nchunks = (a.ltot + CH - 1) / CH;
   const int c_begin = split * a.cps;
   const int c_end = min(c_begin + a.cps, nchunks);
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_d
     s_pg[i] = tb[e0 + i];
   }
   if constexpr (kMfma)
-    attn_row_mfma<G, 3>(a, row, split, s_idx, s_pg, e0, true);
+    attn_row_mfma<G, 3, VK>(a, row, split, s_idx, s_pg, e0, true);
   else
     attn_row_valu<T, D, G, 3>(a, row, split, s_idx, s_pg, e0, true);
 }
@@ -155,7 +156,14 @@ hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStrea
   const dim3 grid(rows * p.splits), block(p.nw * 64);
   constexpr bool mfma = KSA_MFMA && std::is_same<T, uint16_t>::value && D == 128 && G >= 4;
   if (kind == 3 && a.idx == nullptr) {  // paged dense: every block of the row
-    hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G>), grid, block, 0, s, a);
+    if constexpr (mfma) {
+      if (a.vkeys)
+        hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G>), grid, block, 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_paged_dense_kernel<T, D, G>), grid, block, 0, s, a);
+    }
   } else if (kind == 3) {
     hipLaunchKernelGGL((attn_paged_list_kernel<T, D, G, 3>), grid, block, 0, s, a);
   } else if (kind == 5) {
@@ -167,7 +175,12 @@ hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStrea
     switch (kind) {
       case 0: hipLaunchKernelGGL((attn_mfma_kernel<G, 0>), grid, block, 0, s, a); break;
       case 1: hipLaunchKernelGGL((attn_mfma_kernel<G, 1>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((attn_mfma_kernel<G, 2>), grid, block, 0, s, a); break;
+      default:
+        if (a.vkeys)
+          hipLaunchKernelGGL((attn_mfma_kernel<G, 2, true>), grid, block, 0, s, a);
+        else
+          hipLaunchKernelGGL((attn_mfma_kernel<G, 2>), grid, block, 0, s, a);
+        break;
     }
   } else {
     switch (kind) {
@@ -250,6 +263,8 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
     a.vkeys = vote_keys->keys;
     a.vkstride = vote_keys->kstride;
     a.vhist = vote_keys->hist;
+    a.vbudget = vote_keys->budget;
+    a.vwindow = vote_keys->window;
   }
   if (kind == 4) a.kv_div = kv_div;
   if (d.dtype == KSA_BF16) {

@@ -72,10 +72,12 @@ struct AttnArgs {
   int tstride;             // max_blocks
   int page_rows;           // Hkv * Bs: token rows per page
   // dense (kind 2) on MFMA: the order keys of the raw logits of history
-  // tokens t < vhist go to vkeys [B, Hq, vkstride] (the vote's scores)
+  // tokens t < vhist go to vkeys [B, Hq, vkstride] (the vote's scores); a
+  // paged dense walk sets vhist per row from vbudget and vwindow
   uint32_t* vkeys;
   int vkstride;
   int vhist;
+  int vbudget, vwindow;
   // kind 4 (one token list per query head): the rows are query heads
   // (d.Hkv = Hq, d.G = 1) and row (b, h) reads KV head h / kv_div
   int kv_div;
@@ -119,6 +121,8 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.vkeys = nullptr;
   a.vkstride = 0;
   a.vhist = 0;
+  a.vbudget = 0;
+  a.vwindow = 0;
   a.kv_div = 1;
   return a;
 }
@@ -434,9 +438,12 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
 // merged by plain sums.
 // Attention of one row (or one split of it) with MFMA QK^T (bf16, D = 128,
 // G in {4, 8}); indices staged as for attn_row_valu.
-template <int G, int KIND>
+// VK: the dense walk (kind 2, or kind 3 over every block) also writes the
+// vote's keys (a.vkeys); dense walks without a vote compile without them.
+template <int G, int KIND, bool VK = false>
 __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int split, const int* s_idx,
                                               const int* s_pg, int e0, bool sync) {
+  static_assert(!VK || KIND == 2 || KIND == 3, "vote keys come from dense walks");
   constexpr int D = 128;
   constexpr int EPL = 8;
   constexpr int LPT = 16;
@@ -515,10 +522,12 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
     f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[i]), qop[i], S, 0, 0, 0);
-    if constexpr (KIND == 2) {
+    if constexpr (VK) {
       // the selection layer: keys of head r's raw logits of tokens 4kg..4kg+3
-      // (the vote scorer's arithmetic, so the same keys), 16 bytes at a time
-      if (a.vkeys != nullptr && r < G) {
+      // (the vote scorer's arithmetic, so the same keys), 16 bytes at a time;
+      // positions are token ids in a dense walk (kind 3: over every block in
+      // order)
+      if (r < G) {
         const int t = (c0 + j * nw) * CH + 4 * kg;
         uint32_t* kout = a.vkeys + ((int64_t)b * d.Hq + g * G + r) * a.vkstride;
         if (t + 3 < a.vhist) {

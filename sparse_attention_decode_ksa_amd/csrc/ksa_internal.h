@@ -63,6 +63,9 @@ struct VoteKeys {
   uint32_t* keys;  // [B, Hq, kstride]
   int kstride;
   int hist;        // tokens t < hist get keys
+  // paged dense (kind 3): each sequence's own history instead, T_b - window
+  // when T_b > budget, else none
+  int budget = 0, window = 0;
 };
 // kind 4 (a token list per query head) takes d with Hkv = Hq and G = 1 and
 // kv_div = the real G: row (b, h) reads KV head h / kv_div.
@@ -128,12 +131,16 @@ hipError_t launch_vote_finish(const Dims& d, int N, int W, int32_t* token_idx, u
 // T <= N: the whole context, no vote.
 hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hipStream_t stream);
 // The vote on a paged cache with per-sequence lengths (d.T the longest):
-// token_idx [B, min(N, T)], -1 past a sequence shorter than N.  Needs
-// plan.words <= 1024 (the one-kernel vote set).
+// token_idx [B, min(N, T)], -1 past a sequence shorter than N.
 hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void* q,
                                     const void* k_pool, int N, int W, int32_t* token_idx,
                                     uint8_t* votes, void* workspace, const VotePlan& plan,
                                     hipStream_t stream);
+// The same vote from keys already in the workspace (written by the paged
+// dense walk with VoteKeys{budget N, window W}).
+hipError_t launch_paged_vote_finish(const Dims& d, const PagedKv& p, int N, int W,
+                                    int32_t* token_idx, uint8_t* votes, void* workspace,
+                                    const VotePlan& plan, hipStream_t stream);
 // Per-head sets: every head's own picks plus the window, token_idx [B, Hq, min(N, T)].
 hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
                                 int32_t* token_idx, void* workspace, const VotePlan& plan,

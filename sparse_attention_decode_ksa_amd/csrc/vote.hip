@@ -1073,6 +1073,15 @@ hipError_t launch_vote_select(const Dims& d, const void* q, const void* k, int N
   return vote_finish(d, N, W, N, token_idx, votes, workspace, plan, stream, voting, none, true);
 }
 
+hipError_t launch_paged_vote_finish(const Dims& d, const PagedKv& p, int N, int W,
+                                    int32_t* token_idx, uint8_t* votes, void* workspace,
+                                    const VotePlan& plan, hipStream_t stream) {
+  const VotePaging pg{p.table, p.seq_lens, p.max_blocks, N, W};
+  const int n_out = d.T < N ? d.T : N;
+  return vote_finish(d, N, W, n_out, token_idx, votes, workspace, plan, stream, HeadMask(), pg,
+                     d.T > N);
+}
+
 hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void* q,
                                     const void* k_pool, int N, int W, int32_t* token_idx,
                                     uint8_t* votes, void* workspace, const VotePlan& plan,

@@ -236,6 +236,17 @@ def test_variant_and_layer_validation():
     g = ksa.PagedKv(FAKE, FAKE, 2500, 3000)
     assert lib.ksa_paged_vote_select(ctypes.byref(pl), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,
                                      null, FAKE, 0, null) == W_
+    # paged selection layer: W > N, no paged description, a workspace smaller
+    # than asked (the asked size covers the vote and the paged dense partials)
+    pgv = ctypes.byref(pl)
+    assert lib.ksa_paged_vote_layer_decode(pgv, ctypes.byref(g), FAKE, FAKE, FAKE, 100, 200, FAKE,
+                                           null, FAKE, null, FAKE, 1 << 34, null) == E
+    assert lib.ksa_paged_vote_layer_decode(pgv, null, FAKE, FAKE, FAKE, 512, 128, FAKE, null, FAKE,
+                                           null, FAKE, 1 << 34, null) == E
+    lneed = ksa.ksa_workspace_bytes(pl, ksa.KSA_OP_PAGED_VOTE_LAYER, 512)
+    assert lneed >= ksa.ksa_workspace_bytes(pl, ksa.KSA_OP_VOTE_SELECT, 512)
+    assert lib.ksa_paged_vote_layer_decode(pgv, ctypes.byref(g), FAKE, FAKE, FAKE, 512, 128, FAKE,
+                                           null, FAKE, null, FAKE, 0, null) == W_
     # more query heads than a uint8 vote total counts
     ph = P(B=1, Hq=256, Hkv=32, D=128, T=4000, Tcap=40000, dtype=ksa.KSA_BF16)
     assert lib.ksa_paged_vote_select(ctypes.byref(ph), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,

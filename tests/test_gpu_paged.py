@@ -231,6 +231,45 @@ def test_paged_vote_equals_contiguous_vote_bitwise_long_history():
     assert torch.equal(pi, ci) and torch.equal(pv[:, :T], cv)
 
 
+LAYER_PAGED = [
+    dict(lens=[5000, 3000, 900, 1], Bs=16, Hq=32, Hkv=8, D=128, dtype="bf16", N=1024, W=256),  # G 4
+    dict(lens=[2500, 1200, 2047], Bs=32, Hq=16, Hkv=2, D=128, dtype="bf16", N=512, W=128),     # G 8
+    dict(lens=[1500, 400, 999], Bs=7, Hq=8, Hkv=4, D=64, dtype="f32", N=256, W=64),            # two passes
+    dict(lens=[300, 200], Bs=16, Hq=8, Hkv=2, D=128, dtype="bf16", N=512, W=128),              # no vote
+    dict(lens=[34000, 2000], Bs=16, Hq=8, Hkv=2, D=128, dtype="bf16", N=1024, W=256),          # long
+]
+
+
+@pytest.mark.parametrize("case", LAYER_PAGED, ids=lambda c: "G%d-%s-%s" % (
+    c["Hq"] // c["Hkv"], c["dtype"], "_".join(map(str, c["lens"]))))
+def test_paged_selection_layer_equals_dense_plus_vote(case):
+    """The paged selection layer gives ksa_paged_dense_decode's outputs and
+    ksa_paged_vote_select's set and votes, bit for bit (on MFMA shapes the
+    vote's keys come from the dense walk's own logits)."""
+    c = dict(case)
+    lens, Bs, N, W = c.pop("lens"), c.pop("Bs"), c.pop("N"), c.pop("W")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=sum(lens) % 991, **c)
+    out, lse, idx, votes = ksa.ksa_paged_vote_layer_decode(q, kp, vp, table, seq, N, W,
+                                                           want_votes=True)
+    do, dl = ksa.ksa_paged_dense_decode(q, kp, vp, table, seq)
+    vi, vv = ksa.ksa_paged_vote_select(q, kp, table, seq, N, W, want_votes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, do) and torch.equal(lse, dl)
+    assert torch.equal(idx, vi) and torch.equal(votes, vv)
+    # and the layer's set is the oracle's rule on the layer's own votes
+    from parity import check_votes
+    ids, vts = idx.cpu().numpy(), votes.cpu().numpy()
+    for b, T in enumerate(lens):
+        if T <= N:
+            assert ids[b][ids[b] >= 0].tolist() == list(range(T))
+            continue
+        if T > 6000:  # the oracle's logits of the long row are covered by the paged vote tests
+            continue
+        kb = gathered(kp, table, b, T, Bs)
+        lg = oracle.head_logits(np_bits(q[b:b + 1]), kb, T)
+        check_votes(vts[b:b + 1, :T], ids[b][None], lg, N, W)
+
+
 def test_paged_sparse_decode_of_the_steps_blocks_equals_the_step():
     """Attending the paged step's own ids (padding included) with the
     separate paged call gives the step's outputs (to fp32 merge order)."""
