@@ -306,6 +306,21 @@ ksa_status ksa_select_topk_ex(const ksa_problem* problem, const void* q, const v
                               float* block_scores, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ksa_paged_select_topk_ex -- ksa_select_topk_ex for a paged cache with
+ * per-sequence lengths (the summaries of ksa_paged_block_summaries,
+ * [B, Hkv, max_blocks, D]): row (b, g) ranks its own NB_b blocks and keeps
+ * k_eff_b = min(top_k, NB_b); block_idx is [B, Hkv, top_k] int32, the ids
+ * ascending, then -1.  force_last_block keeps each row's own newest block
+ * (T_b - 1)/Bs.  block_scores (nullable) is [B, Hkv, NB] (NB from the
+ * problem's T, the longest sequence); entries past a row's NB_b are not
+ * written.  The ids feed ksa_paged_sparse_decode (KSA_SEL_BLOCKS).  Same
+ * limits and workspace as ksa_select_topk (NB from the problem's T). */
+ksa_status ksa_paged_select_topk_ex(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                    const void* q, const void* summaries,
+                                    const ksa_select_options* options, int32_t* block_idx,
+                                    float* block_scores, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* ksa_vote_select_heads -- ksa_vote_select where only the listed query heads
  * vote (voting_heads: host array of num_voting distinct heads < Hq, read
  * during the call).  One head is the random-head ablation of the LessIsMore

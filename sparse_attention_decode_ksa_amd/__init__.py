@@ -11,10 +11,12 @@ Function names match the C entry points: ``ksa_block_summaries``,
 ``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode``,
 ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
-``ksa_paged_dense_decode``, the selection variants ``ksa_select_topk_ex`` and
-``ksa_vote_select_heads``, the diagnostic ``ksa_attention_recall``, the
-selection layer ``ksa_vote_layer_decode``,
-``ksa_workspace_bytes``, ``ksa_status_string``.
+``ksa_paged_dense_decode``, ``ksa_paged_vote_select``, ``ksa_paged_sparse_decode``,
+``ksa_paged_vote_layer_decode`` and ``ksa_paged_select_topk_ex``, the selection
+variants ``ksa_select_topk_ex``, ``ksa_vote_select_heads`` and
+``ksa_vote_select_per_head``, the diagnostic ``ksa_attention_recall``, the
+selection layer ``ksa_vote_layer_decode``, ``ksa_workspace_bytes``,
+``ksa_status_string`` and ``ksa_version``.
 """
 from __future__ import annotations
 
@@ -42,8 +44,8 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_paged_block_summaries", "ksa_paged_block_topk_decode", "ksa_paged_dense_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
             "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
-            "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_workspace_bytes",
-            "ksa_status_string", "ksa_version")
+            "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_paged_select_topk_ex",
+            "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -125,13 +127,15 @@ def load_library(path: str = LIB_PATH):
                                                 P, SZ, P]
         lib.ksa_paged_vote_layer_decode.argtypes = [PP, PG, P, P, P, I32, I32, P, P, P, P, P, SZ,
                                                     P]
+        lib.ksa_paged_select_topk_ex.argtypes = [PP, PG, P, P, ctypes.POINTER(SelectOptions), P, P,
+                                                 P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:17]:
+        for name in EXPORTED[:18]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -486,6 +490,40 @@ def ksa_select_topk_ex(q: torch.Tensor, summaries: torch.Tensor, seq_len: int, b
                                   _dev(block_idx, "block_idx", torch.int32, (B, Hkv, keff)),
                                   _dev(block_scores, "block_scores", torch.float32, (B, Hkv, nb)),
                                   pws, nws, _stream(stream)), "ksa_select_topk_ex")
+    return (block_idx, block_scores) if block_scores is not None else block_idx
+
+
+def ksa_paged_select_topk_ex(q: torch.Tensor, summaries: torch.Tensor, block_table: torch.Tensor,
+                             seq_lens: torch.Tensor, block_size: int, top_k: int,
+                             aggregate: int = KSA_AGG_SUM, force_last_block: bool = False,
+                             max_len: Optional[int] = None, block_idx=None, block_scores=None,
+                             want_scores: bool = False, sm_scale: float = 0.0, workspace=None,
+                             stream=None):
+    """ksa_select_topk_ex for a paged cache: every row ranks its own NB_b
+    blocks of summaries [B,Hkv,max_blocks,D]; block_idx [B,Hkv,top_k] int32
+    (ascending, -1 past k_eff_b); force_last_block keeps each row's newest."""
+    lib = load_library()
+    B, Hkv, max_blocks, D = summaries.shape
+    if max_len is None:
+        max_len = int(seq_lens.max().item())
+    prob = Problem(B, q.shape[1], Hkv, D, int(max_len), max_blocks * int(block_size),
+                   int(block_size), _dtype_code(summaries), float(sm_scale))
+    pg = PagedKv(_dev(block_table, "block_table", torch.int32, (B, max_blocks)),
+                 _dev(seq_lens, "seq_lens", torch.int32, (B,)), max_blocks, 1)
+    nb = nblocks(int(max_len), block_size)
+    if block_idx is None:
+        block_idx = torch.empty((B, Hkv, top_k), dtype=torch.int32, device=q.device)
+    if want_scores and block_scores is None:
+        block_scores = torch.empty((B, Hkv, nb), dtype=torch.float32, device=q.device)
+    opts = SelectOptions(int(top_k), int(aggregate), 1 if force_last_block else 0)
+    ws, pws, nws = _workspace(prob, KSA_OP_SELECT_TOPK, top_k, q.device, workspace)
+    _check(lib.ksa_paged_select_topk_ex(ctypes.byref(prob), ctypes.byref(pg),
+                                        _dev(q, "q", summaries.dtype, (B, prob.num_q_heads, D)),
+                                        _dev(summaries, "summaries"), ctypes.byref(opts),
+                                        _dev(block_idx, "block_idx", torch.int32, (B, Hkv, top_k)),
+                                        _dev(block_scores, "block_scores", torch.float32,
+                                             (B, Hkv, nb)),
+                                        pws, nws, _stream(stream)), "ksa_paged_select_topk_ex")
     return (block_idx, block_scores) if block_scores is not None else block_idx
 
 

@@ -356,6 +356,38 @@ ksa_status ksa_select_topk_ex(const ksa_problem* problem, const void* q, const v
                                      (hipStream_t)stream, var));
 }
 
+ksa_status ksa_paged_select_topk_ex(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                    const void* q, const void* summaries,
+                                    const ksa_select_options* options, int32_t* block_idx,
+                                    float* block_scores, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!options) return KSA_ERR_INVALID_ARGUMENT;
+  if (options->aggregate != KSA_AGG_SUM && options->aggregate != KSA_AGG_MAX)
+    return KSA_ERR_INVALID_ARGUMENT;
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  const int32_t top_k = options->top_k;
+  if (!q || !summaries || !block_idx || top_k < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(summaries) || !aligned4(block_idx) ||
+      (block_scores && !aligned4(block_scores)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.NB > kSelectMaxBlocks) return KSA_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(*problem, KSA_OP_SELECT_TOPK, top_k);
+  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  SelectVariant var;
+  var.agg_max = options->aggregate == KSA_AGG_MAX ? 1 : 0;
+  var.forced_block = options->force_last_block ? 0 : -1;  // each row's own newest block
+  var.seq_lens = pk.seq_lens;
+  var.id_stride = top_k;
+  return from_hip(launch_select_topk(d, q, summaries, top_k, block_idx, block_scores, workspace,
+                                     (hipStream_t)stream, var));
+}
+
 ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, const void* k,
                                  int32_t token_budget, int32_t recent_window,
                                  const int32_t* voting_heads, int32_t num_voting,

@@ -93,7 +93,9 @@ size_t select_workspace_bytes(const Dims& d);
 // instead of the group's sum; always keep one block (its key made maximal).
 struct SelectVariant {
   int agg_max = 0;
-  int forced_block = -1;
+  int forced_block = -1;      // with seq_lens: >= 0 forces each row's own newest block
+  const int32_t* seq_lens = nullptr;  // per-sequence lengths (a paged cache), or uniform d.T
+  int id_stride = 0;          // with seq_lens: ids per row in block_idx (-1 past k_eff_b)
 };
 hipError_t launch_select_topk(const Dims& d, const void* q, const void* summaries, int keff,
                               int32_t* block_idx, float* block_scores, void* workspace,

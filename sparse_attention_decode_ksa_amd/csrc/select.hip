@@ -44,10 +44,19 @@ constexpr int kTopkThreads = 256;  // one workgroup per row; also the histogram 
 // in registers) instead of the group's sum.  forced >= 0: that block's key
 // is the largest possible, so it is always selected (its score is still
 // reported as computed).
+// Row block counts: uniform d.NB, or from seq_lens (rows of a paged cache;
+// key rows keep the stride d.NB, the longest row's).
+__device__ __forceinline__ int row_blocks(const Dims& d, const int32_t* seq_lens, int b) {
+  if (!seq_lens) return d.NB;
+  const int Tb = min(max(seq_lens[b], 1), d.NBcap * d.Bs);
+  return (Tb + d.Bs - 1) / d.Bs;
+}
+
 template <typename T, int D, bool MAXAGG>
 __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
     const T* __restrict__ q, const T* __restrict__ summ, Dims d, uint32_t* __restrict__ keys,
-    float* __restrict__ block_scores, float score_scale, int forced) {
+    float* __restrict__ block_scores, float score_scale, int forced,
+    const int32_t* __restrict__ seq_lens) {
   constexpr int EPL = KV<T>::EPL;
   constexpr int LPT = D / EPL;
   constexpr int NGRP = kScoreThreads / LPT;
@@ -55,7 +64,10 @@ __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
   const int row = blockIdx.y;
   const int b = row / d.Hkv, g = row % d.Hkv;
   const int li = threadIdx.x % LPT, grp = threadIdx.x / LPT;
-  const int NB = d.NB;
+  const int NB = row_blocks(d, seq_lens, b);
+  const int kst = d.NB;  // key row stride
+  if (seq_lens && forced >= 0) forced = NB - 1;  // each row's own newest block
+  if ((int)blockIdx.x * TILE >= NB) return;  // uniform: a tile past this row's blocks
   const int j0 = blockIdx.x * TILE + grp;
   const T* sp = summ + (int64_t)row * d.NBcap * D + li * EPL;
 
@@ -87,8 +99,8 @@ __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
         }
       }
       if (li == 0 && j < NB) {
-        keys[(int64_t)row * NB + j] = j == forced ? 0xFFFFFFFFu : order_key(best);
-        if (block_scores) block_scores[(int64_t)row * NB + j] = best * score_scale;
+        keys[(int64_t)row * kst + j] = j == forced ? 0xFFFFFFFFu : order_key(best);
+        if (block_scores) block_scores[(int64_t)row * kst + j] = best * score_scale;
       }
     }
     return;
@@ -113,27 +125,34 @@ __global__ __launch_bounds__(kScoreThreads) void block_score_kernel(
     for (int e = 0; e < EPL; ++e) p = fmaf(qs[e], f[e], p);
     p = group_sum<LPT>(p);
     if (li == 0 && j < NB) {
-      keys[(int64_t)row * NB + j] = j == forced ? 0xFFFFFFFFu : order_key(p);
-      if (block_scores) block_scores[(int64_t)row * NB + j] = p * score_scale;
+      keys[(int64_t)row * kst + j] = j == forced ? 0xFFFFFFFFu : order_key(p);
+      if (block_scores) block_scores[(int64_t)row * kst + j] = p * score_scale;
     }
   }
 }
 
 // Top-k of one row per workgroup of kTopkThreads threads, keys in registers
 // (thread t holds positions [t*KPT, (t+1)*KPT)).
+// With seq_lens every row has its own block count NB_b and selects
+// min(keff, NB_b) ids into a row of id_stride entries, -1 after them.
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
-    const uint32_t* __restrict__ gkeys, int NB, int keff, int32_t* __restrict__ block_idx) {
+    const uint32_t* __restrict__ gkeys, Dims d, int keff, int32_t* __restrict__ block_idx,
+    const int32_t* __restrict__ seq_lens, int id_stride) {
   __shared__ TopkShared sh;
   const int row = blockIdx.x;
-  const uint32_t* rk = gkeys + (int64_t)row * NB;
+  const uint32_t* rk = gkeys + (int64_t)row * d.NB;
+  const int n = row_blocks(d, seq_lens, row / d.Hkv);
+  const int ke = min(keff, n);
   const int j0 = threadIdx.x * KPT;
   uint32_t key[KPT];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) key[i] = j0 + i < NB ? rk[j0 + i] : 0u;
-  int32_t* out = block_idx + (int64_t)row * keff;
+  for (int i = 0; i < KPT; ++i) key[i] = j0 + i < n ? rk[j0 + i] : 0u;
+  int32_t* out = block_idx + (int64_t)row * (seq_lens ? id_stride : keff);
+  if (seq_lens)
+    for (int i = ke + (int)threadIdx.x; i < id_stride; i += kTopkThreads) out[i] = -1;
   topk_clear(sh);
-  row_topk<KPT>(key, KPT, j0, NB, keff, sh, [&](int rank, int j) { out[rank] = j; });
+  row_topk<KPT>(key, KPT, j0, n, ke, sh, [&](int rank, int j) { out[rank] = j; });
 }
 
 template <typename T, int D>
@@ -145,22 +164,25 @@ hipError_t launch_typed(const Dims& d, const void* q, const void* summ, int keff
   const dim3 sgrid((d.NB + TILE - 1) / TILE, rows);
   if (var.agg_max)
     hipLaunchKernelGGL((block_score_kernel<T, D, true>), sgrid, dim3(kScoreThreads), 0, s,
-                       (const T*)q, (const T*)summ, d, keys, scores, d.scale, var.forced_block);
+                       (const T*)q, (const T*)summ, d, keys, scores, d.scale, var.forced_block,
+                       var.seq_lens);
   else
     hipLaunchKernelGGL((block_score_kernel<T, D, false>), sgrid, dim3(kScoreThreads), 0, s,
                        (const T*)q, (const T*)summ, d, keys, scores, d.scale / (float)d.G,
-                       var.forced_block);
+                       var.forced_block, var.seq_lens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(rows), block(kTopkThreads);
+  const int32_t* sl = var.seq_lens;
+  const int ids = var.id_stride;
   if (d.NB <= 4 * kTopkThreads)
-    hipLaunchKernelGGL((topk_rows_kernel<4>), grid, block, 0, s, keys, d.NB, keff, idx);
+    hipLaunchKernelGGL((topk_rows_kernel<4>), grid, block, 0, s, keys, d, keff, idx, sl, ids);
   else if (d.NB <= 8 * kTopkThreads)
-    hipLaunchKernelGGL((topk_rows_kernel<8>), grid, block, 0, s, keys, d.NB, keff, idx);
+    hipLaunchKernelGGL((topk_rows_kernel<8>), grid, block, 0, s, keys, d, keff, idx, sl, ids);
   else if (d.NB <= 16 * kTopkThreads)
-    hipLaunchKernelGGL((topk_rows_kernel<16>), grid, block, 0, s, keys, d.NB, keff, idx);
+    hipLaunchKernelGGL((topk_rows_kernel<16>), grid, block, 0, s, keys, d, keff, idx, sl, ids);
   else
-    hipLaunchKernelGGL((topk_rows_kernel<64>), grid, block, 0, s, keys, d.NB, keff, idx);
+    hipLaunchKernelGGL((topk_rows_kernel<64>), grid, block, 0, s, keys, d, keff, idx, sl, ids);
   return hipGetLastError();
 }
 

@@ -247,6 +247,13 @@ def test_variant_and_layer_validation():
     assert lneed >= ksa.ksa_workspace_bytes(pl, ksa.KSA_OP_VOTE_SELECT, 512)
     assert lib.ksa_paged_vote_layer_decode(pgv, ctypes.byref(g), FAKE, FAKE, FAKE, 512, 128, FAKE,
                                            null, FAKE, null, FAKE, 0, null) == W_
+    # paged selection variants: no options, a bad aggregate, k < 1
+    assert lib.ksa_paged_select_topk_ex(pgv, ctypes.byref(g), FAKE, FAKE, null, FAKE, null, FAKE,
+                                        1 << 34, null) == E
+    assert lib.ksa_paged_select_topk_ex(pgv, ctypes.byref(g), FAKE, FAKE, ctypes.byref(bad), FAKE,
+                                        null, FAKE, 1 << 34, null) == E
+    assert lib.ksa_paged_select_topk_ex(pgv, ctypes.byref(g), FAKE, FAKE, ctypes.byref(zero), FAKE,
+                                        null, FAKE, 1 << 34, null) == E
     # more query heads than a uint8 vote total counts
     ph = P(B=1, Hq=256, Hkv=32, D=128, T=4000, Tcap=40000, dtype=ksa.KSA_BF16)
     assert lib.ksa_paged_vote_select(ctypes.byref(ph), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,

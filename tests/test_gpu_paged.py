@@ -1,5 +1,7 @@
 """GPU parity of the paged-cache calls: ksa_paged_block_summaries,
-ksa_paged_block_topk_decode and ksa_paged_dense_decode.
+ksa_paged_block_topk_decode, ksa_paged_dense_decode, ksa_paged_vote_select,
+ksa_paged_sparse_decode, ksa_paged_vote_layer_decode and
+ksa_paged_select_topk_ex.
 
 Pools come from the seeded contiguous inputs through to_paged (a random page
 order plus spare pages of noise); every sequence has its own length.  Each
@@ -283,3 +285,68 @@ def test_paged_sparse_decode_of_the_steps_blocks_equals_the_step():
     o2, l2 = ksa.ksa_paged_sparse_decode(q, kp, vp, table, seq, idx, ksa.KSA_SEL_BLOCKS)
     torch.cuda.synchronize()
     assert float((out - o2).abs().max()) <= 1e-5 and float((lse - l2).abs().max()) <= 1e-5
+
+
+# ----------------------------------------------------------------------------- selection variants
+SELECT_PAGED = [
+    dict(lens=[3000, 700, 16, 1], Bs=16, Hq=8, Hkv=2, D=128, dtype="bf16", top_k=20),
+    dict(lens=[1200, 999, 65], Bs=32, Hq=16, Hkv=2, D=128, dtype="bf16", top_k=8),
+    dict(lens=[500, 333], Bs=7, Hq=4, Hkv=4, D=64, dtype="f32", top_k=30),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_PAGED, ids=case_id)
+def test_paged_select_ex_sum_equals_the_paged_steps_selection(case):
+    """With the method's own ranking the separate paged selection picks the
+    paged step's blocks, bit for bit (the same scores and the same search)."""
+    c = dict(case)
+    lens, Bs, top_k = c.pop("lens"), c.pop("Bs"), c.pop("top_k")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=sum(lens) % 313, **c)
+    s = torch.zeros((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    idx = ksa.ksa_paged_select_topk_ex(q, s, table, seq, Bs, top_k)
+    _, _, sidx = ksa.ksa_paged_block_topk_decode(q, kp, vp, s.clone(), table, seq, top_k,
+                                                 refresh_last_block=False, want_block_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, sidx)
+
+
+@pytest.mark.parametrize("agg", [ksa.KSA_AGG_SUM, ksa.KSA_AGG_MAX])
+@pytest.mark.parametrize("case", SELECT_PAGED, ids=case_id)
+def test_paged_select_ex_variants_match_oracle_per_sequence(case, agg):
+    """MAX aggregation and the forced newest block on a paged cache: each row
+    ranks its own blocks by the oracle's relevance of that aggregation, keeps
+    its own newest block, and pads with -1."""
+    c = dict(case)
+    lens, Bs, top_k = c.pop("lens"), c.pop("Bs"), c.pop("top_k")
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=sum(lens) % 317 + agg, **c)
+    s = torch.zeros((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    name = "max" if agg == ksa.KSA_AGG_MAX else "sum"
+    plain, sc = ksa.ksa_paged_select_topk_ex(q, s, table, seq, Bs, top_k, aggregate=agg,
+                                             want_scores=True)
+    forced = ksa.ksa_paged_select_topk_ex(q, s, table, seq, Bs, top_k, aggregate=agg,
+                                          force_last_block=True)
+    torch.cuda.synchronize()
+    sb_all = np_bits(s)
+    for b, T in enumerate(lens):
+        nb = ksa.nblocks(T, Bs)
+        keff = min(top_k, nb)
+        qb = np_bits(q[b:b + 1])
+        raw, scaled = oracle.group_scores(qb, sb_all[b:b + 1], T, Bs, Tcap=table.shape[1] * Bs,
+                                          aggregate=name)
+        raw = raw.reshape(w.Hkv, -1)
+        ids = plain[b].cpu().numpy()
+        assert np.all(ids[:, keff:] == -1)
+        check_block_selection(np.ascontiguousarray(ids[:, :keff]), raw, top_k)
+        np.testing.assert_allclose(sc[b, :, :nb].cpu().numpy(), scaled[0], rtol=0,
+                                   atol=1e-5 * max(1.0, float(np.abs(scaled).max())))
+        fid = forced[b].cpu().numpy()
+        assert np.all(fid[:, keff:] == -1)
+        fid = fid[:, :keff]
+        assert np.all(np.any(fid == nb - 1, axis=1))
+        if keff < nb:
+            rest = raw.copy()
+            rest[:, nb - 1] = raw.min() - 1.0
+            others = np.array([[j for j in row if j != nb - 1] for row in fid])
+            check_block_selection(others, rest, keff - 1)
