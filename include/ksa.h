@@ -333,6 +333,15 @@ ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, cons
                                  int32_t* token_idx, uint8_t* votes, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ksa_paged_vote_select_heads -- ksa_vote_select_heads on a paged cache with
+ * per-sequence lengths (the outputs of ksa_paged_vote_select, from the listed
+ * heads' picks only).  Same limits and workspace as ksa_paged_vote_select. */
+ksa_status ksa_paged_vote_select_heads(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                       const void* q, const void* k_pool, int32_t token_budget,
+                                       int32_t recent_window, const int32_t* voting_heads,
+                                       int32_t num_voting, int32_t* token_idx, uint8_t* votes,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ksa_vote_select_per_head -- the per-head-sets ablation (LessIsMore
  * explainer, section 五: each head keeps its own set): every query head h
  * keeps its own first Kv = N - W history tokens by (q_h . k desc, t asc),

@@ -12,7 +12,8 @@ Function names match the C entry points: ``ksa_block_summaries``,
 ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
 ``ksa_paged_dense_decode``, ``ksa_paged_vote_select``, ``ksa_paged_sparse_decode``,
-``ksa_paged_vote_layer_decode`` and ``ksa_paged_select_topk_ex``, the selection
+``ksa_paged_vote_layer_decode``, ``ksa_paged_select_topk_ex`` and
+``ksa_paged_vote_select_heads``, the selection
 variants ``ksa_select_topk_ex``, ``ksa_vote_select_heads`` and
 ``ksa_vote_select_per_head``, the diagnostic ``ksa_attention_recall``, the
 selection layer ``ksa_vote_layer_decode``, ``ksa_workspace_bytes``,
@@ -45,7 +46,8 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
             "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
             "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_paged_select_topk_ex",
-            "ksa_workspace_bytes", "ksa_status_string", "ksa_version")
+            "ksa_paged_vote_select_heads", "ksa_workspace_bytes", "ksa_status_string",
+            "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -129,13 +131,14 @@ def load_library(path: str = LIB_PATH):
                                                     P]
         lib.ksa_paged_select_topk_ex.argtypes = [PP, PG, P, P, ctypes.POINTER(SelectOptions), P, P,
                                                  P, SZ, P]
+        lib.ksa_paged_vote_select_heads.argtypes = [PP, PG, P, P, I32, I32, P, I32, P, P, P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:18]:
+        for name in EXPORTED[:19]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -635,6 +638,32 @@ def ksa_paged_vote_select(q: torch.Tensor, k_pool: torch.Tensor, block_table: to
                                      _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
                                      _dev(votes, "votes", torch.uint8, (B, T)), pws, nws,
                                      _stream(stream)), "ksa_paged_vote_select")
+    return (token_idx, votes) if votes is not None else token_idx
+
+
+def ksa_paged_vote_select_heads(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                                seq_lens: torch.Tensor, token_budget: int, recent_window: int,
+                                voting_heads, max_len: Optional[int] = None, token_idx=None,
+                                votes=None, want_votes: bool = False, workspace=None,
+                                stream=None):
+    """ksa_paged_vote_select with only the listed query heads voting."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, 0.0)
+    B, T = q.shape[0], prob.seq_len
+    n_out = min(token_budget, T)
+    heads = (ctypes.c_int32 * len(voting_heads))(*[int(h) for h in voting_heads])
+    if token_idx is None:
+        token_idx = torch.empty((B, n_out), dtype=torch.int32, device=q.device)
+    if want_votes and votes is None:
+        votes = torch.empty((B, T), dtype=torch.uint8, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_SELECT, token_budget, q.device, workspace)
+    _check(lib.ksa_paged_vote_select_heads(ctypes.byref(prob), ctypes.byref(pg),
+                                           _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+                                           int(token_budget), int(recent_window),
+                                           ctypes.cast(heads, ctypes.c_void_p), len(voting_heads),
+                                           _dev(token_idx, "token_idx", torch.int32, (B, n_out)),
+                                           _dev(votes, "votes", torch.uint8, (B, T)), pws, nws,
+                                           _stream(stream)), "ksa_paged_vote_select_heads")
     return (token_idx, votes) if votes is not None else token_idx
 
 

@@ -112,6 +112,21 @@ ksa_status check_paged(const ksa_problem& p, const ksa_paged_kv* pg, PagedKv* ou
   return KSA_OK;
 }
 
+// The voting heads as a bitmask: num_voting distinct heads < Hq (and < 256).
+ksa_status head_mask(const ksa_problem& p, const int32_t* voting_heads, int32_t num_voting,
+                     HeadMask* mask) {
+  if (!voting_heads || num_voting < 1 || num_voting > p.num_q_heads)
+    return KSA_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 8; ++i) mask->w[i] = 0u;
+  for (int32_t i = 0; i < num_voting; ++i) {
+    const int32_t h = voting_heads[i];
+    if (h < 0 || h >= p.num_q_heads || h > 255) return KSA_ERR_INVALID_ARGUMENT;
+    if ((mask->w[h >> 5] >> (h & 31)) & 1u) return KSA_ERR_INVALID_ARGUMENT;  // listed twice
+    mask->w[h >> 5] |= 1u << (h & 31);
+  }
+  return KSA_OK;
+}
+
 }  // namespace
 }  // namespace ksa
 
@@ -388,6 +403,33 @@ ksa_status ksa_paged_select_topk_ex(const ksa_problem* problem, const ksa_paged_
                                      (hipStream_t)stream, var));
 }
 
+ksa_status ksa_paged_vote_select_heads(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                       const void* q, const void* k_pool, int32_t token_budget,
+                                       int32_t recent_window, const int32_t* voting_heads,
+                                       int32_t num_voting, int32_t* token_idx, uint8_t* votes,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  HeadMask mask;
+  st = head_mask(*problem, voting_heads, num_voting, &mask);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k_pool || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned4(token_idx)) return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan plan = plan_vote(d, token_budget, recent_window);
+  if (workspace_bytes < plan.total) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.total && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_paged_vote_select(d, pk, q, k_pool, token_budget, recent_window, token_idx,
+                                           votes, workspace, plan, (hipStream_t)stream, mask));
+}
+
 ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, const void* k,
                                  int32_t token_budget, int32_t recent_window,
                                  const int32_t* voting_heads, int32_t num_voting,
@@ -395,16 +437,9 @@ ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, cons
                                  size_t workspace_bytes, void* stream) {
   ksa_status st = check_problem(problem, false);
   if (st != KSA_OK) return st;
-  if (!voting_heads || num_voting < 1 || num_voting > problem->num_q_heads)
-    return KSA_ERR_INVALID_ARGUMENT;
   HeadMask mask;
-  for (int i = 0; i < 8; ++i) mask.w[i] = 0u;
-  for (int32_t i = 0; i < num_voting; ++i) {
-    const int32_t h = voting_heads[i];
-    if (h < 0 || h >= problem->num_q_heads || h > 255) return KSA_ERR_INVALID_ARGUMENT;
-    if ((mask.w[h >> 5] >> (h & 31)) & 1u) return KSA_ERR_INVALID_ARGUMENT;  // listed twice
-    mask.w[h >> 5] |= 1u << (h & 31);
-  }
+  st = head_mask(*problem, voting_heads, num_voting, &mask);
+  if (st != KSA_OK) return st;
   const Dims d = make_dims(*problem);
   if (!q || !k || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned4(token_idx)) return KSA_ERR_INVALID_ARGUMENT;

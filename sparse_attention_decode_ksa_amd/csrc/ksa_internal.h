@@ -137,7 +137,7 @@ hipError_t launch_vote_all(const Dims& d, int32_t* token_idx, uint8_t* votes, hi
 hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void* q,
                                     const void* k_pool, int N, int W, int32_t* token_idx,
                                     uint8_t* votes, void* workspace, const VotePlan& plan,
-                                    hipStream_t stream);
+                                    hipStream_t stream, const HeadMask& voting = HeadMask());
 // The same vote from keys already in the workspace (written by the paged
 // dense walk with VoteKeys{budget N, window W}).
 hipError_t launch_paged_vote_finish(const Dims& d, const PagedKv& p, int N, int W,

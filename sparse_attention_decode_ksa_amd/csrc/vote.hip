@@ -1085,7 +1085,7 @@ hipError_t launch_paged_vote_finish(const Dims& d, const PagedKv& p, int N, int 
 hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void* q,
                                     const void* k_pool, int N, int W, int32_t* token_idx,
                                     uint8_t* votes, void* workspace, const VotePlan& plan,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, const HeadMask& voting) {
   const VotePaging pg{p.table, p.seq_lens, p.max_blocks, N, W};
   const int n_out = d.T < N ? d.T : N;
   const bool any_vote = d.T > N;  // d.T is the longest sequence
@@ -1094,7 +1094,7 @@ hipError_t launch_paged_vote_select(const Dims& d, const PagedKv& p, const void*
     hipError_t e = launch_scores_any(d, q, k_pool, plan.hist, plan.kstride, keys, stream, pg);
     if (e != hipSuccess) return e;
   }
-  return vote_finish(d, N, W, n_out, token_idx, votes, workspace, plan, stream, HeadMask(), pg,
+  return vote_finish(d, N, W, n_out, token_idx, votes, workspace, plan, stream, voting, pg,
                      any_vote);
 }
 

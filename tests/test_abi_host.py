@@ -247,6 +247,13 @@ def test_variant_and_layer_validation():
     assert lneed >= ksa.ksa_workspace_bytes(pl, ksa.KSA_OP_VOTE_SELECT, 512)
     assert lib.ksa_paged_vote_layer_decode(pgv, ctypes.byref(g), FAKE, FAKE, FAKE, 512, 128, FAKE,
                                            null, FAKE, null, FAKE, 0, null) == W_
+    # paged voting heads: empty, out of range, repeated
+    for heads in ([], [8], [-1], [2, 2]):
+        arr = (ctypes.c_int32 * max(1, len(heads)))(*(heads or [0]))
+        st = lib.ksa_paged_vote_select_heads(pgv, ctypes.byref(g), FAKE, FAKE, 512, 128,
+                                             ctypes.cast(arr, ctypes.c_void_p), len(heads), FAKE,
+                                             null, FAKE, 1 << 34, null)
+        assert st == E, heads
     # paged selection variants: no options, a bad aggregate, k < 1
     assert lib.ksa_paged_select_topk_ex(pgv, ctypes.byref(g), FAKE, FAKE, null, FAKE, null, FAKE,
                                         1 << 34, null) == E

@@ -350,3 +350,32 @@ def test_paged_select_ex_variants_match_oracle_per_sequence(case, agg):
             rest[:, nb - 1] = raw.min() - 1.0
             others = np.array([[j for j in row if j != nb - 1] for row in fid])
             check_block_selection(others, rest, keff - 1)
+
+
+@pytest.mark.parametrize("heads", [[0], [3, 9], list(range(16))])
+def test_paged_vote_of_chosen_heads(heads):
+    """Only the listed heads vote on a paged cache: at one length it is the
+    contiguous call bit for bit; with ragged lengths each sequence's votes
+    are the listed heads' picks over its own history (oracle rule)."""
+    N, W, Bs = 512, 128, 16
+    w, q, k, v, kp, vp, table, seq = paged_inputs([3000] * 2, Bs, seed=81 + len(heads), Hq=16,
+                                                  Hkv=4, D=128, dtype="bf16")
+    pi, pv = ksa.ksa_paged_vote_select_heads(q, kp, table, seq, N, W, heads, want_votes=True)
+    ci, cv = ksa.ksa_vote_select_heads(q, k, 3000, N, W, heads, want_votes=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pi, ci) and torch.equal(pv[:, :3000], cv)
+    from parity import check_votes
+    lens = [2500, 400, 1800]
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=91 + len(heads), Hq=16, Hkv=4,
+                                                  D=128, dtype="bf16")
+    idx, votes = ksa.ksa_paged_vote_select_heads(q, kp, table, seq, N, W, heads, want_votes=True)
+    torch.cuda.synchronize()
+    ids, vts = idx.cpu().numpy(), votes.cpu().numpy()
+    for b, T in enumerate(lens):
+        row = ids[b][ids[b] >= 0]
+        if T <= N:
+            assert row.tolist() == list(range(T))
+            continue
+        kb = gathered(kp, table, b, T, Bs)
+        lg = oracle.head_logits(np_bits(q[b:b + 1]), kb, T)[:, heads]
+        check_votes(vts[b:b + 1, :T], row[None], lg, N, W)
