@@ -274,10 +274,11 @@ ksa_status ksa_paged_vote_select(const ksa_problem* problem, const ksa_paged_kv*
 
 /* ksa_paged_sparse_decode -- ksa_sparse_decode on a paged cache with
  * per-sequence lengths, for BLOCKS (logical block ids [B, Hkv, count], e.g.
- * ksa_paged_block_topk_decode's) and TOKENS (token ids [B, count], e.g.
- * ksa_paged_vote_select's); negative entries are padding and are skipped,
- * as are tokens at or past T_b.  workspace: ksa_workspace_bytes(problem,
- * KSA_OP_SPARSE_BLOCKS or KSA_OP_SPARSE_TOKENS, sel->count). */
+ * ksa_paged_block_topk_decode's), TOKENS (token ids [B, count], e.g.
+ * ksa_paged_vote_select's) and HEAD_TOKENS (token ids [B, Hq, count], e.g.
+ * ksa_paged_vote_select_per_head's); negative entries are padding and are
+ * skipped, as are tokens at or past T_b.  workspace: ksa_workspace_bytes(
+ * problem, KSA_OP_SPARSE_BLOCKS, _TOKENS or _HEAD_TOKENS, sel->count). */
 ksa_status ksa_paged_sparse_decode(const ksa_problem* problem, const ksa_paged_kv* paged,
                                    const void* q, const void* k_pool, const void* v_pool,
                                    const ksa_selection* sel, float* out, float* lse,
@@ -336,6 +337,16 @@ ksa_status ksa_vote_select_heads(const ksa_problem* problem, const void* q, cons
 /* ksa_paged_vote_select_heads -- ksa_vote_select_heads on a paged cache with
  * per-sequence lengths (the outputs of ksa_paged_vote_select, from the listed
  * heads' picks only).  Same limits and workspace as ksa_paged_vote_select. */
+/* ksa_paged_vote_select_per_head -- ksa_vote_select_per_head on a paged cache
+ * with per-sequence lengths: token_idx [B, Hq, min(N, T)] (T the longest
+ * sequence), every row ascending; a sequence no longer than N gives all its
+ * T_b tokens, then -1.  Same limits and workspace as ksa_paged_vote_select. */
+ksa_status ksa_paged_vote_select_per_head(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                          const void* q, const void* k_pool,
+                                          int32_t token_budget, int32_t recent_window,
+                                          int32_t* token_idx, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 ksa_status ksa_paged_vote_select_heads(const ksa_problem* problem, const ksa_paged_kv* paged,
                                        const void* q, const void* k_pool, int32_t token_budget,
                                        int32_t recent_window, const int32_t* voting_heads,

@@ -12,8 +12,8 @@ Function names match the C entry points: ``ksa_block_summaries``,
 ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
 ``ksa_paged_dense_decode``, ``ksa_paged_vote_select``, ``ksa_paged_sparse_decode``,
-``ksa_paged_vote_layer_decode``, ``ksa_paged_select_topk_ex`` and
-``ksa_paged_vote_select_heads``, the selection
+``ksa_paged_vote_layer_decode``, ``ksa_paged_select_topk_ex``,
+``ksa_paged_vote_select_heads`` and ``ksa_paged_vote_select_per_head``, the selection
 variants ``ksa_select_topk_ex``, ``ksa_vote_select_heads`` and
 ``ksa_vote_select_per_head``, the diagnostic ``ksa_attention_recall``, the
 selection layer ``ksa_vote_layer_decode``, ``ksa_workspace_bytes``,
@@ -46,8 +46,8 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
             "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
             "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_paged_select_topk_ex",
-            "ksa_paged_vote_select_heads", "ksa_workspace_bytes", "ksa_status_string",
-            "ksa_version")
+            "ksa_paged_vote_select_heads", "ksa_paged_vote_select_per_head", "ksa_workspace_bytes",
+            "ksa_status_string", "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -132,13 +132,14 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_paged_select_topk_ex.argtypes = [PP, PG, P, P, ctypes.POINTER(SelectOptions), P, P,
                                                  P, SZ, P]
         lib.ksa_paged_vote_select_heads.argtypes = [PP, PG, P, P, I32, I32, P, I32, P, P, P, SZ, P]
+        lib.ksa_paged_vote_select_per_head.argtypes = [PP, PG, P, P, I32, I32, P, P, SZ, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:19]:
+        for name in EXPORTED[:20]:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -667,6 +668,31 @@ def ksa_paged_vote_select_heads(q: torch.Tensor, k_pool: torch.Tensor, block_tab
     return (token_idx, votes) if votes is not None else token_idx
 
 
+def ksa_paged_vote_select_per_head(q: torch.Tensor, k_pool: torch.Tensor,
+                                   block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                   token_budget: int, recent_window: int,
+                                   max_len: Optional[int] = None, token_idx=None, workspace=None,
+                                   stream=None):
+    """Per-head sets on a paged cache: token_idx [B, Hq, min(N, T_max)] int32
+    (a sequence no longer than N: its T_b tokens, then -1), for
+    ksa_paged_sparse_decode with KSA_SEL_HEAD_TOKENS."""
+    lib = load_library()
+    prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, 0.0)
+    B, Hq = q.shape[0], q.shape[1]
+    n_out = min(token_budget, prob.seq_len)
+    if token_idx is None:
+        token_idx = torch.empty((B, Hq, n_out), dtype=torch.int32, device=q.device)
+    ws, pws, nws = _workspace(prob, KSA_OP_VOTE_SELECT, token_budget, q.device, workspace)
+    _check(lib.ksa_paged_vote_select_per_head(ctypes.byref(prob), ctypes.byref(pg),
+                                              _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+                                              int(token_budget), int(recent_window),
+                                              _dev(token_idx, "token_idx", torch.int32,
+                                                   (B, Hq, n_out)),
+                                              pws, nws, _stream(stream)),
+           "ksa_paged_vote_select_per_head")
+    return token_idx
+
+
 def ksa_paged_vote_layer_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                 block_table: torch.Tensor, seq_lens: torch.Tensor,
                                 token_budget: int, recent_window: int,
@@ -707,8 +733,9 @@ def ksa_paged_sparse_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
                             kind: int = KSA_SEL_TOKENS, max_len: Optional[int] = None, out=None,
                             lse=None, want_lse: bool = True, sm_scale: float = 0.0,
                             workspace=None, stream=None):
-    """Attention over selected blocks ([B,Hkv,count]) or a shared token list
-    ([B,count]) of a paged cache; negative entries are skipped."""
+    """Attention over selected blocks ([B,Hkv,count]), a shared token list
+    ([B,count]) or a list per query head ([B,Hq,count]) of a paged cache;
+    negative entries are skipped."""
     lib = load_library()
     prob, pg = _paged_args(q, k_pool, block_table, seq_lens, max_len, sm_scale)
     B, Hq, D = q.shape
@@ -717,9 +744,11 @@ def ksa_paged_sparse_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    ishape = (B, k_pool.shape[1], count) if kind == KSA_SEL_BLOCKS else (B, count)
+    ishape = {KSA_SEL_BLOCKS: (B, k_pool.shape[1], count), KSA_SEL_TOKENS: (B, count),
+              KSA_SEL_HEAD_TOKENS: (B, Hq, count)}[kind]
     sel = Selection(int(kind), _dev(idx, "idx", torch.int32, ishape), int(count))
-    op = KSA_OP_SPARSE_BLOCKS if kind == KSA_SEL_BLOCKS else KSA_OP_SPARSE_TOKENS
+    op = {KSA_SEL_BLOCKS: KSA_OP_SPARSE_BLOCKS, KSA_SEL_TOKENS: KSA_OP_SPARSE_TOKENS,
+          KSA_SEL_HEAD_TOKENS: KSA_OP_SPARSE_HEAD_TOKENS}[kind]
     ws, pws, nws = _workspace(prob, op, count, q.device, workspace)
     _check(lib.ksa_paged_sparse_decode(ctypes.byref(prob), ctypes.byref(pg),
                                        _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),

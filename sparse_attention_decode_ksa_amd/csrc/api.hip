@@ -574,6 +574,30 @@ ksa_status ksa_vote_select_per_head(const ksa_problem* problem, const void* q, c
                                        plan, (hipStream_t)stream));
 }
 
+ksa_status ksa_paged_vote_select_per_head(const ksa_problem* problem, const ksa_paged_kv* paged,
+                                          const void* q, const void* k_pool,
+                                          int32_t token_budget, int32_t recent_window,
+                                          int32_t* token_idx, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  ksa_status st = check_problem(problem, true);
+  if (st != KSA_OK) return st;
+  PagedKv pk;
+  st = check_paged(*problem, paged, &pk);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k_pool || !token_idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned4(token_idx)) return KSA_ERR_INVALID_ARGUMENT;
+  if (token_budget < 1 || recent_window < 0 || recent_window > token_budget)
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (d.Hq > 255) return KSA_ERR_UNSUPPORTED;
+  if (d.T > token_budget && (d.T - recent_window) > (1 << 21)) return KSA_ERR_UNSUPPORTED;
+  const VotePlan plan = plan_vote(d, token_budget, recent_window);
+  if (workspace_bytes < plan.total) return KSA_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.total && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_vote_per_head(d, q, k_pool, token_budget, recent_window, token_idx,
+                                       workspace, plan, (hipStream_t)stream, &pk));
+}
+
 ksa_status ksa_paged_vote_select(const ksa_problem* problem, const ksa_paged_kv* paged,
                                  const void* q, const void* k_pool, int32_t token_budget,
                                  int32_t recent_window, int32_t* token_idx, uint8_t* votes,
@@ -602,7 +626,8 @@ ksa_status ksa_paged_sparse_decode(const ksa_problem* problem, const ksa_paged_k
                                    void* workspace, size_t workspace_bytes, void* stream) {
   if (!sel) return KSA_ERR_INVALID_ARGUMENT;
   const bool blocks = sel->kind == KSA_SEL_BLOCKS;
-  if (!blocks && sel->kind != KSA_SEL_TOKENS) return KSA_ERR_INVALID_ARGUMENT;
+  if (!blocks && sel->kind != KSA_SEL_TOKENS && sel->kind != KSA_SEL_HEAD_TOKENS)
+    return KSA_ERR_INVALID_ARGUMENT;
   ksa_status st = check_problem(problem, true);
   if (st != KSA_OK) return st;
   PagedKv pk;
@@ -617,6 +642,17 @@ ksa_status ksa_paged_sparse_decode(const ksa_problem* problem, const ksa_paged_k
   if (blocks && sel->count > pk.max_blocks) return KSA_ERR_INVALID_ARGUMENT;
   if (!blocks && sel->count > d.Tcap) return KSA_ERR_INVALID_ARGUMENT;
   if (blocks && (int64_t)sel->count * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
+  if (sel->kind == KSA_SEL_HEAD_TOKENS) {  // rows are query heads, each its own group
+    Dims dh = d;
+    dh.Hkv = d.Hq;
+    dh.G = 1;
+    const AttnPlan plan = plan_attention(dh, 6, sel->count);
+    const size_t need = attention_workspace_bytes(dh, plan);
+    if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+    if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
+    return from_hip(launch_attention(dh, 6, q, k_pool, v_pool, sel->idx, sel->count, out, lse,
+                                     workspace, plan, (hipStream_t)stream, &pk, nullptr, d.G));
+  }
   const int kind = blocks ? 3 : 5;
   const int64_t ltot = blocks ? (int64_t)sel->count * d.Bs : sel->count;
   const AttnPlan plan = plan_attention(d, kind, ltot);

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_d
 
 // Attention over a given list on a paged cache: kind 3 = block ids
 // [B, Hkv, count] (logical, -1 = padding), kind 5 = token ids [B, count]
-// shared by the sequence's heads (-1 = padding).  The row's length comes from
+// shared by the sequence's heads (-1 = padding), kind 6 = token ids
+// [B, Hq, count], one list per query head (rows are query heads, G = 1).  The row's length comes from
 // seq_lens; the ids of this split's range and their pages (kind 3) or pool
 // rows (kind 5) are staged in LDS.
 template <typename T, int D, int G, int KIND>
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_l
   } else {
     e0 = c_begin * CH;
     e1 = min(a.ltot, c_end * CH);
-    src = a.idx + (int64_t)b * a.count;
+    src = a.idx + (int64_t)(KIND == 6 ? row : b) * a.count;
   }
   const int nbb = (Tb + Bs - 1) / Bs;
   for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) {
@@ -168,6 +169,9 @@ hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStrea
     hipLaunchKernelGGL((attn_paged_list_kernel<T, D, G, 3>), grid, block, 0, s, a);
   } else if (kind == 5) {
     hipLaunchKernelGGL((attn_paged_list_kernel<T, D, G, 5>), grid, block, 0, s, a);
+  } else if (kind == 6) {  // rows are query heads: one head per row
+    if constexpr (G == 1)
+      hipLaunchKernelGGL((attn_paged_list_kernel<T, D, 1, 6>), grid, block, 0, s, a);
   } else if (kind == 4) {  // rows are query heads: one head per row
     if constexpr (G == 1)
       hipLaunchKernelGGL((attn_partial_kernel<T, D, 1, 4>), grid, block, 0, s, a);
@@ -234,7 +238,7 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   }
   // a workgroup's index slice must fit the LDS stage
   int64_t cap = INT64_MAX;
-  if (kind == 1 || kind == 4 || kind == 5) cap = kIdxStage / ch;
+  if (kind == 1 || kind == 4 || kind == 5 || kind == 6) cap = kIdxStage / ch;
   if (kind == 0 || kind == 3) cap = ((int64_t)(kIdxStage - 2) * d.Bs) / ch;
   if (cps > cap) cps = cap;
   if (cps < 1) cps = 1;
@@ -266,7 +270,8 @@ hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* 
     a.vbudget = vote_keys->budget;
     a.vwindow = vote_keys->window;
   }
-  if (kind == 4) a.kv_div = kv_div;
+  if (kind == 4 || kind == 6) a.kv_div = kv_div;
+  if (kind == 6) a.page_rows = (d.Hkv / kv_div) * d.Bs;  // d has a row per query head
   if (d.dtype == KSA_BF16) {
     if (d.D == 64) return launch_g<uint16_t, 64>(a, kind, plan, stream);
     return launch_g<uint16_t, 128>(a, kind, plan, stream);

@@ -98,8 +98,7 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.idx = idx;
   a.count = count;
   a.d = d;
-  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs
-                                     : ((kind == 1 || kind == 4 || kind == 5) ? count : d.T);
+  a.ltot = (kind == 0 || kind == 3) ? count * d.Bs : (kind == 2 ? d.T : count);
   a.bs_shift = -1;
   if ((kind == 0 || kind == 3) && (d.Bs & (d.Bs - 1)) == 0) {
     int sh = 0;
@@ -144,9 +143,10 @@ __device__ __forceinline__ void resolve_chunk(const AttnArgs& a, const int* s_id
       ok[i] = p < a.ltot;
       const int at = min(max(p - e0, 0), kIdxStage - 1);  // in range whenever ok
       tok[i] = ok[i] ? s_idx[at] : 0;
-    } else if constexpr (KIND == 5) {
-      // a shared token list over a paged cache: s_idx holds the token ids
-      // (negative: padding, skipped), s_pg their pool rows
+    } else if constexpr (KIND == 5 || KIND == 6) {
+      // a token list over a paged cache (5: shared by the sequence's heads, 6:
+      // one per query head): s_idx holds the token ids (negative: padding,
+      // skipped), s_pg their pool rows
       const int at = min(max(p - e0, 0), kIdxStage - 1);
       ok[i] = p < a.ltot && s_idx[at] >= 0 && s_idx[at] < a.d.T;
       tok[i] = ok[i] ? s_pg[at] : 0;
@@ -328,6 +328,7 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   const int b = row / d.Hkv, g = row - b * d.Hkv;
   const int64_t kvrow =
       ((KIND == 3 || KIND == 5) ? (int64_t)g * d.Bs * D
+       : KIND == 6 ? (int64_t)(g / a.kv_div) * d.Bs * D
        : KIND == 4 ? ((int64_t)b * (d.Hkv / a.kv_div) + g / a.kv_div) * d.Tcap * D
                    : (int64_t)row * d.Tcap * D) +
       li * EPL;

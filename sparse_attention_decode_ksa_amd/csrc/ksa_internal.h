@@ -144,9 +144,11 @@ hipError_t launch_paged_vote_finish(const Dims& d, const PagedKv& p, int N, int 
                                     int32_t* token_idx, uint8_t* votes, void* workspace,
                                     const VotePlan& plan, hipStream_t stream);
 // Per-head sets: every head's own picks plus the window, token_idx [B, Hq, min(N, T)].
+// paged: K is a page pool and every sequence has its own length (d.T the
+// longest); token_idx is [B, Hq, min(N, T)], rows of short sequences -1 padded.
 hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
                                 int32_t* token_idx, void* workspace, const VotePlan& plan,
-                                hipStream_t stream);
+                                hipStream_t stream, const PagedKv* paged = nullptr);
 // Whether dense attention of this shape runs the MFMA body (and can emit the
 // vote's keys while it attends).
 inline bool dense_emits_vote_keys(const Dims& d) {

@@ -952,14 +952,24 @@ namespace {
 // exactly Kv bits) in ascending order, then the W most recent tokens.
 // Thread t owns words [t*R, (t+1)*R) of the bitmask; one workgroup scan.
 constexpr int kHeadSetThreads = 256;
+// With paging (pg.seq_lens) each sequence has its own history, and a
+// sequence no longer than N takes all its tokens, then -1.
 __global__ __launch_bounds__(kHeadSetThreads) void head_set_kernel(
     const uint32_t* __restrict__ bits, int words, int hist, int kv, int W, int n_out,
-    int32_t* __restrict__ token_idx) {
+    int32_t* __restrict__ token_idx, Dims d, VotePaging pg) {
   __shared__ uint32_t s_scan[16];
   const int tid = threadIdx.x;
   const int64_t hr = blockIdx.x;
   const uint32_t* br = bits + hr * words;
   int32_t* out = token_idx + hr * n_out;
+  if (pg.seq_lens) {
+    const int Tb = min(max(pg.seq_lens[hr / d.Hq], 1), pg.tstride * d.Bs);
+    if (Tb <= pg.N) {
+      for (int i = tid; i < n_out; i += kHeadSetThreads) out[i] = i < Tb ? i : -1;
+      return;
+    }
+    hist = Tb - W;
+  }
   for (int i = tid; i < W; i += kHeadSetThreads) out[kv + i] = hist + i;
   const int R = (words + kHeadSetThreads - 1) / kHeadSetThreads;
   uint32_t n = 0;
@@ -982,34 +992,42 @@ __global__ __launch_bounds__(kHeadSetThreads) void head_set_kernel(
 }
 
 // T <= N: every head attends the whole context.
-__global__ void head_all_kernel(int T, int rows, int32_t* __restrict__ token_idx) {
+// Every row keeps all its tokens (T <= N): row r of T entries; with paging
+// row (b, h) holds its sequence's T_b tokens, then -1.
+__global__ void head_all_kernel(int T, int rows, int32_t* __restrict__ token_idx, Dims d,
+                                VotePaging pg) {
   const int64_t n = (int64_t)rows * T;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    token_idx[i] = (int32_t)(i % T);
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int col = (int)(i % T);
+    int lim = T;
+    if (pg.seq_lens) lim = min(max(pg.seq_lens[(i / T) / d.Hq], 1), pg.tstride * d.Bs);
+    token_idx[i] = col < lim ? col : -1;
+  }
 }
 }  // namespace
 
 hipError_t launch_vote_per_head(const Dims& d, const void* q, const void* k, int N, int W,
                                 int32_t* token_idx, void* workspace, const VotePlan& plan,
-                                hipStream_t stream) {
+                                hipStream_t stream, const PagedKv* paged) {
   const int rows = d.B * d.Hq;
+  const VotePaging pg = paged ? VotePaging{paged->table, paged->seq_lens, paged->max_blocks, N, W}
+                              : VotePaging{nullptr, nullptr, 0, N, W};
   if (d.T <= N) {
     hipLaunchKernelGGL(head_all_kernel, dim3(std::min<int64_t>(4096, ((int64_t)rows * d.T + 255) / 256)),
-                       dim3(256), 0, stream, d.T, rows, token_idx);
+                       dim3(256), 0, stream, d.T, rows, token_idx, d, pg);
     return hipGetLastError();
   }
   char* ws = (char*)workspace;
   uint32_t* keys = (uint32_t*)(ws + plan.keys_off);
   uint32_t* bits = (uint32_t*)(ws + plan.bits_off);
   uint32_t* vhist = (uint32_t*)(ws + plan.vhist_off);
-  const VotePaging none{nullptr, nullptr, 0, N, W};
-  hipError_t e = launch_scores_any(d, q, k, plan.hist, plan.kstride, keys, stream, none);
+  hipError_t e = launch_scores_any(d, q, k, plan.hist, plan.kstride, keys, stream, pg);
   if (e != hipSuccess) return e;
-  e = launch_head_select(d, plan, keys, bits, vhist, HeadMask(), stream, none);
+  e = launch_head_select(d, plan, keys, bits, vhist, HeadMask(), stream, pg);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(head_set_kernel, dim3(rows), dim3(kHeadSetThreads), 0, stream, bits,
-                     plan.words, plan.hist, plan.kv, W, N, token_idx);
+                     plan.words, plan.hist, plan.kv, W, N, token_idx, d, pg);
   return hipGetLastError();
 }
 

@@ -265,8 +265,8 @@ def test_variant_and_layer_validation():
     ph = P(B=1, Hq=256, Hkv=32, D=128, T=4000, Tcap=40000, dtype=ksa.KSA_BF16)
     assert lib.ksa_paged_vote_select(ctypes.byref(ph), ctypes.byref(g), FAKE, FAKE, 512, 128, FAKE,
                                      null, FAKE, 1 << 34, null) == U
-    # paged sparse decode: per-head lists are not a paged kind; more blocks than the table holds
-    sel = ksa.Selection(ksa.KSA_SEL_HEAD_TOKENS, FAKE.value, 4)
+    # paged sparse decode: an unknown selection kind; more blocks than the table holds
+    sel = ksa.Selection(7, FAKE.value, 4)
     g2 = ksa.PagedKv(FAKE, FAKE, 256, 1000)
     assert lib.ksa_paged_sparse_decode(pp, ctypes.byref(g2), FAKE, FAKE, FAKE, ctypes.byref(sel),
                                        FAKE, null, FAKE, 1 << 30, null) == E

@@ -379,3 +379,52 @@ def test_paged_vote_of_chosen_heads(heads):
         kb = gathered(kp, table, b, T, Bs)
         lg = oracle.head_logits(np_bits(q[b:b + 1]), kb, T)[:, heads]
         check_votes(vts[b:b + 1, :T], row[None], lg, N, W)
+
+
+PER_HEAD_PAGED = [
+    dict(lens=[4000, 900, 300, 1], Hq=16, Hkv=4, D=128, dtype="bf16", N=512, W=128),
+    dict(lens=[2100, 1500], Hq=8, Hkv=2, D=64, dtype="f32", N=300, W=60),
+]
+
+
+@pytest.mark.parametrize("case", PER_HEAD_PAGED, ids=lambda c: "G%d-%s-%s" % (
+    c["Hq"] // c["Hkv"], c["dtype"], "_".join(map(str, c["lens"]))))
+def test_paged_per_head_sets_and_their_attention(case):
+    """Per-head sets on a paged cache: every head's own picks over its
+    sequence's history (oracle rule per sequence; a sequence no longer than
+    N keeps all its tokens, then -1), and attention over one list per query
+    head through the block table against the oracle."""
+    from test_gpu_variants import check_head_sets
+    c = dict(case)
+    lens, N, W, Bs = c.pop("lens"), c.pop("N"), c.pop("W"), 16
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=sum(lens) % 331, **c)
+    idx = ksa.ksa_paged_vote_select_per_head(q, kp, table, seq, N, W)
+    out, lse = ksa.ksa_paged_sparse_decode(q, kp, vp, table, seq, idx, ksa.KSA_SEL_HEAD_TOKENS)
+    torch.cuda.synchronize()
+    ids = idx.cpu().numpy()
+    for b, T in enumerate(lens):
+        kb, vb = gathered(kp, table, b, T, Bs), gathered(vp, table, b, T, Bs)
+        qb = np_bits(q[b:b + 1])
+        if T <= N:
+            row = ids[b][:, :T]
+            assert np.all(ids[b][:, T:] == -1)
+            assert np.all(row == np.arange(T)[None])
+        else:
+            row = ids[b]
+            check_head_sets(row[None], oracle.head_logits(qb, kb, T), N, W)
+        ro, rl = oracle.attend_head_tokens(qb, kb, vb, T, np.ascontiguousarray(row[None]))
+        check_attention(out[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), ro, rl)
+
+
+def test_paged_per_head_sets_equal_contiguous_bitwise():
+    T, Bs, N, W = 3000, 16, 512, 128
+    w, q, k, v, kp, vp, table, seq = paged_inputs([T] * 2, Bs, seed=97, Hq=16, Hkv=4, D=128,
+                                                  dtype="bf16")
+    pi = ksa.ksa_paged_vote_select_per_head(q, kp, table, seq, N, W)
+    ci = ksa.ksa_vote_select_per_head(q, k, T, N, W)
+    torch.cuda.synchronize()
+    assert torch.equal(pi, ci)
+    po, pl = ksa.ksa_paged_sparse_decode(q, kp, vp, table, seq, pi, ksa.KSA_SEL_HEAD_TOKENS)
+    co, cl = ksa.ksa_sparse_decode(q, k, v, T, ci, ksa.KSA_SEL_HEAD_TOKENS)
+    torch.cuda.synchronize()
+    assert torch.equal(po, co) and torch.equal(pl, cl)
