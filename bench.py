@@ -206,7 +206,7 @@ def timed(torch, stream, n, body):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(every (sequence, KV head) row is independent; DESIGN.md describes how it "
               "would shard).", file=sys.stderr)
         sys.exit(2)

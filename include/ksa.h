@@ -65,7 +65,7 @@ extern "C" {
 typedef enum {
   KSA_OK = 0,
   KSA_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or parameter is out of range */
-  KSA_ERR_UNSUPPORTED = 2,      /* valid, but outside what this build handles */
+  KSA_ERR_UNSUPPORTED = 2,      /* valid, but outside what this library handles */
   KSA_ERR_WORKSPACE_TOO_SMALL = 3,
   KSA_ERR_HIP = 4               /* a HIP launch failed */
 } ksa_status;
@@ -76,7 +76,7 @@ typedef enum { KSA_F32 = 0, KSA_BF16 = 1 } ksa_dtype;
  * decoded included (its K/V are appended before the call).  Every sequence of
  * the batch has the same T (the uniform-workload setting of the Kinetics news
  * page, section on the Qwen3-0.6B throughput gain).
- * Supported by this build: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8};
+ * Supported by this library: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8};
  * dtype fp32 or bf16; B*Hkv*T_cap*D < 2^40; B*Hkv <= 16384. */
 typedef struct {
   int32_t batch;        /* B >= 1 */

@@ -25,7 +25,7 @@ bool supported_shape(const ksa_problem& p) {
 }
 
 // Checks the fields every call uses; INVALID for impossible shapes,
-// UNSUPPORTED for valid ones outside this build.
+// UNSUPPORTED for valid ones outside this library.
 ksa_status check_problem(const ksa_problem* p, bool needs_block_size) {
   if (!p) return KSA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
@@ -140,7 +140,7 @@ const char* ksa_status_string(ksa_status status) {
   switch (status) {
     case KSA_OK: return "KSA_OK: success";
     case KSA_ERR_INVALID_ARGUMENT: return "KSA_ERR_INVALID_ARGUMENT: an argument is out of range";
-    case KSA_ERR_UNSUPPORTED: return "KSA_ERR_UNSUPPORTED: valid arguments outside what this build handles";
+    case KSA_ERR_UNSUPPORTED: return "KSA_ERR_UNSUPPORTED: valid arguments outside what this library handles";
     case KSA_ERR_WORKSPACE_TOO_SMALL: return "KSA_ERR_WORKSPACE_TOO_SMALL: workspace smaller than ksa_workspace_bytes()";
     case KSA_ERR_HIP: return "KSA_ERR_HIP: a HIP kernel launch failed";
     default: return "unknown ksa_status";
