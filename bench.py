@@ -482,6 +482,9 @@ def main():
         "dense": {"ms_per_step": round(ms_dense, 5), "value": round(B / (ms_dense * 1e-3), 1),
                   "gbps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)},
         "speedup_vs_dense": round(ms_dense / ms_step, 3),
+        # the step's bandwidth against what dense decode (a plain stream of K and V
+        # over the same caches) reaches on this machine
+        "step_frac_of_dense_gbps": round((step_bytes / ms_step) / (dense_bytes / ms_dense), 4),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "avg_launch_ms": round(ms_attn, 5),
