@@ -185,3 +185,86 @@ def test_random_dense_and_selection_layers(i):
         ro, rl = oracle.attend_dense(np_bits(q[b:b + 1]), gathered(kp, table, b, T, Bs),
                                      gathered(vp, table, b, T, Bs), T)
         check_attention(do[b:b + 1].cpu().numpy(), dl[b:b + 1].cpu().numpy(), ro, rl)
+
+
+def forced_rule_ok(ids, raw, keff, forced):
+    """ids [rows, keff] keep block `forced` of each row and, apart from it,
+    the top keff - 1 of the rest (near-tie rules)."""
+    assert np.all(np.diff(ids, axis=1) > 0)
+    assert np.all(np.any(ids == forced[:, None], axis=1))
+    if keff < 2 or keff == raw.shape[1]:
+        return
+    rest = raw.copy()
+    rest[np.arange(raw.shape[0]), forced] = raw.min() - 1.0
+    others = np.array([[j for j in row if j != f] for row, f in zip(ids, forced)])
+    check_block_selection(others, rest, keff - 1)
+
+
+@pytest.mark.parametrize("i", CASES, ids=cid)
+def test_random_selection_variants(i):
+    """MAX aggregation and the forced newest block (contiguous and paged) and
+    the vote of a random subset of heads (contiguous and paged) against the
+    oracle's rules."""
+    c = draw(i)
+    r = np.random.default_rng(7000 + i)
+    N, W, Bs, top_k = c["N"], c["W"], c["Bs"], c["top_k"]
+    w = small_workload(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"], dtype=c["dtype"], Bs=Bs,
+                       T=c["T"], Tcap=c["Tcap"], top_k=top_k, seed=700 + i)
+    q, k, v = gpu_inputs(w)
+    s = torch.zeros((w.B, w.Hkv, ksa.nblocks(w.cap, Bs), w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_block_summaries(k, s, w.T, Bs)
+    heads = sorted(r.choice(w.Hq, size=int(r.integers(1, w.Hq + 1)), replace=False).tolist())
+    mx, sc = ksa.ksa_select_topk_ex(q, s, w.T, Bs, top_k, aggregate=ksa.KSA_AGG_MAX,
+                                    want_scores=True)
+    fs = ksa.ksa_select_topk_ex(q, s, w.T, Bs, top_k, force_last_block=True)
+    fm = ksa.ksa_select_topk_ex(q, s, w.T, Bs, top_k, aggregate=ksa.KSA_AGG_MAX,
+                                force_last_block=True)
+    hidx, hv = ksa.ksa_vote_select_heads(q, k, w.T, N, W, heads, want_votes=True)
+    torch.cuda.synchronize()
+    rows = w.B * w.Hkv
+    qn, sn = np_bits(q), np_bits(s)
+    raw_max, scaled = oracle.group_scores(qn, sn, w.T, Bs, Tcap=w.cap, aggregate="max")
+    raw_sum, _ = oracle.group_scores(qn, sn, w.T, Bs, Tcap=w.cap)
+    raw_max, raw_sum = raw_max.reshape(rows, -1), raw_sum.reshape(rows, -1)
+    check_block_selection(mx.cpu().numpy().reshape(rows, -1), raw_max, top_k)
+    np.testing.assert_allclose(sc.cpu().numpy(), scaled, rtol=0,
+                               atol=1e-5 * max(1.0, float(np.abs(scaled).max())))
+    keff = min(top_k, w.NB)
+    last = np.full(rows, w.NB - 1)
+    forced_rule_ok(fs.cpu().numpy().reshape(rows, -1), raw_sum, keff, last)
+    forced_rule_ok(fm.cpu().numpy().reshape(rows, -1), raw_max, keff, last)
+    if w.T <= N:
+        assert np.array_equal(hidx.cpu().numpy(), np.broadcast_to(np.arange(w.T), hidx.shape))
+    else:
+        lg = oracle.head_logits(qn, np_bits(k), w.T)[:, heads]
+        check_votes(hv.cpu().numpy(), hidx.cpu().numpy(), lg, N, W)
+
+    lens = c["lens"]
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=800 + i, Hq=c["Hq"],
+                                                  Hkv=c["Hkv"], D=c["D"], dtype=c["dtype"])
+    s = torch.zeros((w.B, w.Hkv, table.shape[1], w.D), dtype=k.dtype, device=DEV)
+    ksa.ksa_paged_block_summaries(kp, s, table, seq)
+    pm = ksa.ksa_paged_select_topk_ex(q, s, table, seq, Bs, top_k, aggregate=ksa.KSA_AGG_MAX)
+    pf = ksa.ksa_paged_select_topk_ex(q, s, table, seq, Bs, top_k, force_last_block=True)
+    pidx, pv = ksa.ksa_paged_vote_select_heads(q, kp, table, seq, N, W, heads, want_votes=True)
+    torch.cuda.synchronize()
+    sn = np_bits(s)
+    pm, pf, pids, pvts = pm.cpu().numpy(), pf.cpu().numpy(), pidx.cpu().numpy(), pv.cpu().numpy()
+    for b, T in enumerate(lens):
+        nb = ksa.nblocks(T, Bs)
+        keff = min(top_k, nb)
+        qb = np_bits(q[b:b + 1])
+        rm, _ = oracle.group_scores(qb, sn[b:b + 1], T, Bs, Tcap=table.shape[1] * Bs,
+                                    aggregate="max")
+        rs, _ = oracle.group_scores(qb, sn[b:b + 1], T, Bs, Tcap=table.shape[1] * Bs)
+        rm, rs = rm.reshape(w.Hkv, -1), rs.reshape(w.Hkv, -1)
+        assert np.all(pm[b][:, keff:] == -1) and np.all(pf[b][:, keff:] == -1)
+        check_block_selection(np.ascontiguousarray(pm[b][:, :keff]), rm, top_k)
+        forced_rule_ok(np.ascontiguousarray(pf[b][:, :keff]), rs, keff, np.full(w.Hkv, nb - 1))
+        row = pids[b][pids[b] >= 0]
+        if T <= N:
+            assert row.tolist() == list(range(T))
+        else:
+            assert row.shape[0] == N
+            lg = oracle.head_logits(qb, gathered(kp, table, b, T, Bs), T)[:, heads]
+            check_votes(pvts[b:b + 1, :T], row[None], lg, N, W)
