@@ -507,9 +507,19 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
     for (int i = 0; i < NI; ++i) vr[i] = ld_kv(vbase + (int64_t)tv[i] * D);
   };
 
+  // VK: the key rows [G, vkstride] of the group's heads as one store range;
+  // lanes without a key (heads past G, tokens past the history) are dropped
+  const __amdgpu_buffer_rsrc_t krs =
+      store_range(VK ? (void*)(a.vkeys + ((int64_t)b * d.Hq + g * G) * a.vkstride) : nullptr,
+                  VK ? (uint32_t)(G * a.vkstride) * 4u : 0u);
+
   uint4 kb[NI], vb[NI];
   bool okb = false;
   if (my_n > 0) load(c0, kb, vb, okb);
+  // a store that writes nothing: the loop is entered with the same memory
+  // operations outstanding as every iteration leaves behind, so the waits
+  // for the next chunk's loads leave the previous chunk's key store in flight
+  if constexpr (VK) st16_range(krs, kDropOffset, make_uint4(0u, 0u, 0u, 0u));
   for (int j = 0; j < my_n; ++j) {
     uint4 kc[NI], vc[NI];
 #pragma unroll
@@ -527,19 +537,14 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
       // the selection layer: keys of head r's raw logits of tokens 4kg..4kg+3
       // (the vote scorer's arithmetic, so the same keys), 16 bytes at a time;
       // positions are token ids in a dense walk (kind 3: over every block in
-      // order)
-      if (r < G) {
-        const int t = (c0 + j * nw) * CH + 4 * kg;
-        uint32_t* kout = a.vkeys + ((int64_t)b * d.Hq + g * G + r) * a.vkstride;
-        if (t + 3 < a.vhist) {
-          st16(kout + t, make_uint4(order_key(S[0]), order_key(S[1]), order_key(S[2]),
-                                    order_key(S[3])));
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (t + jj < a.vhist) kout[t + jj] = order_key(S[jj]);
-        }
-      }
+      // order).  A group that straddles the end of the history is stored
+      // whole: its slots past the history lie in the row's padding to a
+      // multiple of 4, which nothing reads.
+      const int t = (c0 + j * nw) * CH + 4 * kg;
+      const uint32_t off =
+          (r < G && t < a.vhist) ? (uint32_t)(r * a.vkstride + t) * 4u : kDropOffset;
+      st16_range(krs, off,
+                 make_uint4(order_key(S[0]), order_key(S[1]), order_key(S[2]), order_key(S[3])));
     }
     const uint64_t vm = __ballot(okc);  // bit t (t < 16): chunk token t is attended
     float sv[4];

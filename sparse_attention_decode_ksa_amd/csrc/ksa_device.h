@@ -53,6 +53,21 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Stores through a buffer resource of `bytes` bytes at `base`: the hardware
+// drops every lane whose offset lies past the end, so a wave can issue one
+// store instruction whatever subset of its lanes has data (no branch, and a
+// fixed number of memory operations per loop iteration, which lets the
+// compiler wait for later loads without waiting for the store).
+constexpr uint32_t kDropOffset = 0x80000000u;  // past the end of any range made here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_range(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void st16_range(__amdgpu_buffer_rsrc_t rs, uint32_t off, const uint4& v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 d = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(d, rs, (int)off, 0, 0);
+}
+
 // ---------------------------------------------------------------- DPP
 // Lane permutations inside a 16-lane row (gfx9 DPP controls).
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
