@@ -447,7 +447,6 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
   static_assert(!VK || KIND == 2 || KIND == 3, "vote keys come from dense walks");
   constexpr int D = 128;
   constexpr int EPL = 8;
-  constexpr int LPT = 16;
   constexpr int SPW = 4;
   constexpr int NI = 4;
   constexpr int CH = 16;
