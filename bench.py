@@ -81,7 +81,8 @@ def parse():
                                                           "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv files "
                          "(workload run, then the --copy-probe run) into "
-                         "profiles/traffic_sparse_decode_<workload>.json")
+                         "profiles/traffic_<kernel>_<workload>.json (kernel: block_topk_decode "
+                         "for the fused path, else sparse_decode)")
     return ap.parse_args()
 
 
@@ -207,8 +208,8 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
-              "(every (sequence, KV head) row is independent; DESIGN.md describes how it "
-              "would shard).", file=sys.stderr)
+              "(every (sequence, KV head) row is independent, so batch or KV-head sharding "
+              "would need no communication; it is not built).", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()

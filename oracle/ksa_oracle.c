@@ -24,7 +24,7 @@
  *            and finally adds the most recent tokens; sparse layers attend the
  *            chosen set only, the set being shared by all heads of a GQA group.
  *
- * Readings taken where the pages are silent (each listed in the design doc):
+ * Readings taken where the pages are silent:
  *   summary = arithmetic mean of the block's keys, summed in fp64 in token
  *   order, divided by the block's token count in fp64 and stored rounded
  *   to nearest-even in the KV dtype; the group score of a block is the mean
