@@ -207,6 +207,25 @@ ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, cons
                                  int32_t refresh_last_block, int32_t* block_idx, float* out,
                                  float* lse, void* stream);
 
+/* ksa_block_topk_decode_varlen -- ksa_block_topk_decode on the contiguous
+ * cache with one length per sequence (the batches of unequal lengths a
+ * paged cache also serves, Kinetics news page on the uniform workload and
+ * Kinetics explainer, section 五): sequence b holds T_b = seq_lens[b] tokens
+ * (device [B] int32; not validated, clamped into [1, T] with T the problem's
+ * seq_len, which must be the longest length), so NB_b = ceil(T_b / Bs) and
+ * k_eff_b = min(top_k, NB_b).  For every (sequence, KV head) the refresh
+ * rewrites block (T_b - 1) / Bs, the ranking covers blocks [0, NB_b) and the
+ * attention covers the tokens below T_b of the chosen blocks.  block_idx
+ * [B, Hkv, min(top_k, NB)] (NB from T) holds each row's k_eff_b ascending
+ * ids, then -1.  With every T_b = T it is ksa_block_topk_decode bit for bit.
+ * seq_lens NULL or misaligned: KSA_ERR_INVALID_ARGUMENT.  Same layouts,
+ * limits and (no) workspace as ksa_block_topk_decode. */
+ksa_status ksa_block_topk_decode_varlen(const ksa_problem* problem, const int32_t* seq_lens,
+                                        const void* q, const void* k, const void* v,
+                                        void* summaries, int32_t top_k,
+                                        int32_t refresh_last_block, int32_t* block_idx,
+                                        float* out, float* lse, void* stream);
+
 /* ---------------------------------------------------------------------
  * Paged KV cache with one length per sequence (Kinetics explainer, section
  * 五: block top-k attention works with a paged cache, the attention blocks

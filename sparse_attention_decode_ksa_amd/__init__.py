@@ -8,8 +8,8 @@ library's HIP kernels; there is no CPU or PyTorch fallback, and a missing or
 unloadable library raises :class:`KsaLibraryError` on first use.
 
 Function names match the C entry points: ``ksa_block_summaries``,
-``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode``,
-``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
+``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode`` (and
+``ksa_block_topk_decode_varlen``, one length per sequence), ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
 ``ksa_paged_dense_decode``, ``ksa_paged_vote_select``, ``ksa_paged_sparse_decode``,
 ``ksa_paged_vote_layer_decode``, ``ksa_paged_select_topk_ex``,
@@ -46,8 +46,9 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_select_topk_ex", "ksa_vote_select_heads", "ksa_attention_recall",
             "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
             "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_paged_select_topk_ex",
-            "ksa_paged_vote_select_heads", "ksa_paged_vote_select_per_head", "ksa_workspace_bytes",
-            "ksa_status_string", "ksa_version")
+            "ksa_paged_vote_select_heads", "ksa_paged_vote_select_per_head",
+            "ksa_block_topk_decode_varlen", "ksa_workspace_bytes", "ksa_status_string",
+            "ksa_version")
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -133,13 +134,14 @@ def load_library(path: str = LIB_PATH):
                                                  P, SZ, P]
         lib.ksa_paged_vote_select_heads.argtypes = [PP, PG, P, P, I32, I32, P, I32, P, P, P, SZ, P]
         lib.ksa_paged_vote_select_per_head.argtypes = [PP, PG, P, P, I32, I32, P, P, SZ, P]
+        lib.ksa_block_topk_decode_varlen.argtypes = [PP, P, P, P, P, P, I32, I32, P, P, P, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
         lib.ksa_status_string.restype = ctypes.c_char_p
         lib.ksa_version.argtypes = []
         lib.ksa_version.restype = ctypes.c_char_p
-        for name in EXPORTED[:20]:
+        for name in EXPORTED[:-3]:  # every call but the three below returns a status
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib
@@ -325,6 +327,38 @@ def ksa_block_topk_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev(block_idx, "block_idx", torch.int32, (B, Hkv, keff)),
         _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
         _stream(stream)), "ksa_block_topk_decode")
+    return out, lse, block_idx
+
+
+def ksa_block_topk_decode_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                 summaries: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                                 top_k: int, max_len: Optional[int] = None,
+                                 refresh_last_block: bool = True, block_idx=None,
+                                 want_block_idx: bool = False, out=None, lse=None,
+                                 want_lse: bool = True, sm_scale: float = 0.0, stream=None):
+    """ksa_block_topk_decode with one length per sequence (seq_lens [B] int32
+    on the device; max_len, the longest, defaults to the cache capacity).
+    block_idx [B,Hkv,min(k,NB(max_len))] holds each row's ids, then -1."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, Tcap = k.shape[1], k.shape[2]
+    T = int(max_len) if max_len is not None else Tcap
+    prob = make_problem(q, k, T, block_size, sm_scale)
+    keff = min(top_k, nblocks(T, block_size))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if block_idx is None and want_block_idx:
+        block_idx = torch.empty((B, Hkv, keff), dtype=torch.int32, device=q.device)
+    _check(lib.ksa_block_topk_decode_varlen(
+        ctypes.byref(prob), _dev(seq_lens, "seq_lens", torch.int32, (B,)), _dev(q, "q", k.dtype),
+        _dev(k, "k"), _dev(v, "v", k.dtype, k.shape),
+        _dev(summaries, "summaries", k.dtype, (B, Hkv, nblocks(Tcap, block_size), D)),
+        int(top_k), 1 if refresh_last_block else 0,
+        _dev(block_idx, "block_idx", torch.int32, (B, Hkv, keff)),
+        _dev(out, "out", torch.float32, (B, Hq, D)), _dev(lse, "lse", torch.float32, (B, Hq)),
+        _stream(stream)), "ksa_block_topk_decode_varlen")
     return out, lse, block_idx
 
 

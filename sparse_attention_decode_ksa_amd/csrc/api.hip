@@ -261,10 +261,12 @@ ksa_status ksa_dense_decode(const ksa_problem* problem, const void* q, const voi
                                    (hipStream_t)stream));
 }
 
-ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, const void* k,
-                                 const void* v, void* summaries, int32_t top_k,
-                                 int32_t refresh_last_block, int32_t* block_idx, float* out,
-                                 float* lse, void* stream) {
+namespace {
+// ksa_block_topk_decode with an optional length per sequence
+ksa_status block_topk_decode(const ksa_problem* problem, const int32_t* seq_lens, const void* q,
+                             const void* k, const void* v, void* summaries, int32_t top_k,
+                             int32_t refresh_last_block, int32_t* block_idx, float* out,
+                             float* lse, void* stream) {
   ksa_status st = check_problem(problem, true);
   if (st != KSA_OK) return st;
   const Dims d = make_dims(*problem);
@@ -277,7 +279,27 @@ ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, cons
   if ((int64_t)keff * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
   if (refresh_last_block && d.Bs > kStepMaxBs) return KSA_ERR_UNSUPPORTED;
   return from_hip(launch_block_topk_decode(d, q, k, v, summaries, keff, refresh_last_block, block_idx,
-                                           out, lse, (hipStream_t)stream));
+                                           out, lse, (hipStream_t)stream, nullptr, seq_lens));
+}
+}  // namespace
+
+ksa_status ksa_block_topk_decode(const ksa_problem* problem, const void* q, const void* k,
+                                 const void* v, void* summaries, int32_t top_k,
+                                 int32_t refresh_last_block, int32_t* block_idx, float* out,
+                                 float* lse, void* stream) {
+  return block_topk_decode(problem, nullptr, q, k, v, summaries, top_k, refresh_last_block,
+                           block_idx, out, lse, stream);
+}
+
+ksa_status ksa_block_topk_decode_varlen(const ksa_problem* problem, const int32_t* seq_lens,
+                                        const void* q, const void* k, const void* v,
+                                        void* summaries, int32_t top_k,
+                                        int32_t refresh_last_block, int32_t* block_idx,
+                                        float* out, float* lse, void* stream) {
+  if (!problem) return KSA_ERR_INVALID_ARGUMENT;
+  if (!seq_lens || !aligned4(seq_lens)) return KSA_ERR_INVALID_ARGUMENT;
+  return block_topk_decode(problem, seq_lens, q, k, v, summaries, top_k, refresh_last_block,
+                           block_idx, out, lse, stream);
 }
 
 ksa_status ksa_paged_block_summaries(const ksa_problem* problem, const ksa_paged_kv* paged,

@@ -63,7 +63,8 @@ constexpr int ref_stage_slots() {
 }
 
 // NW waves per workgroup (4 or 8).  PAGED: K and V are page pools (the
-// attention's kind 3) and every row has its own length from seq_lens.
+// attention's kind 3) and every row has its own length from seq_lens.  A
+// contiguous cache may also carry seq_lens (lengths up to the call's T).
 template <typename T, int D, int G, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_topk_decode_kernel(
     StepArgs s) {
@@ -99,6 +100,11 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
     keff = min(s.keff, a.d.NB);
     a.ltot = keff * d.Bs;
     ptab = a.table + (int64_t)b * a.tstride;
+  } else if (a.seq_lens) {  // contiguous cache, one length per sequence (at most T)
+    a.d.T = min(max(a.seq_lens[b], 1), d.T);
+    a.d.NB = (a.d.T + d.Bs - 1) / d.Bs;
+    keff = min(s.keff, a.d.NB);
+    a.ltot = keff * d.Bs;
   }
   const int Trow = a.d.T;
   const int NB = a.d.NB;
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
     if constexpr (PAGED) s_pg[rank] = ptab[j];
     if (gidx) gidx[rank] = j;
   });
-  if constexpr (PAGED) {  // ids past this row's k_eff
+  if (PAGED || a.seq_lens) {  // ids past this row's k_eff
     if (gidx)
       for (int i = keff + tid; i < s.keff; i += kStepThreads) gidx[i] = -1;
   }
@@ -320,7 +326,7 @@ hipError_t launch_dtype(const StepArgs& s, hipStream_t stream) {
 hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k, const void* v,
                                     void* summaries, int keff, int refresh, int32_t* block_idx,
                                     float* out, float* lse, hipStream_t stream,
-                                    const PagedKv* paged) {
+                                    const PagedKv* paged, const int32_t* seq_lens) {
   // keff is the id stride; a paged call's rows select at most max_blocks
   const int kplan = keff < d.NBcap ? keff : d.NBcap;
   const int ch = chunk_tokens(d);
@@ -338,6 +344,7 @@ hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k,
     s.a.tstride = paged->max_blocks;
     return launch_dtype<true>(s, stream);
   }
+  s.a.seq_lens = seq_lens;
   return launch_dtype<false>(s, stream);
 }
 

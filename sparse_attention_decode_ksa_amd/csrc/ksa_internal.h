@@ -107,7 +107,8 @@ constexpr int kStepMaxBs = 64;        // largest block size the step refreshes
 hipError_t launch_block_topk_decode(const Dims& d, const void* q, const void* k, const void* v,
                                     void* summaries, int keff, int refresh, int32_t* block_idx,
                                     float* out, float* lse, hipStream_t stream,
-                                    const PagedKv* paged = nullptr);
+                                    const PagedKv* paged = nullptr,
+                                    const int32_t* seq_lens = nullptr);
 
 // Vote-union selection.
 struct VotePlan {

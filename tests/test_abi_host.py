@@ -145,6 +145,31 @@ def test_fused_step_validation():
     assert call(P(Bs=65), refresh=1) == U
 
 
+def test_fused_step_varlen_validation():
+    """ksa_block_topk_decode_varlen: a lengths pointer is required and 4-byte
+    aligned; everything else is checked as for ksa_block_topk_decode."""
+    lib = ksa.load_library()
+    null = None
+    E = ksa.KSA_ERR_INVALID_ARGUMENT
+    U = ksa.KSA_ERR_UNSUPPORTED
+
+    def call(p, lens=FAKE, top_k=4, refresh=1, q=FAKE, out=FAKE):
+        return lib.ksa_block_topk_decode_varlen(ctypes.byref(p) if p is not None else None, lens,
+                                                q, FAKE, FAKE, FAKE, top_k, refresh, null, out,
+                                                null, null)
+
+    p = P()
+    assert call(None) == E
+    assert call(p, lens=null) == E
+    assert call(p, lens=ctypes.c_void_p(0x10002)) == E   # seq_lens must be 4-byte aligned
+    assert call(p, top_k=0) == E
+    assert call(p, q=null) == E
+    assert call(p, out=null) == E
+    assert call(P(D=96)) == U
+    assert call(P(T=4097 * 16, Tcap=4097 * 16)) == U
+    assert call(P(Bs=65), refresh=1) == U
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 64)

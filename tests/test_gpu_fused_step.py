@@ -133,6 +133,77 @@ def test_fused_step_integer_ties_are_bit_exact(G, Bs, dtype):
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), ro, rl)
 
 
+VARLEN_CASES = [
+    dict(lens=[1000, 17, 1, 512], Bs=16, Hq=4, Hkv=2, D=64, dtype="bf16", top_k=8),
+    dict(lens=[3000, 2048, 777], Bs=16, Hq=8, Hkv=1, D=128, dtype="bf16", top_k=64),   # MFMA G = 8
+    dict(lens=[4099, 64, 2000], Bs=32, Hq=16, Hkv=4, D=128, dtype="bf16", top_k=20),   # MFMA G = 4
+    dict(lens=[517, 200, 7], Bs=7, Hq=2, Hkv=2, D=64, dtype="bf16", top_k=30),         # Bs not 2^n
+    dict(lens=[1025, 1024, 33], Bs=16, Hq=4, Hkv=2, D=128, dtype="f32", top_k=12),     # T-1 opens a block
+    dict(lens=[200, 150], Bs=1, Hq=4, Hkv=4, D=128, dtype="f32", top_k=17),            # one-token blocks
+]
+
+
+def varlen_inputs(lens, Bs, seed, **kw):
+    """A contiguous cache holding sequences of the given lengths, and summaries
+    as they stood before each sequence's newest token (its newest block holds
+    noise, so the refresh does real work)."""
+    T = max(lens)
+    w = small_workload(B=len(lens), T=T, Tcap=T + 2 * Bs, Bs=Bs, seed=seed, **kw)
+    q, k, v = gpu_inputs(w)
+    s = torch.zeros((w.B, w.Hkv, ksa.nblocks(w.cap, Bs), w.D), dtype=k.dtype, device=DEV)
+    for b, Tb in enumerate(lens):
+        ksa.ksa_block_summaries(k[b:b + 1], s[b:b + 1], Tb, Bs)
+        s[b, :, (Tb - 1) // Bs] = (torch.randn(s[b, :, 0].shape, device=DEV) * 3).to(s.dtype)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return w, q, k, v, s, seq
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "%s-G%d-D%d-Bs%d-k%d-%s" % (
+    c["dtype"], c["Hq"] // c["Hkv"], c["D"], c["Bs"], c["top_k"], "_".join(map(str, c["lens"]))))
+def test_fused_step_varlen_matches_oracle_per_sequence(case):
+    """One length per sequence on a contiguous cache: every sequence's newest
+    block is refreshed, its own blocks ranked and its own tokens attended
+    (oracle per sequence on its own length); ids past a row's k_eff are -1."""
+    c = dict(case)
+    lens, Bs, top_k = c.pop("lens"), c.pop("Bs"), c.pop("top_k")
+    w, q, k, v, s, seq = varlen_inputs(lens, Bs, seed=sum(lens) % 499, **c)
+    out, lse, idx = ksa.ksa_block_topk_decode_varlen(q, k, v, s, seq, Bs, top_k, max_len=w.T,
+                                                     want_block_idx=True)
+    torch.cuda.synchronize()
+    got_s, ids = np_bits(s), idx.cpu().numpy()
+    assert ids.shape[2] == min(top_k, ksa.nblocks(w.T, Bs))
+    for b, T in enumerate(lens):
+        nb = ksa.nblocks(T, Bs)
+        keff = min(top_k, nb)
+        qb, kb, vb = np_bits(q[b:b + 1]), np_bits(k[b:b + 1]), np_bits(v[b:b + 1])
+        sb = oracle.block_summaries(kb, T, Bs)
+        np.testing.assert_array_equal(got_s[b:b + 1, :, :nb], sb[:, :, :nb])
+        assert np.all(ids[b, :, keff:] == -1)
+        raw, _ = oracle.group_scores(qb, sb, T, Bs, Tcap=w.cap)
+        ib = np.ascontiguousarray(ids[b:b + 1, :, :keff])
+        check_block_selection(ib.reshape(w.Hkv, -1), raw.reshape(w.Hkv, -1), top_k)
+        ro, rl = oracle.attend_blocks(qb, kb, vb, T, Bs, ib)
+        check_attention(out[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("G,Bs,dtype,T", [(2, 16, "bf16", 5000), (4, 32, "bf16", 4097),
+                                           (8, 16, "bf16", 3001), (1, 16, "f32", 999)])
+def test_fused_step_varlen_at_one_length_equals_the_step_bitwise(G, Bs, dtype, T):
+    """Every length equal to T: the varlen call is the plain step bit for bit."""
+    w = small_workload(B=5, Hq=2 * G, Hkv=2, D=128 if dtype == "bf16" else 64, T=T, Bs=Bs,
+                       dtype=dtype, top_k=24, seed=T)
+    q, k, v = gpu_inputs(w)
+    s1 = stale_summaries(k, w)
+    s2 = s1.clone()
+    o1, l1, i1 = ksa.ksa_block_topk_decode(q, k, v, s1, w.T, w.Bs, w.top_k, want_block_idx=True)
+    seq = torch.full((w.B,), T, dtype=torch.int32, device=DEV)
+    o2, l2, i2 = ksa.ksa_block_topk_decode_varlen(q, k, v, s2, seq, w.Bs, w.top_k, max_len=T,
+                                                  want_block_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(i1, i2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_fused_step_optional_outputs():
     """block_idx and lse are optional; leaving them out changes nothing else."""
     w = small_workload(B=4, Hq=8, Hkv=4, D=128, T=5000, Bs=16, dtype="bf16", top_k=40, seed=8)

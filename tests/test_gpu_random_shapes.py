@@ -94,6 +94,33 @@ def test_random_block_step(i):
 
 
 @pytest.mark.parametrize("i", CASES, ids=cid)
+def test_random_block_step_varlen(i):
+    """The fused step with one length per sequence on a contiguous cache
+    matches the oracle on each sequence's own length."""
+    from test_gpu_fused_step import varlen_inputs
+    c = draw(i)
+    lens, Bs, top_k = c["lens"], c["Bs"], c["top_k"]
+    w, q, k, v, s, seq = varlen_inputs(lens, Bs, seed=900 + i, Hq=c["Hq"], Hkv=c["Hkv"],
+                                       D=c["D"], dtype=c["dtype"])
+    out, lse, idx = ksa.ksa_block_topk_decode_varlen(q, k, v, s, seq, Bs, top_k, max_len=w.T,
+                                                     want_block_idx=True)
+    torch.cuda.synchronize()
+    got_s, ids = np_bits(s), idx.cpu().numpy()
+    for b, T in enumerate(lens):
+        nb = ksa.nblocks(T, Bs)
+        keff = min(top_k, nb)
+        qb, kb, vb = np_bits(q[b:b + 1]), np_bits(k[b:b + 1]), np_bits(v[b:b + 1])
+        sb = oracle.block_summaries(kb, T, Bs)
+        np.testing.assert_array_equal(got_s[b:b + 1, :, :nb], sb[:, :, :nb])
+        assert np.all(ids[b, :, keff:] == -1)
+        raw, _ = oracle.group_scores(qb, sb, T, Bs, Tcap=w.cap)
+        ib = np.ascontiguousarray(ids[b:b + 1, :, :keff])
+        check_block_selection(ib.reshape(w.Hkv, -1), raw.reshape(w.Hkv, -1), top_k)
+        ro, rl = oracle.attend_blocks(qb, kb, vb, T, Bs, ib)
+        check_attention(out[b:b + 1].cpu().numpy(), lse[b:b + 1].cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("i", CASES, ids=cid)
 def test_random_vote_paths(i):
     """The shared vote-union set, its token attention and the per-head sets
     match the oracle on a contiguous cache; the paged vote and its attention
