@@ -33,6 +33,7 @@ Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--path fused|calls]
     python bench.py --paged uniform|ragged [--workload c2|c3|c5]  # the step on a paged cache
+    python bench.py --varlen [--workload c2|c3|c5]   # contiguous cache, one length per sequence
     python bench.py --schedule [--schedule-layers 36 --select-every 8]  # LessIsMore layers (c4)
     python bench.py --copy-probe      # a plain 1 GiB copy, to calibrate HBM counters
 """
@@ -69,6 +70,9 @@ def parse():
     ap.add_argument("--paged", default="none", choices=["none", "uniform", "ragged"],
                     help="the step on a paged cache (random page order; for c4 the vote "
                          "path): every sequence at T, or lengths drawn in [T/2, T]")
+    ap.add_argument("--varlen", action="store_true",
+                    help="the one-launch step on the contiguous cache with one length per "
+                         "sequence, drawn in [T/2, T] (ksa_block_topk_decode_varlen)")
     ap.add_argument("--schedule", action="store_true",
                     help="c4 shape: a LessIsMore layer schedule (2 dense layers, then a "
                          "selection layer every --select-every layers, sparse layers between), "
@@ -214,7 +218,7 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
-    if args.paged != "none":
+    if args.paged != "none" or args.varlen:
         paged_main(args)
         return
     if args.schedule:
@@ -507,7 +511,11 @@ def paged_main(args):
     """The block top-k decode step on a paged cache: every layer's K and V are
     stored as page pools in a seeded random page order (to_paged), each
     sequence has its own length (all T, or drawn in [T/2, T]), and the step
-    is one ksa_paged_block_topk_decode launch; dense is ksa_paged_dense_decode."""
+    is one ksa_paged_block_topk_decode launch; dense is ksa_paged_dense_decode.
+    With --varlen the cache stays contiguous and the step is one
+    ksa_block_topk_decode_varlen launch (lengths drawn in [T/2, T]); dense is
+    then ksa_dense_decode with every sequence at T, reported for reference
+    only (it reads more than the ragged batch holds, so no speedup is given)."""
     import numpy as np
     import torch
 
@@ -521,13 +529,16 @@ def paged_main(args):
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
     if w.plant == "tokens":
+        if args.varlen and args.paged == "none":
+            raise SystemExit("--varlen times the block top-k step (c2, c3, c5)")
         return paged_vote_main(args, w)
     B, Hq, Hkv, D, T, Bs, K = w.B, w.Hq, w.Hkv, w.D, w.T, w.Bs, w.top_k
     elt = 2 if w.dtype == "bf16" else 4
     rows = B * Hkv
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed * 7 + 1)
-    if args.paged == "ragged":
+    varlen = args.varlen and args.paged == "none"
+    if args.paged == "ragged" or varlen:
         lens = torch.randint(T // 2, T + 1, (B,), generator=gen).tolist()
     else:
         lens = [T] * B
@@ -538,29 +549,43 @@ def paged_main(args):
     L = []
     for l in range(layers):
         x = make_inputs(w, device=dev, seed=w.seed * 1000 + l)
-        kp, vp, table = to_paged(x["k"], x["v"], Bs, seed=w.seed * 1000 + l + 1)
-        del x["k"], x["v"]
-        x.update(kp=kp, vp=vp, table=table,
-                 seq=torch.tensor(lens, dtype=torch.int32, device=dev),
-                 s=torch.empty((B, Hkv, table.shape[1], D), dtype=kp.dtype, device=dev),
+        if varlen:
+            x.update(s=torch.empty((B, Hkv, (w.cap + Bs - 1) // Bs, D), dtype=x["k"].dtype,
+                                   device=dev))
+            ksa.ksa_block_summaries(x["k"], x["s"], T, Bs)
+        else:
+            kp, vp, table = to_paged(x["k"], x["v"], Bs, seed=w.seed * 1000 + l + 1)
+            del x["k"], x["v"]
+            x.update(kp=kp, vp=vp, table=table,
+                     s=torch.empty((B, Hkv, table.shape[1], D), dtype=kp.dtype, device=dev))
+        x.update(seq=torch.tensor(lens, dtype=torch.int32, device=dev),
                  out=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
                  lse=torch.empty((B, Hq), dtype=torch.float32, device=dev),
                  idx=torch.empty((B, Hkv, K), dtype=torch.int32, device=dev),
                  dout=torch.empty((B, Hq, D), dtype=torch.float32, device=dev),
                  dlse=torch.empty((B, Hq), dtype=torch.float32, device=dev))
-        ksa.ksa_paged_block_summaries(x["kp"], x["s"], x["table"], x["seq"], max_len=T)
+        if not varlen:
+            ksa.ksa_paged_block_summaries(x["kp"], x["s"], x["table"], x["seq"], max_len=T)
         L.append(x)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
-    prob = ksa.Problem(B, Hq, Hkv, D, T, L[0]["table"].shape[1] * Bs, Bs,
+    prob = ksa.Problem(B, Hq, Hkv, D, T, w.cap if varlen else L[0]["table"].shape[1] * Bs, Bs,
                        ksa.KSA_BF16 if elt == 2 else ksa.KSA_F32, 0.0)
     pp = ctypes.byref(prob)
     stream = torch.cuda.Stream(device=dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     V = lambda t: ctypes.c_void_p(t.data_ptr())
-    wsd = ksa.new_workspace(ksa.ksa_workspace_bytes(prob, ksa.KSA_OP_PAGED_DENSE, 0), dev)
-    for x in L:
+    wsd = ksa.new_workspace(ksa.ksa_workspace_bytes(
+        prob, ksa.KSA_OP_DENSE if varlen else ksa.KSA_OP_PAGED_DENSE, 0), dev)
+    for x in L if varlen else []:
+        x["step"] = (lib.ksa_block_topk_decode_varlen,
+                     (pp, V(x["seq"]), V(x["q"]), V(x["k"]), V(x["v"]), V(x["s"]), K, 1,
+                      V(x["idx"]), V(x["out"]), V(x["lse"]), sp))
+        x["dense"] = (lib.ksa_dense_decode,
+                      (pp, V(x["q"]), V(x["k"]), V(x["v"]), V(x["dout"]), V(x["dlse"]), V(wsd),
+                       wsd.numel(), sp))
+    for x in [] if varlen else L:
         x["pg"] = ksa.PagedKv(V(x["table"]).value, V(x["seq"]).value, x["table"].shape[1],
                               x["kp"].shape[0])
         pg = ctypes.byref(x["pg"])
@@ -602,26 +627,33 @@ def paged_main(args):
                   + last_tok * D * elt + rows * D * elt      # newest block refreshed
                   + sel_tok * D * elt * 2                    # selected K and V
                   + 2 * q_bytes + out_bytes + int(np.minimum(K, nb).sum()) * Hkv * 8 + B * 4)
-    dense_bytes = int(tl.sum()) * Hkv * D * elt * 2 + q_bytes + out_bytes
+    dense_bytes = (B * T if varlen else int(tl.sum())) * Hkv * D * elt * 2 + q_bytes + out_bytes
     achieved = step_bytes / (ms_step * 1e-3) / 1e9
     cfg = {"workload": "%s: %s" % (w.name, w.description), "batch": B, "q_heads": Hq,
            "kv_heads": Hkv, "head_dim": D, "context": T, "layers_cycled": layers,
            "block_size": Bs, "top_k_blocks": K, "paged": args.paged,
-           "seq_len_mean": round(float(tl.mean()), 1), "seq_len_min": int(tl.min()),
-           "pages_per_layer": int(L[0]["kp"].shape[0])}
+           "seq_len_mean": round(float(tl.mean()), 1), "seq_len_min": int(tl.min())}
+    if varlen:
+        cfg["varlen"] = True
+    else:
+        cfg["pages_per_layer"] = int(L[0]["kp"].shape[0])
     line = {
         "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
         "value": round(B / (ms_step * 1e-3), 1), "unit": "seqs*steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if elt == 2 else "f32",
-        "data": "synthetic (seeded N(0,1) K/V/q with planted structure), paged in a random page order",
+        "data": "synthetic (seeded N(0,1) K/V/q with planted structure)" +
+                ("" if varlen else ", paged in a random page order"),
         "config": cfg, "step_bytes": step_bytes,
         "dense": {"ms_per_step": round(ms_dense, 5), "value": round(B / (ms_dense * 1e-3), 1),
-                  "gbps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)},
-        "speedup_vs_dense": round(ms_dense / ms_step, 3),
-        "roofline": {"kernel": "ksa_paged_block_topk_decode (refresh + score + top-k + attention, "
-                               "one launch)", "bound": "hbm", "achieved": round(achieved, 1),
+                  "gbps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1),
+                  **({"note": "every sequence at T (reference only)"} if varlen else {})},
+        "speedup_vs_dense": None if varlen else round(ms_dense / ms_step, 3),
+        "roofline": {"kernel": ("ksa_block_topk_decode_varlen" if varlen else
+                                "ksa_paged_block_topk_decode") +
+                               " (refresh + score + top-k + attention, one launch)",
+                     "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None, "avg_launch_ms": round(ms_step, 5),
                      "bytes_per_launch": step_bytes},
