@@ -25,6 +25,8 @@ prepared ctypes arguments):
      (for the fused path the step is that one call: region 1)
   3. dense decode steps                           -> dense, speedup_vs_dense
   4. K steps replayed from HIP graphs             -> graph_ms_per_step
+  5. K steps with an event between consecutive steps -> step_ms_percentiles
+     (p10 / p50 / p90 of single steps)
 Each layer's step is also captured into a HIP graph (the C calls launched on
 the capturing stream); replay is checked to reproduce the eager step's
 outputs bit for bit.  For a step of one kernel, graph replay costs about 2 us
@@ -208,6 +210,22 @@ def timed(torch, stream, n, body):
     return a.elapsed_time(b) / n
 
 
+def per_step(torch, stream, n, body):
+    """Time n calls of body(i) with an event between consecutive calls;
+    returns the p10 / p50 / p90 of the per-call times in ms (the events add a
+    little to each call, so region timing stays the headline)."""
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        body(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
+    pick = lambda f: round(t[min(n - 1, int(f * n))], 5)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -353,6 +371,7 @@ def main():
         for i in range(args.warmup):
             step(i)
         ms_step = timed(torch, stream, args.steps, step)             # region 1
+        pct = per_step(torch, stream, args.steps, step)               # region 5
 
         # graphs: one step per layer, and one whole cycle over the layers
         ref = [(x["out"].clone(), x["lse"].clone(), x["idx"].clone()) for x in L]
@@ -472,6 +491,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms_percentiles": pct,
         "graph_ms_per_step": round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
