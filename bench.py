@@ -627,6 +627,7 @@ def paged_main(args):
         for i in range(args.warmup):
             step(i)
         ms_step = timed(torch, stream, args.steps, step)
+        pct = per_step(torch, stream, args.steps, step)
         dense_only(0)
         ms_dense = timed(torch, stream, args.dense_steps, dense_only)
 
@@ -661,6 +662,7 @@ def paged_main(args):
         "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
         "value": round(B / (ms_step * 1e-3), 1), "unit": "seqs*steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "step_ms_percentiles": pct,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if elt == 2 else "f32",
         "data": "synthetic (seeded N(0,1) K/V/q with planted structure)" +
@@ -759,6 +761,7 @@ def paged_vote_main(args, w):
         for i in range(args.warmup):
             sel_step(i)
         ms_step = timed(torch, stream, args.steps, sel_step)
+        pct = per_step(torch, stream, args.steps, sel_step)
         ms_sparse = timed(torch, stream, args.steps, run("attn"))
         run("layer")(0)
         ms_layer = timed(torch, stream, max(3, args.dense_steps), run("layer"))
@@ -782,6 +785,7 @@ def paged_vote_main(args, w):
         "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
         "value": round(B / (ms_step * 1e-3), 1), "unit": "seqs*steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "step_ms_percentiles": pct,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if elt == 2 else "f32",
         "data": "synthetic (seeded N(0,1) K/V/q with planted tokens), paged in a random page order",
