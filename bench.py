@@ -1,25 +1,34 @@
 """Benchmark of one decode step of sparse attention on one MI355X.
 
-Block top-k workloads (c2 default, c3, c5): one step = refresh the summary of
+Block top-k workloads (c5 default, c2, c3): one step = refresh the summary of
 the block holding the newest token, score and select the top-k blocks of every
 (sequence, KV head), and attend the selected blocks with every query head.
 --path fused (default) times that step as one ksa_block_topk_decode launch;
 --path calls times it as ksa_block_summaries + ksa_select_topk +
-ksa_sparse_decode.  The other path is timed beside it and its outputs are
-checked to be bitwise the same.
+ksa_sparse_decode.  The other path is run beside it and its outputs are
+checked to be the same.
 Vote-union workload (c4): one step = the selection layer's vote (all heads
 score every history token, votes are pooled, the recency window appended) and
 the attention over the shared set; the sparse-layer step (attention over a
 set chosen earlier) is reported beside it.
+
+The headline is --workload (c5: one GPU's share of the largest setting on the
+pages, 34 GB of KV per layer); the workloads in --extra (c2, c3, c4) are timed
+afterwards in the same process, each once the previous one's caches are
+freed, and summarised under `configs`.
 
 Steps cycle over several independent KV caches ("layers", distinct seeds) so
 that a step's bytes were not touched by the steps just before it and the
 256 MB Infinity Cache does not serve them.  Inputs are resident in HBM before
 timing starts.  Dense decode of the same shape is timed the same way.
 
-Timed regions (each bracketed by torch.cuda.synchronize() and HIP events on
-the stream the kernels run on; every step is the plain C calls, launched from
-prepared ctypes arguments):
+Order per workload: inputs; correctness checks (untimed: every layer's step,
+the other path on the same inputs, HIP-graph capture and replay checked bit
+for bit against the eager step); warm-up of at least --warmup steps and
+--warm-seconds of wall time (the chip's clocks settle within ~15 ms of
+sustained load); then the timed regions, each bracketed by
+torch.cuda.synchronize() and HIP events on the stream the kernels run on
+(every step is the plain C calls, launched from prepared ctypes arguments):
   1. K whole steps back to back                   -> value, ms_per_step
   2. K launches of the dominant call alone        -> roofline.achieved
      (for the fused path the step is that one call: region 1)
@@ -27,10 +36,9 @@ prepared ctypes arguments):
   4. K steps replayed from HIP graphs             -> graph_ms_per_step
   5. K steps with an event between consecutive steps -> step_ms_percentiles
      (p10 / p50 / p90 of single steps)
-Each layer's step is also captured into a HIP graph (the C calls launched on
-the capturing stream); replay is checked to reproduce the eager step's
-outputs bit for bit.  For a step of one kernel, graph replay costs about 2 us
-more per step than plain launches on MI355X, so region 1 is the headline.
+Then the oracle leg on the first sequences of layer 0 (copied from the GPU):
+the step's outputs checked against the fp64 oracle (`parity`) and the oracle
+timed on the host cores (`cpu_baseline`, headline only).
 Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload c2|c3|c4|c5] [--path fused|calls]
@@ -38,11 +46,13 @@ Prints ONE JSON line.
     python bench.py --varlen [--workload c2|c3|c5]   # contiguous cache, one length per sequence
     python bench.py --schedule [--schedule-layers 36 --select-every 8]  # LessIsMore layers (c4)
     python bench.py --copy-probe      # a plain 1 GiB copy, to calibrate HBM counters
+    python bench.py --trace-summary TRACE_DIR OUT_MD   # rocprofv3 kernel-trace durations
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import gc
 import hashlib
 import json
 import math
@@ -62,11 +72,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"],
+                    help="the headline workload (default c5, the largest that fits one GPU)")
+    ap.add_argument("--extra", default="c2,c3,c4",
+                    help="workloads also timed in the same process, each after the previous "
+                         "one's caches are freed (reported under `configs`; '' for none)")
+    ap.add_argument("--extra-steps", type=int, default=100)
     ap.add_argument("--path", default="fused", choices=["fused", "calls"],
                     help="block top-k step as one fused launch or as the three separate calls")
     ap.add_argument("--layers", type=int, default=0, help="KV caches cycled over (0: auto)")
     ap.add_argument("--dense-steps", type=int, default=20)
+    ap.add_argument("--warm-seconds", type=float, default=0.25,
+                    help="least wall time of untimed warm-up before each timed workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     ap.add_argument("--paged", default="none", choices=["none", "uniform", "ragged"],
@@ -83,6 +100,9 @@ def parse():
     ap.add_argument("--select-every", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of 1 GiB (counter calibration)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
+                    help="summarise the rocprofv3 --kernel-trace csv files under TRACE_DIR "
+                         "(durations per kernel) into the markdown file OUT_MD")
     ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                           "COPY_WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter_collection.csv files "
@@ -113,8 +133,9 @@ def kernel_source_hash(kernel):
                         for n in KERNEL_SOURCES[kernel]])
 
 
-def traffic_kernel(args):
-    return "block_topk_decode" if args.path == "fused" and args.workload != "c4" else "sparse_decode"
+def traffic_kernel(args, workload=None):
+    workload = workload or args.workload
+    return "block_topk_decode" if args.path == "fused" and workload != "c4" else "sparse_decode"
 
 
 def counter_summary(args):
@@ -165,6 +186,35 @@ def counter_summary(args):
     print(json.dumps(out))
 
 
+def trace_summary(args):
+    """Durations per kernel from rocprofv3 --kernel-trace csv files (every
+    *kernel_trace.csv under the directory), as a markdown table: launches,
+    median, mean, min and max in microseconds, largest total time first."""
+    import csv
+    import glob
+    import statistics
+
+    tdir, out_md = args.trace_summary
+    by = {}
+    for p in sorted(glob.glob(os.path.join(tdir, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"].replace("ksa::(anonymous namespace)::", "")
+                name = name.split("(")[0] if name.startswith("void ") else name
+                name = name[5:] if name.startswith("void ") else name
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                by.setdefault(name, []).append(us)
+    rows = sorted(by.items(), key=lambda kv: -sum(kv[1]))
+    lines = ["| kernel | launches | median us | mean us | min us | max us |",
+             "|---|---|---|---|---|---|"]
+    for name, v in rows:
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (
+            name, len(v), statistics.median(v), sum(v) / len(v), min(v), max(v)))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_probe():
     import torch
     n = 1 << 30
@@ -198,6 +248,22 @@ class Runner:
             raise RuntimeError("%s failed: %s" % (fn.__name__, self.ksa.ksa_status_string(st)))
 
 
+def warm(torch, body, n, seconds):
+    """n untimed calls of body(i), then more until `seconds` of wall time have
+    passed: under a sudden sustained load the MI355X's clocks take some 15 ms
+    to settle (the first ~30 c5 steps ran up to 28 % slower than the rest in
+    a kernel trace), so a short warm-up would time the transient."""
+    for i in range(n):
+        body(i)
+    torch.cuda.synchronize()
+    t0, i = time.time(), n
+    while time.time() - t0 < seconds:
+        for _ in range(4):
+            body(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def timed(torch, stream, n, body):
     """Time n calls of body(i) between two events; returns ms per call."""
     torch.cuda.synchronize()
@@ -226,42 +292,114 @@ def per_step(torch, stream, n, body):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path "
-              "(every (sequence, KV head) row is independent, so batch or KV-head sharding "
-              "would need no communication; it is not built).", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_probe:
-        copy_probe()
-        return
-    if args.paged != "none" or args.varlen:
-        paged_main(args)
-        return
-    if args.schedule:
-        schedule_main(args)
-        return
-    if args.counter_summary:
-        counter_summary(args)
-        return
+def environment():
+    """What the line was measured on: software versions, the GPU, the host CPU."""
+    import platform
 
+    import torch
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"torch": torch.__version__, "hip": torch.version.hip,
+            "gpu": torch.cuda.get_device_name(0), "cpu_model": cpu,
+            "host_threads": len(os.sched_getaffinity(0)), "python": platform.python_version()}
+
+
+def input_checksum(torch, x):
+    """sha256 (16 hex digits) of q and of a strided sample of 65536 elements
+    of K and V: the same seed gives the same inputs."""
+    h = hashlib.sha256()
+    for name in ("q", "k", "v"):
+        t = x[name].reshape(-1)
+        step = max(1, t.numel() // 65536)
+        s = t[::step].contiguous() if name != "q" else t.contiguous()
+        s = s.view(torch.int16) if s.dtype == torch.bfloat16 else s.view(torch.int32)
+        h.update(s.cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
+REL_TIE = 1e-5  # near-tie gap, relative to the row's largest |relevance|
+
+
+def block_parity(oracle, np, w, gpu_idx, gpu_out, gpu_lse, gpu_summ, qn, kn, vn):
+    """The GPU's step on the first sequences against the fp64 oracle on the
+    same bytes: summaries bitwise, selected blocks as sets (a difference is a
+    near tie when the two blocks' relevances lie within REL_TIE of the row's
+    largest |relevance|, else a mismatch), and the attention over the GPU's
+    own selection (max abs error of out and lse)."""
+    T, Bs, K = w.T, w.Bs, w.top_k
+    NB = (T + Bs - 1) // Bs
+    summ = oracle.block_summaries(kn, T, Bs)
+    summ_exact = bool(np.array_equal(gpu_summ[:, :, :NB], summ[:, :, :NB]))
+    raw, _ = oracle.group_scores(qn, summ, T, Bs, Tcap=w.cap)
+    ref = oracle.topk(raw, K)
+    rows = raw.reshape(-1, NB)
+    gi, ri = gpu_idx.reshape(rows.shape[0], -1), ref.reshape(rows.shape[0], -1)
+    near, bad = 0, 0
+    for r in range(rows.shape[0]):
+        a, b = set(gi[r].tolist()), set(ri[r].tolist())
+        if a == b:
+            continue
+        tol = REL_TIE * np.abs(rows[r]).max()
+        for j in a - b:
+            if any(abs(rows[r, j] - rows[r, o]) < tol for o in b - a):
+                near += 1
+            else:
+                bad += 1
+    ro, rl = oracle.attend_blocks(qn, kn, vn, T, Bs, gpu_idx)
+    return {"summaries_bitexact": summ_exact, "rows": int(rows.shape[0]),
+            "near_tie_swaps": near, "mismatches": bad,
+            "max_abs_err_out": float(np.abs(gpu_out - ro).max()),
+            "max_abs_err_lse": float(np.abs(gpu_lse - rl).max())}
+
+
+def vote_parity(oracle, np, w, gpu_tok, gpu_votes, gpu_out, gpu_lse, qn, kn, vn):
+    """The vote-union step on the first sequences against the oracle: the
+    GPU's token set must be the integer rule applied to the GPU's own votes;
+    vote counts and sets are compared with the oracle's (they may differ
+    only through per-head near ties at a head's threshold), and the attention
+    over the GPU's set is compared with the oracle's."""
+    T, N, W = w.T, w.token_budget, w.recent_window
+    ref_tok, ref_votes = oracle.vote_select(qn, kn, T, N, W)
+    rule = oracle.set_from_votes(gpu_votes.astype(np.int32), N, W)
+    diff = sum(len(set(gpu_tok[b].tolist()) ^ set(ref_tok[b].tolist())) // 2
+               for b in range(gpu_tok.shape[0]))
+    ro, rl = oracle.attend_tokens(qn, kn, vn, T, gpu_tok)
+    return {"sequences": int(gpu_tok.shape[0]),
+            "set_is_rule_on_gpu_votes": bool(np.array_equal(rule, gpu_tok)),
+            "vote_count_diffs": int(np.abs(gpu_votes.astype(np.int64) - ref_votes).sum()),
+            "set_diffs_vs_oracle": int(diff),
+            "max_abs_err_out": float(np.abs(gpu_out - ro).max()),
+            "max_abs_err_lse": float(np.abs(gpu_lse - rl).max())}
+
+
+def run_workload(args, name, headline):
+    """One workload: layer caches resident in HBM, the correctness checks
+    (untimed; they also bring the GPU to its working clocks), then the timed
+    regions.  Returns the result dict (the headline's is the printed line)."""
     import numpy as np
     import torch
 
     import sparse_attention_decode_ksa_amd as ksa
     from sparse_attention_decode_ksa_amd.inputs import WORKLOADS, as_numpy_bits, make_inputs
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     lib = ksa.load_library()
     R = Runner(lib, ksa)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[name]
     vote = w.plant == "tokens"
     B, Hq, Hkv, D, T = w.B, w.Hq, w.Hkv, w.D, w.T
     elt = 2 if w.dtype == "bf16" else 4
     rows = B * Hkv
+    steps = args.steps if headline else args.extra_steps
+    warmup = args.warmup if headline else max(args.warmup, 5)
     if vote:
         N, W = w.token_budget, w.recent_window
         n_sel = min(N, T)
@@ -295,6 +433,7 @@ def main():
         L.append(x)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
+    checksum = input_checksum(torch, L[0])
 
     # ---------------------------------------------------------------- prepared C calls
     prob = ksa.Problem(B, Hq, Hkv, D, T, w.cap, Bs, ksa.KSA_BF16 if elt == 2 else ksa.KSA_F32, 0.0)
@@ -366,60 +505,68 @@ def main():
     def dense_only(i):
         R.run(L[i % layers]["calls"]["dense"])
 
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        return g
+
     torch.cuda.synchronize()
+    ms_graph = ms_attn = ms_select = ms_other = None
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
-        ms_step = timed(torch, stream, args.steps, step)             # region 1
-        pct = per_step(torch, stream, args.steps, step)               # region 5
-
-        # graphs: one step per layer, and one whole cycle over the layers
+        # -------------------------------------------------------- checks (untimed)
+        for l in range(layers):
+            step(l)
+        torch.cuda.synchronize()
         ref = [(x["out"].clone(), x["lse"].clone(), x["idx"].clone()) for x in L]
-
-        def capture(fn):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fn()
-            return g
-
         if other_step is not None:
-            # the other path on the same inputs gives bitwise the same step
-            for l, x in enumerate(L):
+            # the other path on the same inputs: block ids bitwise, outputs bitwise
+            # unless the separate attention is planned with another split (which
+            # reorders its fp32 merge)
+            for l in range(layers):
                 other_step(l)
             torch.cuda.synchronize()
-            # (block ids bitwise; outputs bitwise unless the separate attention is
-            # planned with another split, which reorders its fp32 merge)
-            for l, x in enumerate(L):
+            for x in L:
                 assert torch.equal(x["idx2"], x["idx"]), "fused step and separate calls select differently"
                 assert float((x["out2"] - x["out"]).abs().max()) <= 1e-5 \
                     and float((x["lse2"] - x["lse"]).abs().max()) <= 1e-5, \
                     "fused step and separate calls differ"
-        g_step = [capture(lambda l=l: step(l)) for l in range(layers)]
-        g_cycle = capture(lambda: [step(l) for l in range(layers)])
-        for x in L:
-            x["out"].zero_(), x["lse"].zero_(), x["idx"].zero_()
-        g_cycle.replay()
-        torch.cuda.synchronize()
-        for l, x in enumerate(L):
-            assert torch.equal(x["out"], ref[l][0]) and torch.equal(x["lse"], ref[l][1]) \
-                and torch.equal(x["idx"], ref[l][2]), "graph replay differs from the eager step"
+        if headline:
+            # graphs: one step per layer, and one whole cycle over the layers; a
+            # replay reproduces the eager step bit for bit
+            g_step = [capture(lambda l=l: step(l)) for l in range(layers)]
+            g_cycle = capture(lambda: [step(l) for l in range(layers)])
+            for x in L:
+                x["out"].zero_(), x["lse"].zero_(), x["idx"].zero_()
+            g_cycle.replay()
+            torch.cuda.synchronize()
+            for l, x in enumerate(L):
+                assert torch.equal(x["out"], ref[l][0]) and torch.equal(x["lse"], ref[l][1]) \
+                    and torch.equal(x["idx"], ref[l][2]), "graph replay differs from the eager step"
 
-        full, rest = divmod(args.steps, layers)
+        # -------------------------------------------------------- timed regions
+        warm(torch, step, warmup, args.warm_seconds)
+        ms_step = timed(torch, stream, steps, step)             # region 1
+        pct = per_step(torch, stream, steps, step)               # region 5
+        if headline:
+            full, rest = divmod(steps, layers)
 
-        def graph_steps(i):
-            if i < full:
-                g_cycle.replay()
-            else:
-                g_step[i - full].replay()
+            def graph_steps(i):
+                if i < full:
+                    g_cycle.replay()
+                else:
+                    g_step[i - full].replay()
 
-        ms_graph = timed(torch, stream, full + rest, graph_steps) * (full + rest) / args.steps  # 4
-        ms_attn = ms_step if fused_path else timed(torch, stream, args.steps, attn_only)      # 2
-        ms_select = timed(torch, stream, args.steps, select_only)
-        ms_other = None
-        if other_step is not None:
-            ms_other = timed(torch, stream, args.steps, other_step)
-        dense_only(0)
+            ms_graph = timed(torch, stream, full + rest, graph_steps) * (full + rest) / steps  # 4
+            ms_select = timed(torch, stream, steps, select_only)
+            if other_step is not None:
+                ms_other = timed(torch, stream, steps, other_step)
+        ms_attn = ms_step if fused_path else timed(torch, stream, steps, attn_only)     # 2
+        warm(torch, dense_only, 1, args.warm_seconds)
         ms_dense = timed(torch, stream, args.dense_steps, dense_only)  # region 3
+        for l in range(layers):  # layer caches back to the timed path's outputs
+            step(l)
+        torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- algorithmic bytes
     q_bytes = B * Hq * D * elt
@@ -437,7 +584,7 @@ def main():
     achieved = dom_bytes / (ms_attn * 1e-3) / 1e9
 
     traffic = None
-    tk = traffic_kernel(args)
+    tk = traffic_kernel(args, name)
     tr_path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (tk, w.name))
     if os.path.exists(tr_path):
         with open(tr_path) as f:
@@ -445,37 +592,54 @@ def main():
         if tr.get("source_hash") == kernel_source_hash(tk):
             traffic = tr.get("bytes_per_launch")
 
-    # ---------------------------------------------------------------- CPU baseline (oracle)
-    cpu = None
+    # ---------------------------------------------------------------- oracle leg (CPU baseline + parity)
+    cpu = parity = None
     if not args.no_cpu_baseline:
         import oracle
         x = L[0]
-        n_seq = B if not vote else min(B, 4)
+        n_seq = min(B, 8 if headline else 2) if not vote else min(B, 4 if headline else 2)
         sl = slice(0, n_seq)
         qn, kn, vn = as_numpy_bits(x["q"][sl]), as_numpy_bits(x["k"][sl]), as_numpy_bits(x["v"][sl])
-        if not vote:
-            summ = oracle.block_summaries(kn, T, Bs)  # prefill, untimed
-        reps, tcpu = 0, 0.0
-        while tcpu < args.cpu_seconds and reps < 50:
-            c0 = time.time()
-            if vote:
-                tok, _ = oracle.vote_select(qn, kn, T, N, W)
-                oracle.attend_tokens(qn, kn, vn, T, tok)
-            else:
-                oracle.block_summaries(kn, T, Bs, first_block=last_block, num_blocks=1, out=summ)
-                raw, _ = oracle.group_scores(qn, summ, T, Bs, Tcap=w.cap)
-                oracle.attend_blocks(qn, kn, vn, T, Bs, oracle.topk(raw, K))
-            tcpu += time.time() - c0
-            reps += 1
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-        cpu = {"value": round(n_seq * reps / tcpu, 2), "unit": "seqs*steps/s", "cores": threads,
-               "kind": "oracle",
-               "sample": "%d full steps of %d of the %d sequences of %s (fp64 C oracle, OpenMP), "
-                         "inputs copied from the GPU" % (reps, n_seq, B, w.name)}
+        g_out = x["out"][sl].cpu().numpy().astype(np.float64)
+        g_lse = x["lse"][sl].cpu().numpy().astype(np.float64)
+        if vote:
+            # the timed vote writes no vote counts: one more untimed call with them
+            votes = torch.empty((B, T), dtype=torch.uint8, device=dev)
+            tok2 = torch.empty_like(x["idx"])
+            R.run((lib.ksa_vote_select, (pp, V(x["q"]), V(x["k"]), N, W, V(tok2), V(votes),
+                                         V(wsel), wsel.numel(), sp)))
+            torch.cuda.synchronize()
+            assert torch.equal(tok2, x["idx"]), "vote select is not repeatable"
+            parity = vote_parity(oracle, np, w, x["idx"][sl].cpu().numpy(),
+                                 votes[sl].cpu().numpy(), g_out, g_lse, qn, kn, vn)
+        else:
+            parity = block_parity(oracle, np, w, x["idx"][sl].cpu().numpy(), g_out, g_lse,
+                                  as_numpy_bits(x["s"][sl]), qn, kn, vn)
+        if headline:
+            if not vote:
+                summ = oracle.block_summaries(kn, T, Bs)  # prefill, untimed
+            reps, tcpu = 0, 0.0
+            while tcpu < args.cpu_seconds and reps < 50:
+                c0 = time.time()
+                if vote:
+                    tok, _ = oracle.vote_select(qn, kn, T, N, W)
+                    oracle.attend_tokens(qn, kn, vn, T, tok)
+                else:
+                    oracle.block_summaries(kn, T, Bs, first_block=last_block, num_blocks=1, out=summ)
+                    raw, _ = oracle.group_scores(qn, summ, T, Bs, Tcap=w.cap)
+                    oracle.attend_blocks(qn, kn, vn, T, Bs, oracle.topk(raw, K))
+                tcpu += time.time() - c0
+                reps += 1
+            threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+            cpu = {"value": round(n_seq * reps / tcpu, 2), "unit": "seqs*steps/s", "cores": threads,
+                   "kind": "oracle", "cpu_model": environment()["cpu_model"],
+                   "sample": "%d full steps of %d of the %d sequences of %s (fp64 C oracle, OpenMP), "
+                             "inputs copied from the GPU" % (reps, n_seq, B, w.name)}
 
     value = B / (ms_step * 1e-3)
     cfg = {"workload": "%s: %s" % (w.name, w.description), "batch": B, "q_heads": Hq,
-           "kv_heads": Hkv, "head_dim": D, "context": T, "layers_cycled": layers}
+           "kv_heads": Hkv, "head_dim": D, "context": T, "layers_cycled": layers,
+           "input_sha256_16": checksum}
     if vote:
         cfg.update(token_budget=N, recent_window=W)
         dom = "ksa_sparse_decode (shared token set)"
@@ -483,16 +647,23 @@ def main():
         cfg.update(block_size=Bs, top_k_blocks=K, path=args.path)
         dom = ("ksa_block_topk_decode (refresh + score + top-k + attention, one launch)"
                if fused_path else "ksa_sparse_decode (selected blocks, split-K online softmax)")
+    if vote:
+        # the sparse layer (attention over a set chosen earlier) against 0.6 x T / N
+        target = 0.6 * T / n_sel
+        speedup = ms_dense / ms_attn
+    else:
+        target = 0.6 * T / (keff * Bs)
+        speedup = ms_dense / ms_step
     line = {
         "metric": "sparse decode seqs*steps/s per layer, with achieved HBM GB/s (% of peak) vs dense",
         "value": round(value, 1),
         "unit": "seqs*steps/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "step_ms_percentiles": pct,
-        "graph_ms_per_step": round(ms_graph, 5),
+        "graph_ms_per_step": None if ms_graph is None else round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -502,11 +673,14 @@ def main():
         "step_bytes": step_bytes,
         "step_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "select": {"ms_eager": round(ms_select, 5),
+        "select": None if ms_select is None else
+                  {"ms_eager": round(ms_select, 5),
                    "gbps": round(select_bytes / (ms_select * 1e-3) / 1e9, 1)},
         "dense": {"ms_per_step": round(ms_dense, 5), "value": round(B / (ms_dense * 1e-3), 1),
                   "gbps": round(dense_bytes / (ms_dense * 1e-3) / 1e9, 1)},
         "speedup_vs_dense": round(ms_dense / ms_step, 3),
+        "speedup_target": {"value": round(target, 3), "measured": round(speedup, 3),
+                           "on": "sparse layer" if vote else "step", "met": speedup >= target},
         # the step's bandwidth against what dense decode (a plain stream of K and V
         # over the same caches) reaches on this machine
         "step_frac_of_dense_gbps": round((step_bytes / ms_step) / (dense_bytes / ms_dense), 4),
@@ -515,15 +689,70 @@ def main():
                      "traffic": traffic, "avg_launch_ms": round(ms_attn, 5),
                      "bytes_per_launch": dom_bytes},
         "cpu_baseline": cpu,
+        "parity": parity,
         "input_gen_s": round(gen_s, 2),
     }
-    if other_step is not None:
+    if ms_other is not None:
         line["other_path"] = {"path": "calls" if fused_path else "fused",
                               "ms_per_step": round(ms_other, 5),
                               "speedup_vs_dense": round(ms_dense / ms_other, 3)}
     if vote:
         line["sparse_layer_step"] = {"ms": round(ms_attn, 5), "value": round(B / (ms_attn * 1e-3), 1),
+                                     "gbps": round(attn_bytes / (ms_attn * 1e-3) / 1e9, 1),
+                                     "frac_of_peak": round(attn_bytes / (ms_attn * 1e-3) / 1e9
+                                                           / HBM_PEAK_GBPS, 4),
                                      "speedup_vs_dense": round(ms_dense / ms_attn, 3)}
+    return line
+
+
+def compact(line):
+    """The per-config summary kept in the headline's `configs`."""
+    keep = ("value", "ms_per_step", "step_ms_percentiles", "step_gbps", "step_frac_of_peak",
+            "speedup_vs_dense", "speedup_target", "step_frac_of_dense_gbps", "parity",
+            "sparse_layer_step", "steps", "warmup")
+    out = {k: line[k] for k in keep if k in line}
+    out["workload"] = line["config"]["workload"]
+    out["dense_ms"] = line["dense"]["ms_per_step"]
+    out["roofline"] = {k: line["roofline"][k] for k in ("kernel", "achieved", "frac", "traffic",
+                                                         "avg_launch_ms", "bytes_per_launch")}
+    out["input_sha256_16"] = line["config"]["input_sha256_16"]
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(every (sequence, KV head) row is independent, so batch or KV-head sharding "
+              "would need no communication; it is not built).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.paged != "none" or args.varlen:
+        paged_main(args)
+        return
+    if args.schedule:
+        schedule_main(args)
+        return
+    if args.counter_summary:
+        counter_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
+        return
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    line = run_workload(args, args.workload, headline=True)
+    extra = [c for c in args.extra.split(",") if c and c != args.workload]
+    if extra:
+        line["configs"] = {}
+        for c in extra:
+            gc.collect()  # the previous workload's caches go back to the allocator
+            torch.cuda.empty_cache()
+            line["configs"][c] = compact(run_workload(args, c, headline=False))
+    line["env"] = environment()
     print(json.dumps(line), flush=True)
 
 
@@ -624,11 +853,10 @@ def paged_main(args):
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
+        warm(torch, step, args.warmup, args.warm_seconds)
         ms_step = timed(torch, stream, args.steps, step)
         pct = per_step(torch, stream, args.steps, step)
-        dense_only(0)
+        warm(torch, dense_only, 1, args.warm_seconds)
         ms_dense = timed(torch, stream, args.dense_steps, dense_only)
 
     # algorithmic bytes of one step, from each row's length and its selected blocks
@@ -758,14 +986,13 @@ def paged_vote_main(args, w):
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            sel_step(i)
+        warm(torch, sel_step, args.warmup, args.warm_seconds)
         ms_step = timed(torch, stream, args.steps, sel_step)
         pct = per_step(torch, stream, args.steps, sel_step)
         ms_sparse = timed(torch, stream, args.steps, run("attn"))
-        run("layer")(0)
+        warm(torch, run("layer"), 1, args.warm_seconds)
         ms_layer = timed(torch, stream, max(3, args.dense_steps), run("layer"))
-        run("dense")(0)
+        warm(torch, run("dense"), 1, args.warm_seconds)
         ms_dense = timed(torch, stream, args.dense_steps, run("dense"))
     tl = np.array(lens)
     hist = np.where(tl > N, tl - W, 0)
@@ -880,11 +1107,10 @@ def schedule_main(args):
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        for i in range(max(1, args.warmup // 4)):
-            model_step(i)
+        warm(torch, model_step, max(1, args.warmup // 4), args.warm_seconds)
         steps = max(2, args.steps // 10)
         ms_model = timed(torch, stream, steps, model_step)
-        dense_step(0)
+        warm(torch, dense_step, 1, args.warm_seconds)
         ms_dense = timed(torch, stream, max(2, args.dense_steps // 4), dense_step)
     per_layer = ms_model / nL
     cfg = {"workload": "c4 shape, LessIsMore schedule: %d layers, 2 dense, a selection layer every "

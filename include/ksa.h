@@ -240,8 +240,10 @@ ksa_status ksa_block_topk_decode_varlen(const ksa_problem* problem, const int32_
  * In the problem struct, seq_len is the longest T_b (it sizes launches and
  * workspaces) and max_seq_len must equal max_blocks * Bs.  The table and the
  * lengths are device data and are not validated: a page id >= num_pages for
- * a block < NB_b is undefined behaviour; lengths are clamped into
- * [1, max_blocks * Bs].  num_pages * Hkv * Bs must stay below 2^31. */
+ * a block < NB_b is undefined behaviour; every kernel clamps a length into
+ * [1, T] with T the problem's seq_len, since launches, workspaces and
+ * outputs (votes [B, T], token_idx, block_scores) are sized from T.
+ * num_pages * Hkv * Bs must stay below 2^31. */
 typedef struct {
   const int32_t* block_table; /* device [B, max_blocks] int32 */
   const int32_t* seq_lens;    /* device [B] int32 */

@@ -29,8 +29,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# KSA_LIB selects another build of the same library (variant builds for tuning)
-LIB_PATH = os.environ.get("KSA_LIB", os.path.join(_HERE, "libksa.so"))
+# the in-tree build (python -m sparse_attention_decode_ksa_amd.build)
+LIB_PATH = os.path.join(_HERE, "libksa.so")
 
 KSA_OK, KSA_ERR_INVALID_ARGUMENT, KSA_ERR_UNSUPPORTED, KSA_ERR_WORKSPACE_TOO_SMALL, KSA_ERR_HIP = range(5)
 KSA_F32, KSA_BF16 = 0, 1

@@ -2,9 +2,6 @@
 // The per-row bodies (numerics, lane layout, pipelining) are in
 // ksa_attention.h; this file holds the kernels that give each workgroup one
 // (row, split) pair, the fixed-order split merge, and plan_attention.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "ksa_attention.h"
@@ -53,7 +50,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_d
   const int b = row / a0.d.Hkv;
   const int Bs = a0.d.Bs;
   AttnArgs a = a0;
-  const int Tb = min(max(a0.seq_lens[b], 1), a0.tstride * Bs);
+  const int Tb = seq_len_of(a0.seq_lens, b, a0.d.T);
   const int nb = (Tb + Bs - 1) / Bs;
   a.d.T = Tb;
   a.ltot = nb * Bs;
@@ -93,7 +90,7 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_l
   const int b = row / a0.d.Hkv;
   const int Bs = a0.d.Bs;
   AttnArgs a = a0;
-  const int Tb = min(max(a0.seq_lens[b], 1), a0.tstride * Bs);
+  const int Tb = seq_len_of(a0.seq_lens, b, a0.d.T);
   a.d.T = Tb;
   const int nchunks = (a.ltot + CH - 1) / CH;
   const int c_begin = split * a.cps;
@@ -227,15 +224,13 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   int64_t cps = (chunks + splits - 1) / splits;
   int nw = 1;
   while (nw < kMaxWaves && (int64_t)nw * 2 * kMinChunksPerWave <= cps) nw *= 2;
-  // Tuning override "waves,splits" for launch-shape sweeps (read per call).
-  if (const char* env = getenv("KSA_ATTN_PLAN")) {
-    int enw = 0, esp = 0;
-    if (sscanf(env, "%d,%d", &enw, &esp) == 2 && enw >= 1 && enw <= kMaxWaves && esp >= 1) {
-      nw = enw;
-      splits = esp;
-      cps = (chunks + splits - 1) / splits;
-    }
-  }
+#if defined(KSA_PLAN_WAVES) && defined(KSA_PLAN_SPLITS)
+  // a fixed launch shape, for variant builds that sweep shapes
+  static_assert(KSA_PLAN_WAVES >= 1 && KSA_PLAN_WAVES <= kMaxWaves && KSA_PLAN_SPLITS >= 1, "plan");
+  nw = KSA_PLAN_WAVES;
+  splits = KSA_PLAN_SPLITS;
+  cps = (chunks + splits - 1) / splits;
+#endif
   // a workgroup's index slice must fit the LDS stage
   int64_t cap = INT64_MAX;
   if (kind == 1 || kind == 4 || kind == 5 || kind == 6) cap = kIdxStage / ch;

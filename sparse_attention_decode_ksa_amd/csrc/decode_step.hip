@@ -27,6 +27,7 @@
 // and selections are bitwise those of ksa_block_summaries + ksa_select_topk;
 // the attention equals ksa_sparse_decode's up to the fp32 order of the wave
 // merge (bitwise when both run one 8-wave workgroup per row).
+#include <atomic>
 #include <type_traits>
 
 #include "ksa_attention.h"
@@ -95,13 +96,13 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   int keff = s.keff;
   const int32_t* ptab = nullptr;
   if constexpr (PAGED) {
-    a.d.T = min(max(a.seq_lens[b], 1), a.tstride * d.Bs);
+    a.d.T = seq_len_of(a.seq_lens, b, d.T);
     a.d.NB = (a.d.T + d.Bs - 1) / d.Bs;
     keff = min(s.keff, a.d.NB);
     a.ltot = keff * d.Bs;
     ptab = a.table + (int64_t)b * a.tstride;
   } else if (a.seq_lens) {  // contiguous cache, one length per sequence (at most T)
-    a.d.T = min(max(a.seq_lens[b], 1), d.T);
+    a.d.T = seq_len_of(a.seq_lens, b, d.T);
     a.d.NB = (a.d.T + d.Bs - 1) / d.Bs;
     keff = min(s.keff, a.d.NB);
     a.ltot = keff * d.Bs;
@@ -274,25 +275,37 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
     attn_row_valu<T, D, G, KIND>(a, row, 0, s_idx, s_pg, 0, false, qraw);
 }
 
+// Eight-wave workgroups of the step kernel that the device holds at once
+// (resident per CU times CUs), found once per kernel and device.
+constexpr int kMaxDevices = 64;
+template <typename T, int D, int G, bool PAGED>
+int eight_wave_capacity(int dev) {
+  static std::atomic<int> cache[kMaxDevices];  // 0: not yet known
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  int cap = cached ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (cap > 0) return cap;
+  int n = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_topk_decode_kernel<T, D, G, 8, PAGED>,
+                                                   512, 0) != hipSuccess || n < 1)
+    n = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  cap = n * cus;
+  if (cached) cache[dev].store(cap, std::memory_order_relaxed);
+  return cap;
+}
+
 template <typename T, int D, int G, bool PAGED>
 hipError_t launch_g(const StepArgs& s, int rows, hipStream_t stream) {
   // Eight waves per row unless the rows outnumber the workgroups of eight
   // waves that fit on the chip at once: then four, so that more rows are in
   // flight and one row's top-k is covered by the others' streaming.
-  // eight-wave workgroups per CU: a property of the kernel, found once
-  static const int resident8 = [] {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, block_topk_decode_kernel<T, D, G, 8, PAGED>,
-                                                     512, 0) != hipSuccess)
-      n = 1;
-    return n > 0 ? n : 1;
-  }();
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   const dim3 grid(rows);
-  if ((int64_t)rows > (int64_t)resident8 * cus)
+  if (rows > eight_wave_capacity<T, D, G, PAGED>(dev))
     hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 4, PAGED>), grid, dim3(256), 0, stream, s);
   else
     hipLaunchKernelGGL((block_topk_decode_kernel<T, D, G, 8, PAGED>), grid, dim3(512), 0, stream, s);

@@ -68,6 +68,13 @@ __device__ __forceinline__ void st16_range(__amdgpu_buffer_rsrc_t rs, uint32_t o
   __builtin_amdgcn_raw_buffer_store_b128(d, rs, (int)off, 0, 0);
 }
 
+// A sequence's own length read from a device length array, clamped into
+// [1, T] with T the call's seq_len (the longest length: launches, workspaces
+// and outputs are sized from it, so no length may exceed it).
+__device__ __forceinline__ int seq_len_of(const int32_t* seq_lens, int b, int T) {
+  return min(max(seq_lens[b], 1), T);
+}
+
 // ---------------------------------------------------------------- DPP
 // Lane permutations inside a 16-lane row (gfx9 DPP controls).
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]

@@ -48,7 +48,7 @@ constexpr int kTopkThreads = 256;  // one workgroup per row; also the histogram 
 // key rows keep the stride d.NB, the longest row's).
 __device__ __forceinline__ int row_blocks(const Dims& d, const int32_t* seq_lens, int b) {
   if (!seq_lens) return d.NB;
-  const int Tb = min(max(seq_lens[b], 1), d.NBcap * d.Bs);
+  const int Tb = seq_len_of(seq_lens, b, d.T);
   return (Tb + d.Bs - 1) / d.Bs;
 }
 

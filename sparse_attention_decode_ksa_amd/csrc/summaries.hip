@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void paged_block_summaries_kernel(
   if (rowid >= rows) return;
   const int64_t bg = rowid / num_blocks;
   const int b = (int)(bg / d.Hkv), g = (int)(bg - (int64_t)b * d.Hkv);
-  const int Tb = min(max(seq_lens[b], 1), tstride * d.Bs);
+  const int Tb = seq_len_of(seq_lens, b, d.T);
   const int j = first_block < 0 ? (Tb - 1) / d.Bs : first_block + (int)(rowid % num_blocks);
   const int t0 = j * d.Bs;
   if (t0 >= Tb) return;

@@ -77,7 +77,7 @@ struct VotePaging {
 // The history length of sequence b (0: no vote for it).
 __device__ __forceinline__ int vote_hist(const VotePaging& pg, const Dims& d, int b, int hist) {
   if (!pg.seq_lens) return hist;
-  const int Tb = min(max(pg.seq_lens[b], 1), pg.tstride * d.Bs);
+  const int Tb = seq_len_of(pg.seq_lens, b, d.T);
   return Tb > pg.N ? Tb - pg.W : 0;
 }
 
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
   int32_t* out = token_idx + (int64_t)b * n_out;
   const int64_t vstride = (int64_t)((hist + 31) / 32) * 32;  // votes8 row stride (longest history)
   if (pg.seq_lens) {  // this sequence's own length (T is then the longest)
-    const int Tb = min(max(pg.seq_lens[b], 1), pg.tstride * d.Bs);
+    const int Tb = seq_len_of(pg.seq_lens, b, d.T);
     if (Tb <= N) {  // no vote: the whole sequence, then -1
       for (int i = tid; i < n_out; i += kSetThreads) out[i] = i < Tb ? i : -1;
       if (votes)
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kSetThreads) void vote_tally_set_kernel(
   const int b = blockIdx.x;
   int32_t* out = token_idx + (int64_t)b * n_out;
   if (pg.seq_lens) {  // this sequence's own length (T is then the longest)
-    const int Tb = min(max(pg.seq_lens[b], 1), pg.tstride * d.Bs);
+    const int Tb = seq_len_of(pg.seq_lens, b, d.T);
     if (Tb <= N) {  // no vote: the whole sequence, then -1
       for (int i = tid; i < n_out; i += kSetThreads) out[i] = i < Tb ? i : -1;
       if (votes)
@@ -963,7 +963,7 @@ __global__ __launch_bounds__(kHeadSetThreads) void head_set_kernel(
   const uint32_t* br = bits + hr * words;
   int32_t* out = token_idx + hr * n_out;
   if (pg.seq_lens) {
-    const int Tb = min(max(pg.seq_lens[hr / d.Hq], 1), pg.tstride * d.Bs);
+    const int Tb = seq_len_of(pg.seq_lens, (int)(hr / d.Hq), d.T);
     if (Tb <= pg.N) {
       for (int i = tid; i < n_out; i += kHeadSetThreads) out[i] = i < Tb ? i : -1;
       return;
@@ -1001,7 +1001,7 @@ __global__ void head_all_kernel(int T, int rows, int32_t* __restrict__ token_idx
        i += (int64_t)gridDim.x * blockDim.x) {
     const int col = (int)(i % T);
     int lim = T;
-    if (pg.seq_lens) lim = min(max(pg.seq_lens[(i / T) / d.Hq], 1), pg.tstride * d.Bs);
+    if (pg.seq_lens) lim = seq_len_of(pg.seq_lens, (int)((i / T) / d.Hq), d.T);
     token_idx[i] = col < lim ? col : -1;
   }
 }

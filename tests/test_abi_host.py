@@ -300,3 +300,36 @@ def test_variant_and_layer_validation():
                                        FAKE, null, FAKE, 1 << 30, null) == E
     # recall: count < 1
     assert lib.ksa_attention_recall(FAKE, FAKE, FAKE, 0, null) == E
+
+
+def test_paged_vote_history_limit():
+    """ksa_paged_vote_select keeps the vote's history limit (T - W <= 2^21)
+    like every other vote entry point: a longer history is unsupported and
+    nothing is launched."""
+    lib = ksa.load_library()
+    U = ksa.KSA_ERR_UNSUPPORTED
+    FA = ctypes.c_void_p(0x10000)
+    T = (1 << 21) + 2048
+    p = P(B=1, Hq=4, Hkv=1, D=128, T=T, Tcap=T, Bs=16, dtype=ksa.KSA_BF16)
+    g = ksa.PagedKv(FA, FA, T // 16, T // 16)
+
+    def vote(N, W):
+        return lib.ksa_paged_vote_select(ctypes.byref(p), ctypes.byref(g), FAKE, FAKE, N, W, FAKE,
+                                         None, FAKE, 1 << 40, None)
+
+    assert vote(1024, 0) == U
+    assert vote(4096, 2047) == U          # T - W = 2^21 + 1
+    assert lib.ksa_vote_select(ctypes.byref(p), FAKE, FAKE, 1024, 0, FAKE, None, FAKE, 1 << 40,
+                               None) == U
+
+
+def test_workspace_sizing_ignores_the_environment(monkeypatch):
+    """Workspace sizes (and the launch plans behind them) are a function of
+    the arguments alone: no environment variable changes them."""
+    shapes = [P(B=16, Hq=32, Hkv=8, D=128, T=20000, Tcap=20000, Bs=1, dtype=ksa.KSA_BF16),
+              P(B=1, Hkv=1, Hq=1, T=1 << 15, Tcap=1 << 15), P()]
+    ops = [(ksa.KSA_OP_SPARSE_TOKENS, 2048), (ksa.KSA_OP_DENSE, 0), (ksa.KSA_OP_SPARSE_BLOCKS, 8)]
+    before = [ksa.ksa_workspace_bytes(p, op, prm) for p in shapes for op, prm in ops]
+    monkeypatch.setenv("KSA_ATTN_PLAN", "1,32")
+    after = [ksa.ksa_workspace_bytes(p, op, prm) for p in shapes for op, prm in ops]
+    assert before == after

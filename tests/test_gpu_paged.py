@@ -428,3 +428,96 @@ def test_paged_per_head_sets_equal_contiguous_bitwise():
     co, cl = ksa.ksa_sparse_decode(q, k, v, T, ci, ksa.KSA_SEL_HEAD_TOKENS)
     torch.cuda.synchronize()
     assert torch.equal(po, co) and torch.equal(pl, cl)
+
+
+def _canary(shape, dtype, fill, extra=4096):
+    """A buffer of `shape` followed by `extra` elements of `fill`; returns
+    (view of the front, the whole buffer)."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + extra,), fill, dtype=dtype, device=DEV)
+    return buf[:n].view(*shape), buf
+
+
+def _ws(prob, op, param):
+    need = max(16, ksa.ksa_workspace_bytes(prob, op, param))
+    front, buf = _canary((need,), torch.uint8, 0x5A, extra=1 << 16)
+    return front, buf, need
+
+
+@pytest.mark.parametrize("G,D,dtype", [(4, 128, "bf16"), (2, 64, "f32")], ids=["mfma", "valu"])
+def test_paged_lengths_past_seq_len_are_clamped(G, D, dtype):
+    """A length above the call's seq_len T acts as T in every paged call: the
+    outputs equal those of the same call with the lengths clamped, and no
+    write lands past the buffers sized from T (votes [B,T], token_idx,
+    block_idx, block_scores, workspaces)."""
+    Bs, T, N, W, top_k = 16, 800, 256, 64, 12
+    lens = [700, 1100, 300]
+    w, q, k, v, kp, vp, table, seq = paged_inputs(lens, Bs, seed=91, Hq=G * 2, Hkv=2, D=D,
+                                                  dtype=dtype)
+    seq_c = torch.tensor([min(t, T) for t in lens], dtype=torch.int32, device=DEV)
+    B, Hkv, mb = w.B, w.Hkv, table.shape[1]
+    prob, _ = ksa._paged_args(q, kp, table, seq, T, 0.0)
+    NB = ksa.nblocks(T, Bs)
+
+    def run(lengths):
+        r = {}
+        s = torch.zeros((B, Hkv, mb, D), dtype=kp.dtype, device=DEV)
+        ksa.ksa_paged_block_summaries(kp, s, table, lengths, max_len=T)
+        r["summ"] = s.clone()
+        idx, ib = _canary((B, Hkv, top_k), torch.int32, -7)
+        r["step"] = ksa.ksa_paged_block_topk_decode(q, kp, vp, s, table, lengths, top_k, max_len=T,
+                                                    block_idx=idx)
+        r["idx_pad"] = ib[idx.numel():]
+        ws, wb, need = _ws(prob, ksa.KSA_OP_PAGED_DENSE, 0)
+        r["dense"] = ksa.ksa_paged_dense_decode(q, kp, vp, table, lengths, max_len=T, workspace=ws)
+        r["dense_ws_pad"] = wb[need:]
+        sc, sb = _canary((B, Hkv, NB), torch.float32, -3.0)
+        ws, wb, need = _ws(prob, ksa.KSA_OP_SELECT_TOPK, top_k)
+        ids2, ib2 = _canary((B, Hkv, top_k), torch.int32, -7)
+        ksa.ksa_paged_select_topk_ex(q, r["summ"], table, lengths, Bs, top_k, max_len=T,
+                                     block_idx=ids2, block_scores=sc, workspace=ws)
+        r["sel_ex"], r["scores"] = ids2.clone(), sc.clone()
+        r["sel_pads"] = (sb[sc.numel():], ib2[ids2.numel():], wb[need:])
+        tok, tb = _canary((B, min(N, T)), torch.int32, -9)
+        votes, vb = _canary((B, T), torch.uint8, 0xAB)
+        ws, wb, need = _ws(prob, ksa.KSA_OP_VOTE_SELECT, N)
+        ksa.ksa_paged_vote_select(q, kp, table, lengths, N, W, max_len=T, token_idx=tok,
+                                  votes=votes, workspace=ws)
+        r["vote"] = (tok.clone(), votes.clone())
+        r["vote_pads"] = (tb[tok.numel():], vb[votes.numel():], wb[need:])
+        ws, wb, need = _ws(prob, ksa.KSA_OP_SPARSE_TOKENS, tok.shape[1])
+        r["tok_attn"] = ksa.ksa_paged_sparse_decode(q, kp, vp, table, lengths, tok, max_len=T,
+                                                    workspace=ws)
+        r["tok_ws_pad"] = wb[need:]
+        tok2, tb2 = _canary((B, min(N, T)), torch.int32, -9)
+        votes2, vb2 = _canary((B, T), torch.uint8, 0xAB)
+        ws, wb, need = _ws(prob, ksa.KSA_OP_PAGED_VOTE_LAYER, N)
+        r["layer"] = ksa.ksa_paged_vote_layer_decode(q, kp, vp, table, lengths, N, W, max_len=T,
+                                                     token_idx=tok2, votes=votes2, workspace=ws)
+        r["layer_pads"] = (tb2[tok2.numel():], vb2[votes2.numel():], wb[need:])
+        torch.cuda.synchronize()
+        return r
+
+    got, ref = run(seq), run(seq_c)
+    assert torch.equal(got["summ"], ref["summ"])
+    for a, b in zip(got["step"], ref["step"]):
+        assert torch.equal(a, b)
+    for a, b in zip(got["dense"], ref["dense"]):
+        assert torch.equal(a, b)
+    assert torch.equal(got["sel_ex"], ref["sel_ex"]) and torch.equal(got["scores"], ref["scores"])
+    for a, b in zip(got["vote"], ref["vote"]):
+        assert torch.equal(a, b)
+    for a, b in zip(got["tok_attn"], ref["tok_attn"]):
+        assert torch.equal(a, b)
+    for a, b in zip(got["layer"], ref["layer"]):
+        assert torch.equal(a, b)
+    # nothing written past the T-sized buffers
+    assert torch.all(got["idx_pad"] == -7)
+    assert torch.all(got["dense_ws_pad"] == 0x5A)
+    sp, ip, wp = got["sel_pads"]
+    assert torch.all(sp == -3.0) and torch.all(ip == -7) and torch.all(wp == 0x5A)
+    for pad, fill in zip(got["vote_pads"], (-9, 0xAB, 0x5A)):
+        assert torch.all(pad == fill)
+    assert torch.all(got["tok_ws_pad"] == 0x5A)
+    for pad, fill in zip(got["layer_pads"], (-9, 0xAB, 0x5A)):
+        assert torch.all(pad == fill)
