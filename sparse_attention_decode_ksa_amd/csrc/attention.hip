@@ -2,6 +2,8 @@
 // The per-row bodies (numerics, lane layout, pipelining) are in
 // ksa_attention.h; this file holds the kernels that give each workgroup one
 // (row, split) pair, the fixed-order split merge, and plan_attention.
+#include <atomic>
+#include <chrono>
 #include <type_traits>
 
 #include "ksa_attention.h"
@@ -122,32 +124,6 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_l
     attn_row_valu<T, D, G, KIND>(a, row, split, s_idx, s_pg, e0, true);
 }
 
-// Fixed-order merge of the split partial states of each row.
-template <int D, int G>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_acc,
-                                                         const float* __restrict__ part_ml,
-                                                         int splits, Dims d, float* __restrict__ out,
-                                                         float* __restrict__ lse) {
-  const int row = blockIdx.x;
-  const int b = row / d.Hkv, g = row - b * d.Hkv;
-  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
-    const int h = o / D, e = o - (o / D) * D;
-    const int64_t p0 = (int64_t)row * splits * G + h;
-    float M = -FLT_MAX;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(p0 + (int64_t)s * G) * 2]);
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const int64_t pi = p0 + (int64_t)s * G;
-      const float sc = fast_exp2(part_ml[pi * 2] - M);
-      L = fmaf(part_ml[pi * 2 + 1], sc, L);
-      A = fmaf(part_acc[pi * D + e], sc, A);
-    }
-    const int64_t oh = (int64_t)b * d.Hq + g * G + h;
-    out[oh * D + e] = A / L;
-    if (e == 0 && lse) lse[oh] = (M + log2f(L)) * kLn2;
-  }
-}
-
 template <typename T, int D, int G>
 hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStream_t s) {
   const int rows = a.d.B * a.d.Hkv;
@@ -190,10 +166,6 @@ hipError_t launch_typed(const AttnArgs& a, int kind, const AttnPlan& p, hipStrea
       default: hipLaunchKernelGGL((attn_partial_kernel<T, D, G, 2>), grid, block, 0, s, a); break;
     }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(rows), dim3(256), 0, s, a.part_acc, a.part_ml,
-                     p.splits, a.d, a.out, a.lse);
   return hipGetLastError();
 }
 
@@ -213,11 +185,14 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   const int ch = chunk_tokens(d);
   const int64_t chunks = (tokens_per_row + ch - 1) / ch;
   const int64_t rows = (int64_t)d.B * d.Hkv;
-  const int64_t kCUs = 256;              // MI355X compute units
-  const int64_t kMinChunksPerWave = 8;   // keeps each wave's pipeline busy past its fill
-  // Fewest splits that still give every CU a workgroup (a split costs a merge),
-  // as long as each split keeps real work.
-  int64_t splits = (kCUs + rows - 1) / rows;
+  // Planned for MI355X (256 CUs) whatever the device, so that the plan, the
+  // workspace size and the fp32 merge order are functions of the shape alone.
+  const int64_t kCUs = 256;
+  const int64_t kMinChunksPerWave = KSA_PLAN_MIN_CHUNKS;  // keeps a wave's pipeline busy past its fill
+  // Splits: the fewest that give every CU KSA_PLAN_WGS_PER_CU workgroups (a
+  // split row is merged by its last workgroup to finish), as long as each
+  // split keeps real work.
+  int64_t splits = (kCUs * KSA_PLAN_WGS_PER_CU + rows - 1) / rows;
   const int64_t max_splits = chunks / kMinChunksPerWave > 1 ? chunks / kMinChunksPerWave : 1;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -239,20 +214,40 @@ AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row) {
   if (cps < 1) cps = 1;
   splits = (chunks + cps - 1) / cps;
   if (splits < 1) splits = 1;
+  if (splits > kMaxSplits) {  // arrival counts are 16-bit
+    splits = kMaxSplits;
+    cps = (chunks + splits - 1) / splits;
+  }
   return AttnPlan{nw, (int)splits, (int)cps, ch};
 }
 
 size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p) {
   if (p.splits <= 1) return 0;
   const size_t rows = (size_t)d.B * d.Hkv;
-  return rows * p.splits * d.G * (size_t)(d.D + 2) * sizeof(float);
+  return arrival_bytes(rows) + rows * p.splits * d.G * (size_t)(d.D + 2) * sizeof(float);
 }
+
+namespace {
+// A 47-bit tag per call (bit 47 clear), for the arrival words of split rows:
+// splitmix64 (Steele, Lea and Flood, 2014) of a process-wide call counter
+// started from the clock, so that tags differ between calls and processes.
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> counter{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count()};
+  unsigned long long x = counter.fetch_add(1, std::memory_order_relaxed) + 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  x ^= x >> 31;
+  return x & 0x7FFFFFFFFFFFull;
+}
+}  // namespace
 
 hipError_t launch_attention(const Dims& d, int kind, const void* q, const void* k, const void* v,
                             const int32_t* idx, int count, float* out, float* lse, void* workspace,
                             const AttnPlan& plan, hipStream_t stream, const PagedKv* paged,
                             const VoteKeys* vote_keys, int kv_div) {
   AttnArgs a = make_attn_args(d, kind, q, k, v, idx, count, out, lse, workspace, plan);
+  if (plan.splits > 1) a.tag = next_call_tag();
   if (paged) {
     a.table = paged->table;
     a.seq_lens = paged->seq_lens;

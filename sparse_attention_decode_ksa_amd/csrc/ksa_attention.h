@@ -23,7 +23,8 @@
 // (bf16 x bf16 products are exact), the per-slot online softmax keeps
 // (m, l, acc) in the log2 domain with hardware exp2, and P stays fp32 for the
 // P.V accumulation.  States are merged slot -> wave -> workgroup -> split in
-// a fixed order, so results are bitwise repeatable.
+// a fixed order, so results are bitwise repeatable; the split merge is done
+// by the row's last workgroup to finish (no separate merge launch).
 //
 // Pipelining.  The workgroup's slice of the index list is staged in LDS once;
 // while a wave computes one chunk, the K/V loads of its next
@@ -38,6 +39,19 @@
 namespace ksa {
 
 constexpr int kMaxWaves = 8;
+constexpr int kMaxSplits = 4096;  // workgroups per row (arrival counts are 16-bit)
+// Launch-plan knobs: workgroups per CU the split count aims at, and the
+// fewest chunks a wave is planned to stream.  One workgroup per CU is the
+// measured best for the short rows of a shared token set (c4 shape: 2 / 3 /
+// 4 per CU took 34.8 / 44.7 / 50.8 us against 29.4): a workgroup's fixed
+// costs (index staging, pipeline fill, the wave and split merges) outweigh
+// the extra bytes in flight once a row's 2048 tokens are cut finer.
+#ifndef KSA_PLAN_WGS_PER_CU
+#define KSA_PLAN_WGS_PER_CU 1
+#endif
+#ifndef KSA_PLAN_MIN_CHUNKS
+#define KSA_PLAN_MIN_CHUNKS 8
+#endif
 // chunks whose K/V loads are in flight while a wave computes another
 #ifndef KSA_ATTN_PREFETCH
 #define KSA_ATTN_PREFETCH 1
@@ -66,6 +80,10 @@ struct AttnArgs {
   float* lse;
   float* part_acc; // [rows, splits, G, D]
   float* part_ml;  // [rows, splits, G, 2]
+  // split rows: one arrival word per row, [tag:48 | arrivals:16]; the
+  // workgroup that completes a row's count merges the row (see merge_waves)
+  unsigned long long* arrive;
+  unsigned long long tag;  // this call's 47-bit tag (bit 47 clear)
   // paged cache (kind 3): pages of each sequence's logical blocks, lengths
   const int32_t* table;    // [B, tstride]
   const int32_t* seq_lens; // [B]
@@ -111,8 +129,11 @@ inline AttnArgs make_attn_args(const Dims& d, int kind, const void* q, const voi
   a.out = out;
   a.lse = lse;
   const size_t rows = (size_t)d.B * d.Hkv;
-  a.part_acc = (float*)workspace;
+  // workspace of a split plan: arrival words, then the partial states
+  a.arrive = (unsigned long long*)workspace;
+  a.part_acc = workspace ? (float*)((char*)workspace + arrival_bytes(rows)) : nullptr;
   a.part_ml = workspace ? a.part_acc + rows * plan.splits * d.G * d.D : nullptr;
+  a.tag = 0;
   a.table = nullptr;
   a.seq_lens = nullptr;
   a.tstride = 0;
@@ -244,14 +265,49 @@ __device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], 
   }
 }
 
+// Arrival at a split row's word: returns how many of the row's workgroups
+// (this one included) have arrived in this call.  The word holds
+// [tag:48 | count:16]; a word whose tag is not this call's (left by an
+// earlier call, which re-tags it with bit 47 set, or never written) starts
+// the count afresh, so the workspace needs no clearing between calls.
+__device__ __forceinline__ int arrive_at_row(unsigned long long* w, unsigned long long tag) {
+  unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const bool mine = (old >> 16) == tag;
+    const unsigned long long want = mine ? old + 1ull : ((tag << 16) | 1ull);
+    if (__hip_atomic_compare_exchange_strong(w, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (int)(want & 0xFFFFull);
+  }
+}
+
+// Partial states cross workgroups (and XCDs, whose L2 caches are not
+// coherent with each other) as agent-scope atomic stores and loads, which
+// the hardware keeps coherent device-wide without writing back or
+// invalidating the L2 (an agent-scope fence does both, and costs ~0.7 us per
+// workgroup per XCD under load).  Each wave waits until its stores are
+// complete before the row's arrival word is updated, and the merging
+// workgroup reads the states only after it has seen the last arrival.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Merges the per-wave softmax states of a workgroup (staged in LDS) and
-// writes the row's output, or this split's partial state when the row is
-// split over several workgroups.  Fixed order: bitwise repeatable.
+// writes the row's output.  When the row is split over several workgroups,
+// each writes its partial state to the workspace and arrives at the row's
+// word; the workgroup that arrives last merges the row's partial states in
+// split order (fixed: bitwise repeatable) and re-tags the word for the next
+// call.
 template <int D, int G>
 __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, int g, int split,
                                             int nw, const float (*s_m)[G], const float (*s_l)[G],
                                             const float (*s_acc)[G][D]) {
   const Dims& d = a.d;
+  __shared__ int s_last;
   for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
     const int h = o / D, e = o - (o / D) * D;
     float M = -FLT_MAX;
@@ -268,13 +324,39 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
       if (e == 0 && a.lse) a.lse[oh] = (M + log2f(L)) * kLn2;
     } else {
       const int64_t pi = ((int64_t)row * a.splits + split) * G + h;
-      a.part_acc[pi * D + e] = A;
+      st_coherent(a.part_acc + pi * D + e, A);
       if (e == 0) {
-        a.part_ml[pi * 2] = M;
-        a.part_ml[pi * 2 + 1] = L;
+        st_coherent(a.part_ml + pi * 2, M);
+        st_coherent(a.part_ml + pi * 2 + 1, L);
       }
     }
   }
+  if (a.splits == 1) return;
+  wait_stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive_at_row(a.arrive + row, a.tag) == a.splits;
+  __syncthreads();
+  if (!s_last) return;
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
+    const int h = o / D, e = o - (o / D) * D;
+    const int64_t p0 = (int64_t)row * a.splits * G + h;
+    float M = -FLT_MAX;
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ld_coherent(a.part_ml + (p0 + (int64_t)s * G) * 2));
+    float L = 0.f, A = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+      const int64_t pi = p0 + (int64_t)s * G;
+      const float sc = fast_exp2(ld_coherent(a.part_ml + pi * 2) - M);
+      L = fmaf(ld_coherent(a.part_ml + pi * 2 + 1), sc, L);
+      A = fmaf(ld_coherent(a.part_acc + pi * D + e), sc, A);
+    }
+    const int64_t oh = (int64_t)b * d.Hq + g * G + h;
+    a.out[oh * D + e] = A / L;
+    if (e == 0 && a.lse) a.lse[oh] = (M + log2f(L)) * kLn2;
+  }
+  // every arrival of this call is in: the word takes a tag no call uses
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.arrive + row, ((~a.tag) & 0xFFFFFFFFFFFFull) << 16, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stages the index slice a workgroup (row, split) needs in LDS; returns the

@@ -46,6 +46,9 @@ struct AttnPlan {
 // kind: 0 = selected blocks, 1 = shared token list, 2 = dense range
 AttnPlan plan_attention(const Dims& d, int kind, int64_t tokens_per_row);
 size_t attention_workspace_bytes(const Dims& d, const AttnPlan& p);
+// Bytes of the per-row arrival words at the start of a split plan's
+// workspace (8 bytes a row, rounded up to 256).
+inline size_t arrival_bytes(size_t rows) { return (rows * 8 + 255) & ~(size_t)255; }
 
 // A paged cache (device table and lengths, see ksa_paged_kv).
 struct PagedKv {

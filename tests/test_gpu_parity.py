@@ -203,8 +203,8 @@ def test_all_blocks_selected_equals_dense():
     assert idx.shape[-1] == w.NB
     o1, l1 = ksa.ksa_sparse_decode(q, k, v, w.T, idx, ksa.KSA_SEL_BLOCKS, block_size=16)
     o2, l2 = ksa.ksa_dense_decode(q, k, v, w.T)
-    assert float((o1 - o2).abs().max()) < 1e-5
-    assert float((l1 - l2).abs().max()) < 1e-5
+    assert float((o1 - o2).abs().max()) <= 1e-6
+    assert float((l1 - l2).abs().max()) <= 1e-6
 
 
 def test_results_are_bitwise_repeatable_and_split_invariant():
@@ -223,9 +223,34 @@ def test_results_are_bitwise_repeatable_and_split_invariant():
     # the first sequence alone gets a different launch split; results agree
     o3, l3 = ksa.ksa_sparse_decode(q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(), w.T,
                                    idx[:1].contiguous(), ksa.KSA_SEL_BLOCKS, block_size=16)
-    assert float((o3 - o1[:1]).abs().max()) < 1e-5
+    assert float((o3 - o1[:1]).abs().max()) <= 1e-6
     d3, _ = ksa.ksa_dense_decode(q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(), w.T)
-    assert float((d3 - d1[:1]).abs().max()) < 1e-5
+    assert float((d3 - d1[:1]).abs().max()) <= 1e-6
+
+
+def test_split_rows_on_a_reused_workspace():
+    """Rows split over many workgroups, merged by the last one to arrive:
+    one workspace serves a long run of calls on two alternating inputs
+    (and starts filled with random bytes), and every call equals the same
+    call on a fresh workspace bit for bit, so no call reads another's
+    partial states or arrival counts."""
+    ws = torch.randint(0, 256, (1 << 24,), dtype=torch.uint8, device=DEV)
+    cases = []
+    for seed in (21, 22):
+        w = small_workload(B=2, Hq=8, Hkv=2, D=128, T=8192, dtype="bf16", seed=seed)
+        q, k, v = gpu_inputs(w)
+        tok = ksa.ksa_vote_select(q, k, w.T, 2048, 512)
+        p = ksa.make_problem(q, k, w.T)
+        assert ksa.ksa_workspace_bytes(p, ksa.KSA_OP_SPARSE_TOKENS, 2048) > 0  # rows are split
+        ref_s = ksa.ksa_sparse_decode(q, k, v, w.T, tok, ksa.KSA_SEL_TOKENS)
+        ref_d = ksa.ksa_dense_decode(q, k, v, w.T)
+        cases.append((w, q, k, v, tok, ref_s, ref_d))
+    for i in range(40):
+        w, q, k, v, tok, ref_s, ref_d = cases[i % 2]
+        o, l = ksa.ksa_sparse_decode(q, k, v, w.T, tok, ksa.KSA_SEL_TOKENS, workspace=ws)
+        assert torch.equal(o, ref_s[0]) and torch.equal(l, ref_s[1]), i
+        o, l = ksa.ksa_dense_decode(q, k, v, w.T, workspace=ws)
+        assert torch.equal(o, ref_d[0]) and torch.equal(l, ref_d[1]), i
 
 
 # ----------------------------------------------------------------------------- votes
