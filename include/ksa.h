@@ -27,7 +27,8 @@
  *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is the
  *     default stream) and returns without synchronising.  The library never
  *     allocates, frees or synchronises device memory and keeps no pointer
- *     after a call returns.  Calls on different streams with disjoint outputs
+ *     after a call returns (ksa_sparse_decode_noalloc uses a device array of
+ *     the library's own instead of a workspace).  Calls on different streams with disjoint outputs
  *     and workspaces may run concurrently.
  *   - Arguments are validated on the host before any launch.  On any status
  *     other than KSA_OK nothing is launched and no output is written, except
@@ -38,7 +39,8 @@
  *   - Workspaces: a call that needs one takes `workspace` (device memory,
  *     16-byte aligned, contents irrelevant) of at least ksa_workspace_bytes()
  *     bytes; it is scratch for that call only.  Concurrent calls need
- *     distinct workspaces.
+ *     distinct workspaces.  (An attention workspace starts with one 8-byte
+ *     arrival word per split row, tagged per call, so it needs no clearing.)
  *   - Ranking ties are broken by the lowest index everywhere; every index
  *     list is written in ascending order.
  *   - No C++ exception crosses this interface.
@@ -151,6 +153,33 @@ ksa_status ksa_select_topk(const ksa_problem* problem, const void* q, const void
 ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const void* k,
                              const void* v, const ksa_selection* sel, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the device array behind ksa_sparse_decode_noalloc, one per GPU. */
+#define KSA_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* ksa_sparse_decode_noalloc -- ksa_sparse_decode for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * layouts and results (bit for bit) as ksa_sparse_decode, without the
+ * workspace: the call's scratch (the partial states and arrival words of
+ * rows split over several workgroups) lives in a library-owned device array
+ * of KSA_NOALLOC_SCRATCH_BYTES on each GPU, created with the library and held
+ * until the process ends; its address is looked up once per device on the
+ * first call.  The call allocates nothing and needs nothing cleared (arrival
+ * words carry a per-call tag).  Every call on a GPU shares that GPU's array:
+ * calls that may overlap on one GPU (other streams, or graph replays running
+ * concurrently) race and give undefined results; calls ordered on one
+ * stream are safe.  `stream` must belong to the current device, else
+ * KSA_ERR_INVALID_ARGUMENT.  A call needs scratch only when its rows are
+ * split: when there are fewer than 256 rows (at most ~2.2 MB then, for
+ * lists of up to 2048 entries), or when a row's list has more than 2048
+ * entries (staged 2048 at a time).  A call whose scratch would exceed the
+ * array (ksa_workspace_bytes(problem, KSA_OP_SPARSE_BLOCKS, _TOKENS or
+ * _HEAD_TOKENS, sel->count) > KSA_NOALLOC_SCRATCH_BYTES) returns
+ * KSA_ERR_UNSUPPORTED before touching the device. */
+ksa_status ksa_sparse_decode_noalloc(const ksa_problem* problem, const void* q, const void* k,
+                                     const void* v, const ksa_selection* sel, float* out,
+                                     float* lse, void* stream);
 
 /* ---------------------------------------------------------------------
  * ksa_vote_select -- the shared token set of the vote-union variant

@@ -8,7 +8,7 @@ library's HIP kernels; there is no CPU or PyTorch fallback, and a missing or
 unloadable library raises :class:`KsaLibraryError` on first use.
 
 Function names match the C entry points: ``ksa_block_summaries``,
-``ksa_select_topk``, ``ksa_sparse_decode``, ``ksa_block_topk_decode`` (and
+``ksa_select_topk``, ``ksa_sparse_decode`` (and ``ksa_sparse_decode_noalloc``, no workspace), ``ksa_block_topk_decode`` (and
 ``ksa_block_topk_decode_varlen``, one length per sequence), ``ksa_vote_select``, ``ksa_dense_decode``, the paged-cache calls
 ``ksa_paged_block_summaries``, ``ksa_paged_block_topk_decode`` and
 ``ksa_paged_dense_decode``, ``ksa_paged_vote_select``, ``ksa_paged_sparse_decode``,
@@ -47,8 +47,9 @@ EXPORTED = ("ksa_block_summaries", "ksa_select_topk", "ksa_sparse_decode",
             "ksa_vote_layer_decode", "ksa_vote_select_per_head", "ksa_paged_vote_select",
             "ksa_paged_sparse_decode", "ksa_paged_vote_layer_decode", "ksa_paged_select_topk_ex",
             "ksa_paged_vote_select_heads", "ksa_paged_vote_select_per_head",
-            "ksa_block_topk_decode_varlen", "ksa_workspace_bytes", "ksa_status_string",
-            "ksa_version")
+            "ksa_block_topk_decode_varlen", "ksa_sparse_decode_noalloc", "ksa_workspace_bytes",
+            "ksa_status_string", "ksa_version")
+NOALLOC_SCRATCH_BYTES = 4 << 20  # KSA_NOALLOC_SCRATCH_BYTES
 KSA_AGG_SUM, KSA_AGG_MAX = 0, 1
 
 
@@ -135,6 +136,7 @@ def load_library(path: str = LIB_PATH):
         lib.ksa_paged_vote_select_heads.argtypes = [PP, PG, P, P, I32, I32, P, I32, P, P, P, SZ, P]
         lib.ksa_paged_vote_select_per_head.argtypes = [PP, PG, P, P, I32, I32, P, P, SZ, P]
         lib.ksa_block_topk_decode_varlen.argtypes = [PP, P, P, P, P, P, I32, I32, P, P, P, P]
+        lib.ksa_sparse_decode_noalloc.argtypes = [PP, P, P, P, ctypes.POINTER(Selection), P, P, P]
         lib.ksa_workspace_bytes.argtypes = [PP, I32, I32]
         lib.ksa_workspace_bytes.restype = SZ
         lib.ksa_status_string.argtypes = [ctypes.c_int]
@@ -297,6 +299,33 @@ def ksa_sparse_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len
                                  _dev(out, "out", torch.float32, (B, Hq, D)),
                                  _dev(lse, "lse", torch.float32, (B, Hq)), pws, nws,
                                  _stream(stream)), "ksa_sparse_decode")
+    return out, lse
+
+
+def ksa_sparse_decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_len: int,
+                              idx: torch.Tensor, kind: int = KSA_SEL_BLOCKS, block_size: int = 1,
+                              out=None, lse=None, want_lse: bool = True, sm_scale: float = 0.0,
+                              stream=None):
+    """ksa_sparse_decode without a workspace: the library's own per-GPU
+    scratch array holds the split rows' state (for callers that cannot
+    allocate; calls overlapping on one GPU race).  Pass `out` (and `lse`)
+    to allocate nothing at all."""
+    lib = load_library()
+    prob = make_problem(q, k, seq_len, block_size, sm_scale)
+    B, Hq, D = q.shape
+    count = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ishape = {KSA_SEL_BLOCKS: (B, prob.num_kv_heads, count), KSA_SEL_TOKENS: (B, count),
+              KSA_SEL_HEAD_TOKENS: (B, Hq, count)}[kind]
+    sel = Selection(int(kind), _dev(idx, "idx", torch.int32, ishape), int(count))
+    _check(lib.ksa_sparse_decode_noalloc(ctypes.byref(prob), _dev(q, "q", k.dtype), _dev(k, "k"),
+                                         _dev(v, "v", k.dtype, k.shape), ctypes.byref(sel),
+                                         _dev(out, "out", torch.float32, (B, Hq, D)),
+                                         _dev(lse, "lse", torch.float32, (B, Hq)),
+                                         _stream(stream)), "ksa_sparse_decode_noalloc")
     return out, lse
 
 

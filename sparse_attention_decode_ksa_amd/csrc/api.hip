@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <new>
 
 #include "ksa_internal.h"
@@ -130,6 +131,91 @@ ksa_status head_mask(const ksa_problem& p, const int32_t* voting_heads, int32_t 
 }  // namespace
 }  // namespace ksa
 
+// ---------------------------------------------------------------- no-allocation scratch
+// Split-row scratch (partial states and arrival words) of
+// ksa_sparse_decode_noalloc: one array per GPU the library runs on, held
+// until the process ends, shared by every such call on that GPU.  Rows are
+// split when there are fewer than 256 of them (at most ~2.2 MB of scratch
+// for lists of up to 2048 entries) or when a list outgrows the 2048-entry
+// LDS stage; calls needing more than the array are refused.  On the host,
+// `scratch` names a
+// stand-in, not a device address: kernels get the address that
+// hipGetSymbolAddress returns for the device, found once per device.
+static __device__ __align__(256) unsigned char scratch[KSA_NOALLOC_SCRATCH_BYTES];
+
+namespace ksa {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// The scratch of the device `stream` runs on, which must be the current
+// device (hipGetSymbolAddress resolves the symbol on the current device).
+ksa_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KSA_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return KSA_ERR_HIP;
+    if (sdev != dev) return KSA_ERR_INVALID_ARGUMENT;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return KSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KSA_OK;
+}
+
+// ksa_sparse_decode, with the workspace size check delegated: workspace_for
+// receives the bytes the call needs and returns whether `workspace` holds
+// them (the no-allocation entry point supplies its own scratch there).
+template <typename WorkspaceFor>
+ksa_status sparse_decode(const ksa_problem* problem, const void* q, const void* k, const void* v,
+                         const ksa_selection* sel, float* out, float* lse, void* stream,
+                         WorkspaceFor workspace_for) {
+  if (!sel) return KSA_ERR_INVALID_ARGUMENT;
+  const bool blocks = sel->kind == KSA_SEL_BLOCKS;
+  if (!blocks && sel->kind != KSA_SEL_TOKENS && sel->kind != KSA_SEL_HEAD_TOKENS)
+    return KSA_ERR_INVALID_ARGUMENT;
+  ksa_status st = check_problem(problem, blocks);
+  if (st != KSA_OK) return st;
+  const Dims d = make_dims(*problem);
+  if (!q || !k || !v || !out || !sel->idx) return KSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(out) || !aligned4(sel->idx) ||
+      (lse && !aligned4(lse)))
+    return KSA_ERR_INVALID_ARGUMENT;
+  if (sel->count < 1) return KSA_ERR_INVALID_ARGUMENT;
+  if (blocks && sel->count > d.NB) return KSA_ERR_INVALID_ARGUMENT;
+  if (!blocks && sel->count > d.T) return KSA_ERR_INVALID_ARGUMENT;
+  if (blocks && (int64_t)sel->count * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
+  if (sel->kind == KSA_SEL_HEAD_TOKENS) {  // rows are query heads, each its own group
+    Dims dh = d;
+    dh.Hkv = d.Hq;
+    dh.G = 1;
+    const AttnPlan plan = plan_attention(dh, 4, sel->count);
+    void* workspace = nullptr;
+    st = workspace_for(attention_workspace_bytes(dh, plan), &workspace);
+    if (st != KSA_OK) return st;
+    return from_hip(launch_attention(dh, 4, q, k, v, sel->idx, sel->count, out, lse, workspace,
+                                     plan, (hipStream_t)stream, nullptr, nullptr, d.G));
+  }
+  const int64_t ltot = blocks ? (int64_t)sel->count * d.Bs : sel->count;
+  const AttnPlan plan = plan_attention(d, blocks ? 0 : 1, ltot);
+  void* workspace = nullptr;
+  st = workspace_for(attention_workspace_bytes(d, plan), &workspace);
+  if (st != KSA_OK) return st;
+  return from_hip(launch_attention(d, blocks ? 0 : 1, q, k, v, sel->idx, sel->count, out, lse,
+                                   workspace, plan, (hipStream_t)stream));
+}
+
+}  // namespace
+}  // namespace ksa
+
 using namespace ksa;
 
 extern "C" {
@@ -190,39 +276,25 @@ ksa_status ksa_select_topk(const ksa_problem* problem, const void* q, const void
 ksa_status ksa_sparse_decode(const ksa_problem* problem, const void* q, const void* k,
                              const void* v, const ksa_selection* sel, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (!sel) return KSA_ERR_INVALID_ARGUMENT;
-  const bool blocks = sel->kind == KSA_SEL_BLOCKS;
-  if (!blocks && sel->kind != KSA_SEL_TOKENS && sel->kind != KSA_SEL_HEAD_TOKENS)
-    return KSA_ERR_INVALID_ARGUMENT;
-  ksa_status st = check_problem(problem, blocks);
-  if (st != KSA_OK) return st;
-  const Dims d = make_dims(*problem);
-  if (!q || !k || !v || !out || !sel->idx) return KSA_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(out) || !aligned4(sel->idx) ||
-      (lse && !aligned4(lse)))
-    return KSA_ERR_INVALID_ARGUMENT;
-  if (sel->count < 1) return KSA_ERR_INVALID_ARGUMENT;
-  if (blocks && sel->count > d.NB) return KSA_ERR_INVALID_ARGUMENT;
-  if (!blocks && sel->count > d.T) return KSA_ERR_INVALID_ARGUMENT;
-  if (blocks && (int64_t)sel->count * d.Bs > INT32_MAX / 2) return KSA_ERR_UNSUPPORTED;
-  if (sel->kind == KSA_SEL_HEAD_TOKENS) {  // rows are query heads, each its own group
-    Dims dh = d;
-    dh.Hkv = d.Hq;
-    dh.G = 1;
-    const AttnPlan plan = plan_attention(dh, 4, sel->count);
-    const size_t need = attention_workspace_bytes(dh, plan);
-    if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
-    if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
-    return from_hip(launch_attention(dh, 4, q, k, v, sel->idx, sel->count, out, lse, workspace,
-                                     plan, (hipStream_t)stream, nullptr, nullptr, d.G));
-  }
-  const int64_t ltot = blocks ? (int64_t)sel->count * d.Bs : sel->count;
-  const AttnPlan plan = plan_attention(d, blocks ? 0 : 1, ltot);
-  const size_t need = attention_workspace_bytes(d, plan);
-  if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
-  if (need && (!workspace || !aligned16(workspace))) return KSA_ERR_INVALID_ARGUMENT;
-  return from_hip(launch_attention(d, blocks ? 0 : 1, q, k, v, sel->idx, sel->count, out, lse,
-                                   workspace, plan, (hipStream_t)stream));
+  return sparse_decode(problem, q, k, v, sel, out, lse, stream,
+                       [&](size_t need, void** ws) -> ksa_status {
+                         if (workspace_bytes < need) return KSA_ERR_WORKSPACE_TOO_SMALL;
+                         if (need && (!workspace || !aligned16(workspace)))
+                           return KSA_ERR_INVALID_ARGUMENT;
+                         *ws = workspace;
+                         return KSA_OK;
+                       });
+}
+
+ksa_status ksa_sparse_decode_noalloc(const ksa_problem* problem, const void* q, const void* k,
+                                     const void* v, const ksa_selection* sel, float* out,
+                                     float* lse, void* stream) {
+  return sparse_decode(problem, q, k, v, sel, out, lse, stream,
+                       [&](size_t need, void** ws) -> ksa_status {
+                         if (need > (size_t)KSA_NOALLOC_SCRATCH_BYTES) return KSA_ERR_UNSUPPORTED;
+                         if (need == 0) return KSA_OK;
+                         return noalloc_scratch((hipStream_t)stream, ws);
+                       });
 }
 
 ksa_status ksa_vote_select(const ksa_problem* problem, const void* q, const void* k,

@@ -333,3 +333,28 @@ def test_workspace_sizing_ignores_the_environment(monkeypatch):
     monkeypatch.setenv("KSA_ATTN_PLAN", "1,32")
     after = [ksa.ksa_workspace_bytes(p, op, prm) for p in shapes for op, prm in ops]
     assert before == after
+
+
+def test_noalloc_scratch_size_and_limit():
+    """The binding's copy of KSA_NOALLOC_SCRATCH_BYTES is the header's; every
+    call whose rows are split only to fill the chip (fewer than 256 rows,
+    lists of at most 2048 entries) fits in it; a call needing more is
+    refused with KSA_ERR_UNSUPPORTED on the host, before any device call."""
+    lib = ksa.load_library()
+    text = open(HEADER).read()
+    m = re.search(r"#define KSA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ksa.NOALLOC_SCRATCH_BYTES
+    worst = 0
+    for rows in (1, 2, 3, 5, 16, 100, 128, 255):
+        for G in (1, 2, 4, 8):
+            p = P(B=rows, Hq=G, Hkv=1, D=128, T=1 << 15, Tcap=1 << 15, Bs=16, dtype=ksa.KSA_BF16)
+            for op, prm in ((ksa.KSA_OP_SPARSE_TOKENS, 2048), (ksa.KSA_OP_SPARSE_BLOCKS, 128)):
+                worst = max(worst, ksa.ksa_workspace_bytes(p, op, prm))
+    assert 0 < worst <= ksa.NOALLOC_SCRATCH_BYTES
+    # 255 rows of 8 heads over a 32768-token list: 16 splits a row, 17 MB
+    p = P(B=255, Hq=8, Hkv=1, D=128, T=1 << 15, Tcap=1 << 15, Bs=16, dtype=ksa.KSA_BF16)
+    assert ksa.ksa_workspace_bytes(p, ksa.KSA_OP_SPARSE_TOKENS, 1 << 15) > ksa.NOALLOC_SCRATCH_BYTES
+    sel = ksa.Selection(ksa.KSA_SEL_TOKENS, 0x10000, 1 << 15)
+    st = lib.ksa_sparse_decode_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(sel), FAKE,
+                                       FAKE, None)
+    assert st == ksa.KSA_ERR_UNSUPPORTED
