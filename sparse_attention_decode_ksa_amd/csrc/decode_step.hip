@@ -15,10 +15,12 @@
 //     path): the token rows of block (T-1)/Bs go through LDS, each lane sums
 //     its channels in fp64 in token order, and the rounded mean is written
 //     to the summaries and scored;
-//  3. top-k: the bucket search of ksa_topk.h on the LDS keys (over the
-//     gathered range, so no separate min/max pass) writes the
-//     selected block ids, ascending, into the attention's LDS index stage
-//     (and to block_idx when asked);
+//  3. top-k: row_topk_list of ksa_topk.h on the LDS keys (over the gathered
+//     range, so no separate min/max pass): one histogram round, the cut
+//     bucket ranked from an LDS list, a selection mask; then every wave
+//     writes the selected block ids, ascending, into the attention's LDS
+//     index stage (wave 0 also to block_idx when asked) and goes on to its
+//     attention at once;
 //  4. attention: the per-row body of ksa_attention.h (VALU, or MFMA for bf16
 //     D = 128 with G >= 4) over the selected blocks, one split.
 // The keys never leave the chip and three kernel boundaries disappear.  Each
@@ -256,16 +258,20 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
 #pragma unroll
   for (int i = 0; i < kStepKPT; ++i) key[i] = (i < kpt && j0 + i < NB) ? s_keys[j0 + i] : 0u;
   int32_t* gidx = s.block_idx ? s.block_idx + (int64_t)row * s.keff : nullptr;
-  row_topk_range<kStepKPT>(key, kpt, j0, NB, keff, s_lo, s_hi, s_topk, [&](int rank, int j) {
-    s_idx[rank] = j;
-    if constexpr (PAGED) s_pg[rank] = ptab[j];
-    if (gidx) gidx[rank] = j;
-  });
+  // every wave writes the whole ascending list into the LDS stage (the same
+  // values), so it starts its attention without waiting for the others
+  static_assert(kStepMaxBlocks <= kTopkListMax, "selection mask");
+  row_topk_list<kStepKPT>(key, kpt, j0, NB, keff, s_lo, s_hi, s_topk,
+                          [&](int rank, int j, bool primary) {
+                            s_idx[rank] = j;
+                            if constexpr (PAGED) s_pg[rank] = ptab[j];
+                            if (primary && gidx) gidx[rank] = j;
+                          });
   if (PAGED || a.seq_lens) {  // ids past this row's k_eff
     if (gidx)
       for (int i = keff + tid; i < s.keff; i += kStepThreads) gidx[i] = -1;
   }
-  __syncthreads();
+  wave_lds_fence();
 
   // 4. attention over the selected blocks
   constexpr int KIND = PAGED ? 3 : 0;

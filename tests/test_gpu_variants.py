@@ -15,7 +15,7 @@ import torch
 import oracle
 import sparse_attention_decode_ksa_amd as ksa
 from sparse_attention_decode_ksa_amd.inputs import WORKLOADS, small_workload
-from parity import check_block_selection, check_votes
+from parity import check_attention, check_block_selection, check_votes
 from test_gpu_parity import DEV, gpu_inputs, np_bits, run_summaries
 
 pytestmark = pytest.mark.gpu
@@ -174,7 +174,12 @@ def test_vote_layer_equals_dense_plus_vote(Hq, Hkv, D, dtype, T, N, W):
         check_votes(votes.cpu().numpy(), idx.cpu().numpy(), lg, N, W)
 
 
-def test_vote_layer_on_c4():
+@pytest.mark.parametrize("seqs", [[0, 15]])
+def test_vote_layer_on_c4(seqs):
+    """The selection layer at the full c4 shape: bitwise the dense call plus
+    the vote call, and on sampled sequences the fp64 oracle's dense attention
+    (out, lse) and vote rule (votes up to per-head near ties, the set exactly
+    the rule on the GPU's votes)."""
     w = WORKLOADS["c4"]
     q, k, v = gpu_inputs(w)
     N, W = w.token_budget, w.recent_window
@@ -184,6 +189,13 @@ def test_vote_layer_on_c4():
     torch.cuda.synchronize()
     assert torch.equal(out, dout) and torch.equal(lse, dlse)
     assert torch.equal(idx, ridx) and torch.equal(votes, rvotes)
+    for b in seqs:
+        sl = slice(b, b + 1)
+        qb, kb, vb = np_bits(q[sl]), np_bits(k[sl]), np_bits(v[sl])
+        ro, rl = oracle.attend_dense(qb, kb, vb, w.T)
+        check_attention(out[sl].cpu().numpy(), lse[sl].cpu().numpy(), ro, rl)
+        lg = oracle.head_logits(qb, kb, w.T)
+        check_votes(votes[sl].cpu().numpy(), idx[sl].cpu().numpy(), lg, N, W)
     del q, k, v
     torch.cuda.empty_cache()
 
