@@ -156,14 +156,21 @@ def counter_summary(args):
 
     kernel = traffic_kernel(args)
 
+    def template_args(base):
+        return [t.strip() for t in base[base.index("<") + 1:base.index(">(")].split(",")]
+
     def is_sparse(name):
         base = name.replace("ksa::(anonymous namespace)::", "")
         if kernel == "block_topk_decode":
             return base.startswith("void block_topk_decode_kernel<")
-        # the sparse attention kernel over a block (KIND 0) or token (KIND 1) list
+        # the sparse attention kernel over a block (KIND 0) or token (KIND 1) list:
+        # attn_partial_kernel<T, D, G, KIND> or attn_mfma_kernel<G, KIND, VK>
         kind = "1" if args.workload == "c4" else "0"
-        return (base.startswith("void attn_partial_kernel<") or base.startswith("void attn_mfma_kernel<")) \
-            and base.split(">(")[0].endswith(", " + kind)
+        if base.startswith("void attn_partial_kernel<"):
+            return template_args(base)[3] == kind
+        if base.startswith("void attn_mfma_kernel<"):
+            return template_args(base)[1] == kind
+        return False
 
     copy = lambda n: n == "__amd_rocclr_copyBuffer"
     f_kib, nf = per_kernel(fetch_csv, is_sparse)

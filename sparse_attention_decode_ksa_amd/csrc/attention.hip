@@ -64,10 +64,8 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_d
   const int e0 = (c_begin * CH) / Bs;
   const int e1 = min(nb, (c_end * CH + Bs - 1) / Bs);
   const int32_t* tb = a.table + (int64_t)b * a.tstride;
-  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) {
-    s_idx[i] = e0 + i;
-    s_pg[i] = tb[e0 + i];
-  }
+  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = e0 + i;
+  stage_copy(tb + e0, e1 - e0, s_pg);
   if constexpr (kMfma)
     attn_row_mfma<G, 3, VK>(a, row, split, s_idx, s_pg, e0, true);
   else
@@ -110,13 +108,33 @@ __global__ __launch_bounds__(kMaxWaves * 64, (G <= 2 ? 4 : 1)) void attn_paged_l
     src = a.idx + (int64_t)(KIND == 6 ? row : b) * a.count;
   }
   const int nbb = (Tb + Bs - 1) / Bs;
-  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) {
-    const int x = src[e0 + i];
-    s_idx[i] = x;
-    if constexpr (KIND == 3)
-      s_pg[i] = (x >= 0 && x < nbb) ? tb[x] : 0;
-    else
-      s_pg[i] = (x >= 0 && x < Tb) ? tb[x / Bs] * a.page_rows + x % Bs : 0;
+  // ids, then their pages, each a batch of loads in flight at once
+  const int n = e1 - e0;
+  if (n > 0) {
+    stage_batches(n, [&](int base) {
+      int x[kStageBatch], pg[kStageBatch];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u)
+        x[u] = src[e0 + min(base + u * (int)blockDim.x + (int)threadIdx.x, n - 1)];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const bool ok = KIND == 3 ? (x[u] >= 0 && x[u] < nbb) : (x[u] >= 0 && x[u] < Tb);
+        const int j = ok ? (KIND == 3 ? x[u] : x[u] / Bs) : 0;
+        pg[u] = tb[j];
+      }
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const int i = base + u * (int)blockDim.x + (int)threadIdx.x;
+        if (i < n) {
+          const bool ok = KIND == 3 ? (x[u] >= 0 && x[u] < nbb) : (x[u] >= 0 && x[u] < Tb);
+          s_idx[i] = x[u];
+          if constexpr (KIND == 3)
+            s_pg[i] = ok ? pg[u] : 0;
+          else
+            s_pg[i] = ok ? pg[u] * a.page_rows + x[u] % Bs : 0;
+        }
+      }
+    });
   }
   if constexpr (kMfma)
     attn_row_mfma<G, KIND>(a, row, split, s_idx, s_pg, e0, true);

@@ -310,13 +310,28 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
   __shared__ int s_last;
   for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
     const int h = o / D, e = o - (o / D) * D;
+    // every wave's state read at once (unrolled to kMaxWaves), combined in
+    // wave order
+    float mw[kMaxWaves], lw[kMaxWaves], aw[kMaxWaves];
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; ++w) {
+      const int ww = min(w, nw - 1);
+      mw[w] = s_m[ww][h];
+      lw[w] = s_l[ww][h];
+      aw[w] = s_acc[ww][h][e];
+    }
     float M = -FLT_MAX;
-    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][h]);
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; ++w)
+      if (w < nw) M = fmaxf(M, mw[w]);
     float L = 0.f, A = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      const float sc = fast_exp2(s_m[w][h] - M);
-      L = fmaf(s_l[w][h], sc, L);
-      A = fmaf(s_acc[w][h][e], sc, A);
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; ++w) {
+      if (w < nw) {
+        const float sc = fast_exp2(mw[w] - M);
+        L = fmaf(lw[w], sc, L);
+        A = fmaf(aw[w], sc, A);
+      }
     }
     if (a.splits == 1) {
       const int64_t oh = (int64_t)b * d.Hq + g * G + h;
@@ -337,17 +352,62 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
   if (threadIdx.x == 0) s_last = arrive_at_row(a.arrive + row, a.tag) == a.splits;
   __syncthreads();
   if (!s_last) return;
+  // the partial states of kMergeBatch splits are loaded before any is used
+  // (one round trip per batch rather than per split); the arithmetic keeps
+  // the split order: max over splits, then the rescaled sums in split order
+  constexpr int kMergeBatch = 8;
   for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
     const int h = o / D, e = o - (o / D) * D;
     const int64_t p0 = (int64_t)row * a.splits * G + h;
-    float M = -FLT_MAX;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, ld_coherent(a.part_ml + (p0 + (int64_t)s * G) * 2));
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-      const int64_t pi = p0 + (int64_t)s * G;
-      const float sc = fast_exp2(ld_coherent(a.part_ml + pi * 2) - M);
-      L = fmaf(ld_coherent(a.part_ml + pi * 2 + 1), sc, L);
-      A = fmaf(ld_coherent(a.part_acc + pi * D + e), sc, A);
+    float M = -FLT_MAX, L = 0.f, A = 0.f;
+    if (a.splits <= kMergeBatch) {
+      float pm[kMergeBatch], pl[kMergeBatch], pa[kMergeBatch];
+#pragma unroll
+      for (int s = 0; s < kMergeBatch; ++s) {
+        const int64_t pi = p0 + (int64_t)min(s, a.splits - 1) * G;
+        pm[s] = ld_coherent(a.part_ml + pi * 2);
+        pl[s] = ld_coherent(a.part_ml + pi * 2 + 1);
+        pa[s] = ld_coherent(a.part_acc + pi * D + e);
+      }
+#pragma unroll
+      for (int s = 0; s < kMergeBatch; ++s)
+        if (s < a.splits) M = fmaxf(M, pm[s]);
+#pragma unroll
+      for (int s = 0; s < kMergeBatch; ++s) {
+        if (s < a.splits) {
+          const float sc = fast_exp2(pm[s] - M);
+          L = fmaf(pl[s], sc, L);
+          A = fmaf(pa[s], sc, A);
+        }
+      }
+    } else {
+      for (int s0 = 0; s0 < a.splits; s0 += kMergeBatch) {
+        float pm[kMergeBatch];
+#pragma unroll
+        for (int s = 0; s < kMergeBatch; ++s)
+          pm[s] = ld_coherent(a.part_ml + (p0 + (int64_t)min(s0 + s, a.splits - 1) * G) * 2);
+#pragma unroll
+        for (int s = 0; s < kMergeBatch; ++s)
+          if (s0 + s < a.splits) M = fmaxf(M, pm[s]);
+      }
+      for (int s0 = 0; s0 < a.splits; s0 += kMergeBatch) {
+        float pm[kMergeBatch], pl[kMergeBatch], pa[kMergeBatch];
+#pragma unroll
+        for (int s = 0; s < kMergeBatch; ++s) {
+          const int64_t pi = p0 + (int64_t)min(s0 + s, a.splits - 1) * G;
+          pm[s] = ld_coherent(a.part_ml + pi * 2);
+          pl[s] = ld_coherent(a.part_ml + pi * 2 + 1);
+          pa[s] = ld_coherent(a.part_acc + pi * D + e);
+        }
+#pragma unroll
+        for (int s = 0; s < kMergeBatch; ++s) {
+          if (s0 + s < a.splits) {
+            const float sc = fast_exp2(pm[s] - M);
+            L = fmaf(pl[s], sc, L);
+            A = fmaf(pa[s], sc, A);
+          }
+        }
+      }
     }
     const int64_t oh = (int64_t)b * d.Hq + g * G + h;
     a.out[oh * D + e] = A / L;
@@ -357,6 +417,29 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
   if (threadIdx.x == 0)
     __hip_atomic_store(a.arrive + row, ((~a.tag) & 0xFFFFFFFFFFFFull) << 16, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Copies n int32 from global memory to LDS, the whole workgroup taking turns:
+// each thread issues up to kStageBatch loads before it waits for any (a
+// loop of load-then-store would wait for each load in turn).
+constexpr int kStageBatch = 8;
+template <typename F>
+__device__ __forceinline__ void stage_batches(int n, F body) {
+  for (int base = 0; base < n; base += kStageBatch * (int)blockDim.x) body(base);
+}
+__device__ __forceinline__ void stage_copy(const int32_t* __restrict__ src, int n, int* dst) {
+  if (n <= 0) return;
+  stage_batches(n, [&](int base) {
+    int v[kStageBatch];
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u)
+      v[u] = src[min(base + u * (int)blockDim.x + (int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u) {
+      const int i = base + u * (int)blockDim.x + (int)threadIdx.x;
+      if (i < n) dst[i] = v[u];
+    }
+  });
 }
 
 // Stages the index slice a workgroup (row, split) needs in LDS; returns the
@@ -381,7 +464,7 @@ __device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int spl
     // kind 1: the sequence's list; kind 4: the row's (query head's) own list
     src = a.idx + (int64_t)(KIND == 4 ? row : b) * a.count;
   }
-  for (int i = threadIdx.x; i < e1 - e0; i += blockDim.x) s_idx[i] = src[e0 + i];
+  stage_copy(src + e0, e1 - e0, s_idx);
   return e0;
 }
 
