@@ -276,9 +276,9 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   // 4. attention over the selected blocks
   constexpr int KIND = PAGED ? 3 : 0;
   if constexpr (kMfma)
-    attn_row_mfma<G, KIND>(a, row, 0, s_idx, s_pg, 0, false);
+    attn_row_mfma<G, KIND, false, NW>(a, row, 0, s_idx, s_pg, 0, false);
   else
-    attn_row_valu<T, D, G, KIND>(a, row, 0, s_idx, s_pg, 0, false, qraw);
+    attn_row_valu<T, D, G, KIND, NW>(a, row, 0, s_idx, s_pg, 0, false, qraw);
 }
 
 // Eight-wave workgroups of the step kernel that the device holds at once

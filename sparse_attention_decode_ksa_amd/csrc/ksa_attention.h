@@ -38,7 +38,11 @@
 
 namespace ksa {
 
-constexpr int kMaxWaves = 8;
+// waves a workgroup may have (the LDS merge arrays are sized for it)
+#ifndef KSA_MAX_WAVES
+#define KSA_MAX_WAVES 8
+#endif
+constexpr int kMaxWaves = KSA_MAX_WAVES;
 constexpr int kMaxSplits = 4096;  // workgroups per row (arrival counts are 16-bit)
 // Launch-plan knobs: workgroups per CU the split count aims at, and the
 // fewest chunks a wave is planned to stream.  One workgroup per CU is the
@@ -57,6 +61,12 @@ constexpr int kMaxSplits = 4096;  // workgroups per row (arrival counts are 16-b
 #define KSA_ATTN_PREFETCH 1
 #endif
 constexpr int kPrefetchChunks = KSA_ATTN_PREFETCH;
+// the same for the MFMA body (one chunk in flight is the measured best for
+// the token-set and block shapes it serves)
+#ifndef KSA_MFMA_PREFETCH
+#define KSA_MFMA_PREFETCH 1
+#endif
+constexpr int kMfmaPrefetch = KSA_MFMA_PREFETCH;
 // K/V rows are streamed once per call: nontemporal loads keep them from
 // displacing reusable lines in L2 and the Infinity Cache.
 #ifndef KSA_NT_LOADS
@@ -302,7 +312,7 @@ __device__ __forceinline__ void wait_stores_complete() { asm volatile("s_waitcnt
 // word; the workgroup that arrives last merges the row's partial states in
 // split order (fixed: bitwise repeatable) and re-tags the word for the next
 // call.
-template <int D, int G>
+template <int D, int G, int NWMAX = kMaxWaves>
 __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, int g, int split,
                                             int nw, const float (*s_m)[G], const float (*s_l)[G],
                                             const float (*s_acc)[G][D]) {
@@ -310,11 +320,11 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
   __shared__ int s_last;
   for (int o = threadIdx.x; o < G * D; o += blockDim.x) {
     const int h = o / D, e = o - (o / D) * D;
-    // every wave's state read at once (unrolled to kMaxWaves), combined in
+    // every wave's state read at once (unrolled to NWMAX), combined in
     // wave order
-    float mw[kMaxWaves], lw[kMaxWaves], aw[kMaxWaves];
+    float mw[NWMAX], lw[NWMAX], aw[NWMAX];
 #pragma unroll
-    for (int w = 0; w < kMaxWaves; ++w) {
+    for (int w = 0; w < NWMAX; ++w) {
       const int ww = min(w, nw - 1);
       mw[w] = s_m[ww][h];
       lw[w] = s_l[ww][h];
@@ -322,11 +332,11 @@ __device__ __forceinline__ void merge_waves(const AttnArgs& a, int row, int b, i
     }
     float M = -FLT_MAX;
 #pragma unroll
-    for (int w = 0; w < kMaxWaves; ++w)
+    for (int w = 0; w < NWMAX; ++w)
       if (w < nw) M = fmaxf(M, mw[w]);
     float L = 0.f, A = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMaxWaves; ++w) {
+    for (int w = 0; w < NWMAX; ++w) {
       if (w < nw) {
         const float sc = fast_exp2(mw[w] - M);
         L = fmaf(lw[w], sc, L);
@@ -472,7 +482,7 @@ __device__ __forceinline__ int stage_indices(const AttnArgs& a, int row, int spl
 // staged in s_idx (entries from e0 on).  `sync` waits for the staging.
 // qraw, when given, holds the lane's 16 bytes of each of the group's G query
 // rows (already loaded by the caller in this lane layout).
-template <typename T, int D, int G, int KIND>
+template <typename T, int D, int G, int KIND, int NWMAX = kMaxWaves>
 __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int split, const int* s_idx,
                                               const int* s_pg, int e0, bool sync,
                                               const uint4* qraw = nullptr) {
@@ -482,9 +492,9 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   constexpr int NI = kLoadsPerChunk;
   constexpr int CH = SPW * NI;
   constexpr int P = kPrefetchChunks;
-  __shared__ float s_m[kMaxWaves][G];
-  __shared__ float s_l[kMaxWaves][G];
-  __shared__ float s_acc[kMaxWaves][G][D];
+  __shared__ float s_m[NWMAX][G];
+  __shared__ float s_l[NWMAX][G];
+  __shared__ float s_acc[NWMAX][G][D];
 
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -581,7 +591,7 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   }
   __syncthreads();
 
-  merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
+  merge_waves<D, G, NWMAX>(a, row, b, g, split, nw, s_m, s_l, s_acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -606,7 +616,7 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
 // G in {4, 8}); indices staged as for attn_row_valu.
 // VK: the dense walk (kind 2, or kind 3 over every block) also writes the
 // vote's keys (a.vkeys); dense walks without a vote compile without them.
-template <int G, int KIND, bool VK = false>
+template <int G, int KIND, bool VK = false, int NWMAX = kMaxWaves>
 __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int split, const int* s_idx,
                                               const int* s_pg, int e0, bool sync) {
   static_assert(!VK || KIND == 2 || KIND == 3, "vote keys come from dense walks");
@@ -616,10 +626,10 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
   constexpr int NI = 4;
   constexpr int CH = 16;
   static_assert(CH == SPW * NI, "chunk of the VALU kernel");
-  __shared__ float s_m[kMaxWaves][G];
-  __shared__ float s_l[kMaxWaves][G];
-  __shared__ float s_acc[kMaxWaves][G][D];
-  __shared__ float s_p[kMaxWaves][CH + 1][8];  // rows 0..15: P[token][head]; row 16: rescale
+  __shared__ float s_m[NWMAX][G];
+  __shared__ float s_l[NWMAX][G];
+  __shared__ float s_acc[NWMAX][G][D];
+  __shared__ float s_p[NWMAX][CH + 1][8];  // rows 0..15: P[token][head]; row 16: rescale
 
   const Dims& d = a.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -677,23 +687,8 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
       store_range(VK ? (void*)(a.vkeys + ((int64_t)b * d.Hq + g * G) * a.vkstride) : nullptr,
                   VK ? (uint32_t)(G * a.vkstride) * 4u : 0u);
 
-  uint4 kb[NI], vb[NI];
-  bool okb = false;
-  if (my_n > 0) load(c0, kb, vb, okb);
-  // a store that writes nothing: the loop is entered with the same memory
-  // operations outstanding as every iteration leaves behind, so the waits
-  // for the next chunk's loads leave the previous chunk's key store in flight
-  if constexpr (VK) st16_range(krs, kDropOffset, make_uint4(0u, 0u, 0u, 0u));
-  for (int j = 0; j < my_n; ++j) {
-    uint4 kc[NI], vc[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kc[i] = kb[i];
-      vc[i] = vb[i];
-    }
-    const bool okc = okb;
-    if (j + 1 < my_n) load(c0 + (j + 1) * nw, kb, vb, okb);
-
+  // one chunk's scores, softmax update and P.V (chunk j of the wave)
+  auto consume = [&](const uint4* kc, const uint4* vc, bool okc, int j) {
     f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[i]), qop[i], S, 0, 0, 0);
@@ -760,6 +755,37 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv[h], f[e], acc[h][e]);
     }
     wave_lds_fence();
+  };
+
+  // a ring of kMfmaPrefetch register buffers: chunk j is consumed while the
+  // loads of the wave's next kMfmaPrefetch chunks are in flight
+  constexpr int PF = kMfmaPrefetch;
+  uint4 kb[PF][NI], vb[PF][NI];
+  bool okb[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    okb[u] = false;
+    if (u < my_n) load(c0 + u * nw, kb[u], vb[u], okb[u]);
+  }
+  // a store that writes nothing: the loop is entered with the same memory
+  // operations outstanding as every iteration leaves behind, so the waits
+  // for the next chunk's loads leave the previous chunk's key store in flight
+  if constexpr (VK) st16_range(krs, kDropOffset, make_uint4(0u, 0u, 0u, 0u));
+  for (int j0 = 0; j0 < my_n; j0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int j = j0 + u;
+      if (j >= my_n) break;
+      uint4 kc[NI], vc[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        kc[i] = kb[u][i];
+        vc[i] = vb[u][i];
+      }
+      const bool okc = okb[u];
+      if (j + PF < my_n) load(c0 + (j + PF) * nw, kb[u], vb[u], okb[u]);
+      consume(kc, vc, okc, j);
+    }
   }
 
   // slots share the wave's softmax state: their accumulators simply add up
@@ -781,7 +807,7 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
       for (int e = 0; e < EPL; ++e) s_acc[wave][h][li * EPL + e] = acc[h][e];
   }
   __syncthreads();
-  merge_waves<D, G>(a, row, b, g, split, nw, s_m, s_l, s_acc);
+  merge_waves<D, G, NWMAX>(a, row, b, g, split, nw, s_m, s_l, s_acc);
 }
 
 }  // namespace ksa
