@@ -686,6 +686,44 @@ __global__ __launch_bounds__(kSetThreads) void vote_set_kernel(
 // comes from a binary search whose counts are popcounts of bit-sliced
 // comparisons; the picks are the tokens above v* and the first ones on it,
 // placed in token order by one workgroup scan and staged in LDS.
+// Full adder on 32 lanes of bits: a + b + ci = s + 2 co.
+__device__ __forceinline__ void full_add(uint32_t a, uint32_t b, uint32_t ci, uint32_t& s,
+                                         uint32_t& co) {
+  const uint32_t u = a ^ b;
+  s = u ^ ci;
+  co = (a & b) | (u & ci);
+}
+
+// Adds eight bit vectors x[0..7] (bit j: token j of the word picked by that
+// head) into the bit-sliced counter c (plane k: bit k of each token's
+// total).  A carry-save tree first reduces the eight to a 4-bit count per
+// token (planes n0..n3), which a ripple adder then adds into c: about 53
+// bit operations, where adding the eight one at a time costs 3 * NP each.
+template <int NP>
+__device__ __forceinline__ void add8_bitsliced(uint32_t (&c)[NP], const uint32_t* x) {
+  static_assert(NP >= 4, "a count of eight needs four planes");
+  uint32_t s, t0, t1, t2;
+  full_add(x[0], x[1], x[2], s, t0);
+  full_add(s, x[3], x[4], s, t1);
+  full_add(s, x[5], x[6], s, t2);
+  const uint32_t n0 = s ^ x[7], t3 = s & x[7];  // weight 1; t0..t3 weight 2
+  uint32_t u, f0;
+  full_add(t0, t1, t2, u, f0);
+  const uint32_t n1 = u ^ t3, f1 = u & t3;      // weight 2; f0, f1 weight 4
+  const uint32_t n2 = f0 ^ f1, n3 = f0 & f1;    // weights 4 and 8
+  uint32_t cy = c[0] & n0;
+  c[0] ^= n0;
+  full_add(c[1], n1, cy, c[1], cy);
+  full_add(c[2], n2, cy, c[2], cy);
+  full_add(c[3], n3, cy, c[3], cy);
+#pragma unroll
+  for (int k = 4; k < NP; ++k) {
+    const uint32_t t = c[k] & cy;
+    c[k] ^= cy;
+    cy = t;
+  }
+}
+
 template <int NP>
 __device__ __forceinline__ uint32_t votes_at_least(const uint32_t (&c)[NP], int v) {
   // tokens of the word whose vote total is >= v (0 <= v < 2^NP), MSB first
@@ -741,20 +779,23 @@ __global__ __launch_bounds__(kSetThreads) void vote_tally_set_kernel(
 #pragma unroll
   for (int k = 0; k < NP; ++k) c[k] = 0u;
   const uint32_t* bw = bits + (int64_t)b * Hq * words + min(w, words - 1);
-  for (int h0 = 0; h0 < Hq; h0 += 8) {
-    uint32_t x[8];
+  // the heads' words in batches of 32 loads in flight (one round trip for
+  // up to 32 heads), added 8 at a time by a carry-save tree; waves whose
+  // words all lie past the history skip it (their totals stay zero)
+  if (__builtin_amdgcn_readfirstlane(tid & ~63) < words_b) {
+    for (int h0 = 0; h0 < Hq; h0 += 32) {
+      uint32_t x[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = bw[(int64_t)min(h0 + j, Hq - 1) * words];
+      for (int j = 0; j < 32; ++j) x[j] = bw[(int64_t)min(h0 + j, Hq - 1) * words];
+      if (h0 + 32 > Hq) {  // uniform: heads past Hq add nothing
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t carry = h0 + j < Hq ? x[j] & valid : 0u;
-#pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        const uint32_t t = c[k] & carry;
-        c[k] ^= carry;
-        carry = t;
+        for (int j = 0; j < 32; ++j) x[j] = h0 + j < Hq ? x[j] : 0u;
       }
+#pragma unroll
+      for (int j = 0; j < 32; j += 8) add8_bitsliced<NP>(c, x + j);
     }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) c[k] &= valid;
   }
   if (votes && w < words) {
     for (int j = 0; j < 32 && w * 32 + j < hist; ++j) {
@@ -766,7 +807,9 @@ __global__ __launch_bounds__(kSetThreads) void vote_tally_set_kernel(
   }
   if (kv == 0) return;  // uniform: the whole workgroup leaves
 
-  // v*: count(votes >= lo) >= Kv > count(votes >= hi), hi - lo shrinking to 1
+  // v*: count(votes >= lo) >= Kv > count(votes >= hi), hi - lo shrinking to
+  // 1 (a binary search: a handful of popcount rounds, where a histogram of
+  // every total would cost a wave reduction per total)
   auto count_at_least = [&](int v, int parity) {
     uint32_t n = (uint32_t)__popc(votes_at_least<NP>(c, v) & valid);
     n = wave_incl_scan_dpp(n);
