@@ -240,8 +240,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
 // Per (b, h), history of at most NT * KPT tokens: the head's keys sit in
 // registers, token t = i * NT + tid in key[i] (coalesced loads).  A first
 // histogram on the keys' 12 leading bits picks the bucket where the Kv
-// largest end, the bucket search of ksa_topk.h resolves it, and each wave's
-// ballot of "taken" is two words of the bitmask as it stands.  Ties at the
+// largest end, a second on the next 12 bits of the keys in that bucket
+// narrows it to one bin, the bucket search of ksa_topk.h resolves the last 8
+// bits when needed, and each wave's ballot of "taken" is two words of the
+// bitmask as it stands.  Ties at the
 // threshold (equal fp32 logits) take the lowest token ids: the equal keys
 // are ranked in token order by a per-(slot, wave) count.  The first
 // workgroup of each sequence also clears that sequence's vote histogram,
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
   static_assert(4096 % NT == 0, "radix buckets per thread");
   __shared__ TopkShared sh;
   __shared__ uint32_t s_rh[4097];  // first-round histogram (4096: tokens past the history)
+  __shared__ uint32_t s_rh2[4096];  // second round, inside the first round's cut bucket
   __shared__ uint32_t s_eq[KPT][NWV];  // equal keys per (slot, wave), then their prefix
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t hr = blockIdx.x;  // b * Hq + h
@@ -277,6 +280,7 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
 #pragma unroll
   for (int i = 0; i < KPT; ++i) key[i] = valid(i) ? key[i] : 0u;
   for (int j = tid; j < 4097; j += NT) s_rh[j] = 0u;
+  for (int j = tid; j < 4096; j += NT) s_rh2[j] = 0u;
   topk_clear(sh);
   __syncthreads();
   // First round on the keys' 12 leading bits (sign, exponent and three
@@ -285,17 +289,18 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
 #pragma unroll
   for (int i = 0; i < KPT; ++i) atomicAdd(&s_rh[valid(i) ? key[i] >> 20 : 4096u], 1u);
   __syncthreads();
-  {
-    // thread t owns buckets 4095 - BPT*t down to 4096 - BPT*(t+1)
+  // The bin of a 4096-bin histogram (highest first) that holds the
+  // need-th largest entry: sh.bucket = {bin, entries above it, entries in it}.
+  auto find_bin = [&](const uint32_t* hb, uint32_t need) {
+    // thread t owns bins 4095 - BPT*t down to 4096 - BPT*(t+1)
     constexpr int BPT = 4096 / NT;
     uint32_t c[BPT], sum = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      c[j] = s_rh[4095 - BPT * tid - j];
+      c[j] = hb[4095 - BPT * tid - j];
       sum += c[j];
     }
     const uint32_t excl = block_excl_scan32(sum, sh.scan);
-    const uint32_t need = (uint32_t)kv;
     if (excl < need && need <= excl + sum) {
       uint32_t acc = excl;
 #pragma unroll
@@ -309,12 +314,25 @@ __global__ __launch_bounds__(NT) void vote_head_topk_kernel(
         acc += c[j];
       }
     }
+    __syncthreads();
+  };
+  find_bin(s_rh, (uint32_t)kv);
+  const uint32_t b1 = sh.bucket[0], rem1 = (uint32_t)kv - sh.bucket[1];
+  TopkCut cut{b1 << 20, 0xFFFFFFFFu};  // when the whole bucket is taken
+  if (sh.bucket[2] != rem1) {  // uniform
+    // Second round on the next 12 bits of the keys in that bucket (a few
+    // hundred keys of fp32 logits, which these bins spread to about one
+    // each), so that at most a short bucket search over the last 8 bits
+    // remains.
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (valid(i) && (key[i] >> 20) == b1) atomicAdd(&s_rh2[(key[i] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    find_bin(s_rh2, rem1);
+    const uint32_t lo = (b1 << 20) | (sh.bucket[0] << 8), rem2 = rem1 - sh.bucket[1];
+    cut = sh.bucket[2] == rem2 ? TopkCut{lo, 0xFFFFFFFFu}
+                               : topk_cut<KPT>(key, valid, (int)rem2, lo, lo | 0xFFu, sh);
   }
-  __syncthreads();
-  const uint32_t lo = sh.bucket[0] << 20, rem = (uint32_t)kv - sh.bucket[1];
-  const TopkCut cut = sh.bucket[2] == rem
-                          ? TopkCut{lo, 0xFFFFFFFFu}  // the whole bucket is taken
-                          : topk_cut<KPT>(key, valid, (int)rem, lo, lo | 0xFFFFFu, sh);
   const bool ties = cut.quota != 0xFFFFFFFFu;  // uniform
   const uint64_t below = (1ull << lane) - 1ull;
   if (ties) {
