@@ -100,6 +100,9 @@ def parse():
     ap.add_argument("--select-every", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain copy of 1 GiB (counter calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only measure the read rate of each workload's access patterns with "
+                         "the arithmetic taken away (libksa_probe.so), over a few launch shapes")
     ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "OUT_MD"),
                     help="summarise the rocprofv3 --kernel-trace csv files under TRACE_DIR "
                          "(durations per kernel) into the markdown file OUT_MD")
@@ -239,6 +242,116 @@ def copy_probe():
     ms = a.elapsed_time(b) / 10
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
                       "gbps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def read_probe(args):
+    """Read rates of the step's access patterns with nothing computed: each
+    workload's K/V (or summary, or K-history) rows read through
+    libksa_probe.so with the attention kernels' lane layout, the same bytes as
+    the real kernel and a few launch shapes each (waves per workgroup, splits
+    per row, chunks of loads in flight per wave), cycling over caches that
+    together exceed the 256 MB Infinity Cache.  One JSON line per pattern and
+    shape, then a markdown table (best shape per pattern) on stderr."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_decode_ksa_amd", "libksa_probe.so"))
+    P = ctypes.c_void_p
+    lib.ksa_probe_read.argtypes = [P, P, ctypes.c_longlong, ctypes.c_int, P, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, P, P]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    row_b = 256  # bf16 token row, D = 128
+
+    def sorted_blocks(rows, nblocks, k, bs):
+        # k distinct random blocks per row, ascending, expanded to their tokens
+        ids = torch.rand((rows, nblocks), generator=g, device=dev).argsort(dim=1)[:, :k]
+        ids = ids.sort(dim=1).values.to(torch.int32)
+        tok = ids[:, :, None] * bs + torch.arange(bs, device=dev, dtype=torch.int32)
+        return tok.reshape(rows, k * bs).contiguous()
+
+    def token_set(B, hist, voted, window):
+        ids = torch.rand((B, hist), generator=g, device=dev).argsort(dim=1)[:, :voted]
+        ids = ids.sort(dim=1).values.to(torch.int32)
+        rec = torch.arange(hist, hist + window, device=dev, dtype=torch.int32).expand(B, window)
+        return torch.cat([ids, rec], dim=1).contiguous()
+
+    # name, rows, capacity (tokens a row), two (K and V) or K alone, list maker
+    # (rows_per_list, lists for one cache), launch shapes (waves, splits,
+    # inflight; the real kernel's first), caches cycled
+    pats = [
+        ("c2 selected blocks (64 x 16 tokens, random 4 KB K and V blocks)", 512, 16384, True,
+         lambda: (1, sorted_blocks(512, 1024, 64, 16)),
+         [(8, 1, 1), (8, 1, 2), (8, 2, 1), (4, 1, 2), (8, 1, 4)], 4),
+        ("c2 summaries (1024 per row, contiguous)", 512, 1024, False,
+         lambda: (512, torch.arange(1024, device=dev, dtype=torch.int32)[None]),
+         [(8, 1, 2), (8, 1, 4), (8, 2, 2)], 4),
+        ("c2 dense (16384 tokens per row, contiguous K and V)", 512, 16384, True,
+         lambda: (512, torch.arange(16384, device=dev, dtype=torch.int32)[None]),
+         [(8, 8, 1), (8, 8, 2), (8, 16, 1)], 1),
+        ("c3 selected blocks (64 x 32 tokens, random 8 KB K and V blocks)", 256, 32768, True,
+         lambda: (1, sorted_blocks(256, 1024, 64, 32)),
+         [(8, 1, 1), (8, 1, 2), (8, 2, 1), (8, 1, 4)], 4),
+        ("c5 selected blocks (128 x 16 tokens, random 4 KB K and V blocks)", 2048, 32768, True,
+         lambda: (1, sorted_blocks(2048, 2048, 128, 16)),
+         [(4, 1, 1), (4, 1, 2), (8, 1, 1), (4, 1, 4)], 2),
+        ("c4 shared token set (1536 random + 512 recent tokens, 256 B K and V rows)", 128, 20000, True,
+         lambda: (8, token_set(16, 19488, 1536, 512)),
+         [(8, 2, 1), (8, 2, 2), (8, 4, 1), (4, 4, 2), (8, 2, 4)], 4),
+        ("c4 vote scorer's K history (19488 tokens per row, contiguous K)", 128, 20000, False,
+         lambda: (128, torch.arange(19488, device=dev, dtype=torch.int32)[None]),
+         [(4, 39, 2), (8, 20, 2), (8, 20, 4)], 1),
+    ]
+    best = []
+    for name, rows, cap, two, make, shapes, ncache in pats:
+        caches = []
+        for _ in range(ncache):
+            kk = torch.empty((rows, cap * row_b), dtype=torch.uint8, device=dev)
+            vv = torch.empty_like(kk) if two else None
+            rpl, lists = make()
+            caches.append((kk, vv, rpl, lists))
+        # the lists are made on the default stream and read on `stream`
+        torch.cuda.synchronize()
+        for _, _, rpl, lists in caches:
+            assert lists.dtype == torch.int32 and lists.is_contiguous()
+            assert lists.shape[0] * rpl >= rows and int(lists.min()) >= 0 and int(lists.max()) < cap
+        ntok = caches[0][3].shape[1]
+        bytes_call = rows * ntok * row_b * (2 if two else 1)
+        top = None
+        for waves, splits, inflight in shapes:
+            sink = torch.empty(rows * splits * waves * 64, dtype=torch.int32, device=dev)
+
+            def call(i):
+                kk, vv, rpl, lists = caches[i % ncache]
+                st = lib.ksa_probe_read(kk.data_ptr(), vv.data_ptr() if vv is not None else None,
+                                        cap * row_b, cap, lists.data_ptr(), rpl, rows, ntok,
+                                        splits, waves, inflight, sink.data_ptr(), sp)
+                if st != 0:
+                    raise RuntimeError("ksa_probe_read: status %d" % st)
+            warm(torch, call, 4, 0.1)
+            n = max(10, int(0.05 / max(bytes_call / 6.0e12, 1e-6)))
+            ms = timed(torch, stream, n, call)
+            gbps = bytes_call / (ms * 1e-3) / 1e9
+            rec = {"pattern": name, "waves": waves, "splits": splits, "inflight": inflight,
+                   "bytes_per_call": bytes_call, "us_per_call": round(ms * 1e3, 2),
+                   "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            print(json.dumps(rec), flush=True)
+            if top is None or gbps > top["gbps"]:
+                top = rec
+        best.append(top)
+        del caches
+        torch.cuda.empty_cache()
+    lines = ["| pattern | bytes per call | best shape (waves, splits, in flight) | us | GB/s | of 8 TB/s |",
+             "|---|---|---|---|---|---|"]
+    for r in best:
+        lines.append("| %s | %.1f MB | %d, %d, %d | %.2f | %.0f | %.3f |" % (
+            r["pattern"], r["bytes_per_call"] / 1e6, r["waves"], r["splits"], r["inflight"],
+            r["us_per_call"], r["gbps"], r["frac_of_peak"]))
+    print("\n".join(lines), file=sys.stderr, flush=True)
 
 
 class Runner:
@@ -735,6 +848,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.read_probe:
+        read_probe(args)
         return
     if args.paged != "none" or args.varlen:
         paged_main(args)

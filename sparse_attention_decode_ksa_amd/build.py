@@ -68,6 +68,25 @@ def build_library(jobs: int | None = None, out: str | None = None, objdir: str |
     return lib_out
 
 
+PROBE_SOURCE = "read_probe.hip"
+PROBE_LIB = os.path.join(PKG, "libksa_probe.so")
+
+
+def build_probe(out: str | None = None) -> str:
+    """Compile the measurement-only read probe (csrc/read_probe.hip) into
+    libksa_probe.so, which bench.py --read-probe loads; it is not part of
+    libksa.so or its header."""
+    lib_out = out or PROBE_LIB
+    tmp = lib_out + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + compile_flags() + ["-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SOURCE, " ".join(cmd), r.stderr[-8000:]))
+    os.replace(tmp, lib_out)
+    return lib_out
+
+
 if __name__ == "__main__":
     print(build_library())
+    print(build_probe())
     sys.exit(0)

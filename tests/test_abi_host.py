@@ -358,3 +358,37 @@ def test_noalloc_scratch_size_and_limit():
     st = lib.ksa_sparse_decode_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, ctypes.byref(sel), FAKE,
                                        FAKE, None)
     assert st == ksa.KSA_ERR_UNSUPPORTED
+
+
+def test_read_probe_is_separate_and_validates():
+    """The measurement-only read probe lives in its own library: libksa.so
+    does not export it, and it refuses bad launch arguments on the host
+    (status 1, nothing launched)."""
+    path = os.path.join(os.path.dirname(ksa.LIB_PATH), "libksa_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libksa_probe.so is not built")
+    assert not hasattr(ctypes.CDLL(ksa.LIB_PATH), "ksa_probe_read")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.ksa_probe_read.argtypes = [P, P, ctypes.c_longlong, ctypes.c_int, P, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, P, P]
+    fake = 1 << 20  # never dereferenced: every call below is refused first
+
+    def call(**kw):
+        a = dict(k=fake, v=fake, stride=16 * 256, cap=16, lists=fake, rpl=1, rows=4, ntok=64,
+                 splits=1, waves=4, inflight=1, sink=fake)
+        a.update(kw)
+        return lib.ksa_probe_read(a["k"], a["v"], a["stride"], a["cap"], a["lists"], a["rpl"],
+                                  a["rows"], a["ntok"], a["splits"], a["waves"], a["inflight"],
+                                  a["sink"], None)
+
+    assert call(k=None) == 1
+    assert call(lists=None) == 1
+    assert call(waves=9) == 1
+    assert call(waves=0) == 1
+    assert call(inflight=3) == 1
+    assert call(stride=100) == 1                # not a multiple of 16
+    assert call(stride=16 * 256, cap=17) == 1  # rows shorter than their capacity
+    assert call(ntok=4096, splits=1) == 1      # a workgroup's slice must fit its LDS stage
+    assert call(rows=0) == 1
