@@ -13,10 +13,11 @@
 //  2. vote_head_topk: one workgroup per (b, h), the head's keys held in
 //     registers (in LDS or re-read for very long histories), finds the
 //     Kv-th largest key and how many keys equal to it are taken (lowest
-//     token ids first) by a bucket search over the head's key range, and
-//     writes the head's picks as a bitmask [B, Hq, ceil(C/32)].
+//     token ids first) by radix rounds on the keys' bits and a bucket
+//     search, and writes the head's picks as a bitmask [B, Hq, ceil(C/32)].
 //  3. vote_tally_set (histories up to 32768 tokens): one workgroup per b
-//     adds the heads' bitmasks into bit-sliced vote totals, finds the vote
+//     adds the heads' bitmasks into bit-sliced vote totals (a carry-save
+//     tree, eight heads at a time), finds the vote
 //     threshold by a binary search on popcounts, and compacts the first Kv
 //     tokens by (votes desc, t asc) in ascending order with one workgroup
 //     scan; the W recent tokens follow.  Longer histories take two kernels:
@@ -243,9 +244,9 @@ __global__ __launch_bounds__(kScoreWaves * 64) void vote_scores_mfma_kernel(
 // largest end, a second on the next 12 bits of the keys in that bucket
 // narrows it to one bin, the bucket search of ksa_topk.h resolves the last 8
 // bits when needed, and each wave's ballot of "taken" is two words of the
-// bitmask as it stands.  Ties at the
-// threshold (equal fp32 logits) take the lowest token ids: the equal keys
-// are ranked in token order by a per-(slot, wave) count.  The first
+// bitmask as it stands.  Ties at the threshold (equal fp32 logits) take the
+// lowest token ids: the equal keys are ranked in token order by a
+// per-(slot, wave) count.  The first
 // workgroup of each sequence also clears that sequence's vote histogram,
 // which vote_count fills after this kernel.
 template <int NT, int KPT>
