@@ -33,6 +33,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "ksa_device.h"
 #include "ksa_internal.h"
 
@@ -225,23 +227,44 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& a, const int* s_idx, 
   }
 }
 
+// bf16 logits on v_dot2c_f32_bf16: q and K stay packed (no widening), two
+// exact products per instruction, and the scale is applied to the lane
+// group's sum; fp32 keeps the widened, pre-scaled q of the FMA chain.
+#ifndef KSA_VALU_DOT2
+#define KSA_VALU_DOT2 1
+#endif
+template <typename T>
+constexpr bool kDot2 = KSA_VALU_DOT2 && std::is_same<T, uint16_t>::value;
+
 template <typename T, int D, int G, int NI, int LPT>
-__device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], const uint4* kc,
-                                              const uint4* vc, const bool* okc, float* m, float* l,
+__device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], const uint4 (&qb)[G],
+                                              float qscale, const uint4* kc, const uint4* vc,
+                                              const bool* okc, float* m, float* l,
                                               float (&acc)[G][KV<T>::EPL]) {
   constexpr int EPL = KV<T>::EPL;
   // logits of the NI tokens for every head of the group
   float s[NI][G];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    float f[EPL];
-    KV<T>::widen(kc[i], f);
+    if constexpr (kDot2<T>) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p = 0.f;
+      for (int h = 0; h < G; ++h) {
+        float p = dot2_bf16(qb[h].x, kc[i].x, 0.f);
+        p = dot2_bf16(qb[h].y, kc[i].y, p);
+        p = dot2_bf16(qb[h].z, kc[i].z, p);
+        p = dot2_bf16(qb[h].w, kc[i].w, p);
+        s[i][h] = group_sum<LPT>(p) * qscale;
+      }
+    } else {
+      float f[EPL];
+      KV<T>::widen(kc[i], f);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
-      s[i][h] = group_sum<LPT>(p);
+      for (int h = 0; h < G; ++h) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) p = fmaf(qv[h][e], f[e], p);
+        s[i][h] = group_sum<LPT>(p);
+      }
     }
   }
   // online softmax update, once per chunk
@@ -515,10 +538,11 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
   const int c_end = min(c_begin + a.cps, nchunks);
 
   float qv[G][EPL];
+  uint4 qb[G];  // the raw query pieces (bf16 logits on dot2)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    KV<T>::widen(qraw ? qraw[h] : ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL),
-                 qv[h]);
+    qb[h] = qraw ? qraw[h] : ld16((const T*)a.q + ((int64_t)b * d.Hq + g * G + h) * D + li * EPL);
+    KV<T>::widen(qb[h], qv[h]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[h][e] *= a.qscale;
   }
@@ -558,7 +582,7 @@ __device__ __forceinline__ void attn_row_valu(const AttnArgs& a, int row, int sp
         if (j + P < my_n)
           load_chunk<T, D, KIND, CH, SPW, NI>(a, s_idx, s_pg, e0, slot, c0 + (j + P) * nw, kbase,
                                               vbase, kb[s], vb[s], okb[s]);
-        compute_chunk<T, D, G, NI, LPT>(qv, kc, vc, okc, m, l, acc);
+        compute_chunk<T, D, G, NI, LPT>(qv, qb, a.qscale, kc, vc, okc, m, l, acc);
       }
     }
   }

@@ -110,6 +110,14 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // 4*(l/16)..+4.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// a.bf16[0] * b.bf16[0] + a.bf16[1] * b.bf16[1] + c in fp32 (v_dot2c_f32_bf16;
+// the bf16 products are exact in fp32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
