@@ -251,22 +251,33 @@ __global__ __launch_bounds__(NW * 64, (G <= 2 ? KSA_STEP_OCC : 1)) void block_to
   }
   __syncthreads();
 
-  // 3. top-k over the LDS keys; thread t takes positions [t*kpt, (t+1)*kpt)
+  // 3. top-k over the LDS keys; thread t takes positions [t*kpt, (t+1)*kpt).
+  // The register array is sized for the row's kpt (2, 4 or the most), so
+  // the unrolled passes of the top-k do no predicated-off iterations.
   const int kpt = (NB + kStepThreads - 1) / kStepThreads;
   const int j0 = tid * kpt;
-  uint32_t key[kStepKPT];
-#pragma unroll
-  for (int i = 0; i < kStepKPT; ++i) key[i] = (i < kpt && j0 + i < NB) ? s_keys[j0 + i] : 0u;
   int32_t* gidx = s.block_idx ? s.block_idx + (int64_t)row * s.keff : nullptr;
   // every wave writes the whole ascending list into the LDS stage (the same
   // values), so it starts its attention without waiting for the others
   static_assert(kStepMaxBlocks <= kTopkListMax, "selection mask");
-  row_topk_list<kStepKPT>(key, kpt, j0, NB, keff, s_lo, s_hi, s_topk,
-                          [&](int rank, int j, bool primary) {
-                            s_idx[rank] = j;
-                            if constexpr (PAGED) s_pg[rank] = ptab[j];
-                            if (primary && gidx) gidx[rank] = j;
-                          });
+  auto topk = [&](auto kpt_max) {
+    constexpr int K = decltype(kpt_max)::value;
+    uint32_t key[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) key[i] = (i < kpt && j0 + i < NB) ? s_keys[j0 + i] : 0u;
+    row_topk_list<K>(key, kpt, j0, NB, keff, s_lo, s_hi, s_topk,
+                     [&](int rank, int j, bool primary) {
+                       s_idx[rank] = j;
+                       if constexpr (PAGED) s_pg[rank] = ptab[j];
+                       if (primary && gidx) gidx[rank] = j;
+                     });
+  };
+  if (kpt <= 2)
+    topk(std::integral_constant<int, 2>{});
+  else if (kpt <= 4)
+    topk(std::integral_constant<int, 4>{});
+  else
+    topk(std::integral_constant<int, kStepKPT>{});
   if (PAGED || a.seq_lens) {  // ids past this row's k_eff
     if (gidx)
       for (int i = keff + tid; i < s.keff; i += kStepThreads) gidx[i] = -1;
