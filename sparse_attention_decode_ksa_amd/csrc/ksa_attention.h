@@ -268,13 +268,16 @@ __device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], 
     }
   }
   // online softmax update, once per chunk
+  float alpha[G];
+  bool rescale = false;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float mx = m[h];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       if (okc[i]) mx = fmaxf(mx, s[i][h]);
-    const float alpha = fast_exp2(m[h] - mx);
+    alpha[h] = fast_exp2(m[h] - mx);
+    rescale |= alpha[h] != 1.f;
     float ps = 0.f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -282,10 +285,17 @@ __device__ __forceinline__ void compute_chunk(const float (&qv)[G][KV<T>::EPL], 
       s[i][h] = p;
       ps += p;
     }
-    l[h] = fmaf(l[h], alpha, ps);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+    l[h] = fmaf(l[h], alpha[h], ps);
     m[h] = mx;
+  }
+  // the accumulators change only when some running max moved (a factor of
+  // exactly 1 leaves them as they are, so skipping it is exact); after the
+  // first chunks that is rare, and the test is one wave-wide ballot
+  if (__ballot(rescale)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
   }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -759,13 +769,16 @@ __device__ __forceinline__ void attn_row_mfma(const AttnArgs& a, int row, int sp
       if (kg == 0) pt[CH][r] = alpha;
     }
     wave_lds_fence();
-    float al[G];
+    // rescale only when some head's running max moved (see compute_chunk)
+    if (__ballot(r < G && kg == 0 && alpha != 1.f)) {
+      float al[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) al[h] = pt[CH][h];
+      for (int h = 0; h < G; ++h) al[h] = pt[CH][h];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= al[h];
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float pv[G];
