@@ -54,7 +54,7 @@ __global__ __launch_bounds__(512) void read_probe_kernel(const uint4* __restrict
     s_tok[i] = min(max(list[e0 + i], 0), cap - 1);
   __syncthreads();
   const uint4* kb = k + (long long)row * row_stride + li;
-  const uint4* vb = v + (long long)row * row_stride + li;
+  const uint4* vb = TWO ? v + (long long)row * row_stride + li : nullptr;
   const int c0 = c_begin + wave;
   const int my_n = c0 < c_end ? (c_end - c0 + nw - 1) / nw : 0;
   // entry of load i of the wave's j-th chunk (past the slice: its last entry)
