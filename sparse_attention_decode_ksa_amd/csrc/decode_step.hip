@@ -43,8 +43,13 @@ namespace {
 #ifndef KSA_STEP_OCC
 #define KSA_STEP_OCC 4
 #endif
+// Summaries a lane loads per scoring unit (a unit is SPW * this many blocks).
+// Small units end the scoring phase with the waves close together, since
+// each wave takes its next unit from the shared counter: 4 measured 2-3 %
+// faster than 8 for the Qwen3-8B-shaped step (32 x 8 rows, block 32) and
+// ~1 % for the block-16 shapes, with 2 and 3 no better.  A tuning knob.
 #ifndef KSA_STEP_UNROLL
-#define KSA_STEP_UNROLL 8
+#define KSA_STEP_UNROLL 4
 #endif
 constexpr int kStepUnroll = KSA_STEP_UNROLL;  // summaries in flight per lane per batch
 
